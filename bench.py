@@ -1,0 +1,218 @@
+"""Throughput of the MoE layer forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config glam|glm45|glm5|decode|tiny]
+
+One step is one moe_forward over one batch of synthetic, seeded, HBM-resident
+inputs: router, dispatch, expert FFNs, shared expert (second stream) and
+combine.  Prints ONE JSON line on stdout (logs go to stderr):
+
+* value = tokens/s of the whole layer (wall clock over K steps bracketed by
+  device synchronisation);
+* roofline = the dominant kernel's algorithmic bytes (or FLOPs) per launch
+  over its average launch time, measured with HIP events on its own stream
+  during the timed steps, against MI355X's published peak;
+* cpu_baseline = the CPU oracle timed on this host on a bounded sample of
+  the same workload.
+The default workload is the GLaM-shaped layer (T=4096, D=4096, 64 experts,
+top-2, GELU 16384).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s + active TFLOP/s (prefill), HBM GB/s (decode), % roofline"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_work(cfg, counts):
+    """Algorithmic FLOPs and HBM bytes per launch of each kernel, from the
+    layer shape and the realised per-expert counts (touched experts only)."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    T, D, M, F, k, Fs, G = cfg.T, cfg.D, cfg.M, cfg.F, cfg.k, cfg.F_shared, cfg.G
+    S = T * k
+    U = int(sum(1 for c in counts if c > 0))
+    w = {}
+    w["route"] = (2.0 * T * D * M, T * D * esz + M * D * 4 + S * 8)
+    w["ffn_up"] = (2.0 * S * D * G * F, U * G * F * D * esz + T * D * esz + S * F * esz)
+    w["ffn_down"] = (2.0 * S * F * D, U * D * F * esz + S * F * esz + S * D * esz)
+    w["combine"] = (float(S * D), S * D * esz + (T * D * 4 if Fs else 0) + T * D * esz)
+    w["perm_count"] = (0.0, S * 4)
+    w["perm_scan"] = (0.0, 0)
+    w["perm_scatter"] = (0.0, S * 4 * 4)
+    w["tile_table"] = (0.0, 0)
+    if Fs:
+        w["shared_up"] = (2.0 * T * D * 2 * Fs, 2 * Fs * D * esz + T * D * esz + T * Fs * esz)
+        w["shared_down"] = (2.0 * T * Fs * D, D * Fs * esz + T * Fs * esz + T * D * 4)
+    return w, U
+
+
+def layer_work(cfg, U):
+    """Active FLOPs and algorithmic bytes of the whole layer: touched expert
+    weights, shared weights, router, x and y (intermediates not credited)."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    T, D, M, F, k, Fs, G = cfg.T, cfg.D, cfg.M, cfg.F, cfg.k, cfg.F_shared, cfg.G
+    per_pair = 2 * D * F * (G + 1)
+    flops = T * k * per_pair + (T * 6 * D * Fs) + 2 * T * D * M
+    byts = U * (G + 1) * F * D * esz + 3 * Fs * D * esz + M * D * 4 + 2 * T * D * esz
+    return float(flops), float(byts)
+
+
+def cpu_baseline(cfg, t, target_s: float):
+    """The oracle's whole per-token forward (router, experts, shared expert,
+    sum) on a bounded token sample, on this host's cores."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    h = workloads.host_inputs(t)
+    nthr = oracle.num_threads()
+    rng = np.random.default_rng(0)
+    probe = max(nthr, 4)
+    toks = rng.choice(cfg.T, size=min(cfg.T, probe), replace=False)
+    t0 = time.perf_counter()
+    oracle.forward(cfg, h, tokens=toks)
+    dt = time.perf_counter() - t0
+    per_tok = dt / len(toks)
+    n = int(min(cfg.T, max(len(toks), target_s / max(per_tok, 1e-9))))
+    n = max(nthr, (n // nthr) * nthr) if n >= nthr else n
+    toks = rng.choice(cfg.T, size=min(cfg.T, n), replace=False)
+    t0 = time.perf_counter()
+    oracle.forward(cfg, h, tokens=toks)
+    dt = time.perf_counter() - t0
+    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+            "sample": f"{len(toks)} random tokens of {cfg.name} (seed 0), whole per-token "
+                      f"forward in fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="glam")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-aux-stream", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the layer's expert-parallel sharding is not "
+              f"part of this build (asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    from sparse_mixture_experts_15_amd import binding as B
+    from sparse_mixture_experts_15_amd.layer import MoELayer
+
+    cfg = workloads.get(args.config)
+    log(f"workload {cfg.name}: generating inputs on the GPU")
+    t = workloads.generate(cfg, seed=args.seed, device="cuda")
+    L = MoELayer(B.make_desc(cfg))
+    d = L.desc
+    main = torch.cuda.current_stream()
+    aux = None if args.no_aux_stream else torch.cuda.Stream()
+    y = torch.empty_like(t["x"])
+
+    def step():
+        B.moe_forward(L.handle, d, t["x"], t["W_r"], t["bias"], t["W1"], t["b1"], t["W2"],
+                      t["b2"], t["Wsh_gu"], t["Wsh_dn"], y, L.ws, stream=main, aux_stream=aux)
+
+    # realised routing (touched experts) for the algorithmic byte counts
+    idx = torch.empty(cfg.T * cfg.k, dtype=torch.int32, device="cuda")
+    w = torch.empty(cfg.T * cfg.k, dtype=torch.float32, device="cuda")
+    B.moe_route(L.handle, d, t["x"], t["W_r"], t["bias"], idx, w)
+    counts = torch.bincount(idx.long(), minlength=cfg.M).cpu().tolist()
+    kw, U = kernel_work(cfg, counts)
+    log(f"touched experts {U}/{cfg.M}, max rows {max(counts)}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel split (separate pass) to find the dominant kernel
+    nprof = min(args.steps, 5)
+    B.moe_profile_start(L.handle, 16 * nprof, None)
+    for _ in range(nprof):
+        step()
+    B.moe_profile_stop(L.handle)
+    split = {k: v[1] / nprof for k, v in B.moe_profile_results(L.handle).items()}
+    dominant = max(split, key=split.get)
+    log("per-step kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in split.items()))
+
+    # timed region: the dominant kernel bracketed by HIP events on its stream
+    B.moe_profile_start(L.handle, args.steps + 1, dominant)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    B.moe_profile_stop(L.handle)
+    launches, tot_ms = B.moe_profile_results(L.handle)[dominant]
+    dom_ms = tot_ms / max(launches, 1)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_s = cfg.T / (ms_per_step * 1e-3)
+    F_alg, B_alg = layer_work(cfg, U)
+    active_tflops = F_alg / (ms_per_step * 1e-3) / 1e12
+    alg_gbps = B_alg / (ms_per_step * 1e-3) / 1e9
+    peak_f = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    t_roof = max(F_alg / (peak_f * 1e12), B_alg / (PEAK_HBM_GBPS * 1e9))
+
+    fl, by = kw[dominant]
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    if by > 0 and fl / by < ridge:
+        achieved = by / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None}
+    else:
+        achieved = fl / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_f,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_f, 4), "traffic": None}
+    roof.update({"kernel": dominant, "kernel_ms": round(dom_ms, 4),
+                 "alg_flops": fl, "alg_bytes": by})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on a ~{args.cpu_seconds:.0f} s token sample")
+        cpu = cpu_baseline(cfg, t, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "D": cfg.D, "M": cfg.M, "F": cfg.F,
+                   "k": cfg.k, "F_shared": cfg.F_shared, "scorer": cfg.scorer, "act": cfg.act,
+                   "alpha": cfg.alpha, "seed": args.seed, "touched_experts": U,
+                   "aux_stream": aux is not None},
+        "active_tflops": round(active_tflops, 2),
+        "alg_hbm_gbps": round(alg_gbps, 1),
+        "layer_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),
+        "kernel_ms_per_step": {k: round(v, 4) for k, v in split.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts
+ * feed-forward layer, forward pass.
+ *
+ * The layer (GLaM study note, "Sparse MoE Layer"; "Shared Expert" GLM-4.5
+ * study note, "How it works"; GLM-5 "Shared expert" inspector page, "All 5
+ * steps"):
+ *
+ *   l_t   = W_r x_t                                  router logits, fp32
+ *   score = softmax(l_t)            (SOFTMAX scorer)  selection = gate = score
+ *         = sigmoid(l_t)            (SIGMOID scorer)  selection = score + bias,
+ *                                                     gate = score
+ *   S_t   = the k experts with the largest selection score
+ *   w_j   = alpha * g_j / (sum_{i in S_t} g_i + eps)  (renorm = 1)
+ *         = alpha * g_j                               (renorm = 0)
+ *   E_e(x) = W2[e] (SiLU(gate rows of W1[e] x) * (up rows of W1[e] x))  SWIGLU
+ *          = W2[e] gelu(W1[e] x + b1[e]) + b2[e]                         GELU
+ *   y_t   = sum_j w_j E_{e_j}(x_t) + E_sh(x_t)
+ *
+ * E_sh is a SwiGLU of width F_shared applied to every token's pre-routing
+ * x_t (absent when F_shared == 0).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every data pointer is a DEVICE pointer to a dense, row-major, contiguous
+ *   buffer that the caller allocated and owns, 16-byte aligned.  The library
+ *   never allocates, frees or keeps a caller pointer past the call.
+ * - `dtype` types x, the expert weights W1/b1/W2/b2, the shared weights, the
+ *   sorted expert outputs O and y: fp32 (MOE_DTYPE_F32) or bf16
+ *   (MOE_DTYPE_BF16, stored as raw uint16 bit patterns).  W_r, bias, w and
+ *   Ysh are always fp32; indices are int32.
+ * - `stream` / `aux_stream` are hipStream_t values passed as void*; NULL is
+ *   the null stream.  All work is enqueued asynchronously; no call copies
+ *   between host and device or synchronises the host, so results are valid
+ *   once the stream(s) complete, and every call may be captured in a graph.
+ * - Validation happens before anything is enqueued: on any error nothing is
+ *   launched and the outputs are untouched.  T == 0 is a valid no-op.
+ * - Identical inputs on the same device give bitwise-identical outputs
+ *   (no floating-point atomics anywhere).
+ * - A handle is not thread-safe; use one handle per host thread.
+ *
+ * Return codes are moe_status values; moe_status_string() names them and
+ * moe_last_error_detail() (per host thread) explains the last failure.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = 1,      /* null pointer, bad enum, T < 0, k < 1, k > M, ... */
+    MOE_ERR_UNSUPPORTED = 2,  /* k > 16, M > 1024, D/F/F_shared not multiples of 8,
+                                 T*k or a buffer index beyond int32 */
+    MOE_ERR_WORKSPACE = 3,    /* ws_bytes smaller than the call needs */
+    MOE_ERR_HIP = 4           /* a HIP runtime call or launch failed */
+} moe_status;
+
+enum { MOE_SCORER_SOFTMAX = 0, MOE_SCORER_SIGMOID = 1 };
+enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GELU = 1 };
+enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
+
+#define MOE_MAX_K 16
+#define MOE_MAX_EXPERTS 1024
+
+/* Layer descriptor (plain data).
+ *   T        tokens (the flattened batch x positions, as the GLM-4.5 note's
+ *            "Shapes" paragraph flattens (B,S,D) to (BS,D))
+ *   D        hidden size;  M routed experts;  F routed expert width
+ *   F_shared shared SwiGLU width (n_shared * expert width; 0 = none)
+ *   k        experts per token (1..min(M,16))
+ *   scorer   MOE_SCORER_*;  act MOE_ACT_*;  dtype MOE_DTYPE_*
+ *   renorm   1: divide the selected gate values by their sum + eps
+ *   alpha    routed scaling factor (multiplies every routed weight)
+ *   eps      renormalisation epsilon (1e-20 in the GLM-4.5 note)          */
+typedef struct moe_desc {
+    int64_t T, D, M, F, F_shared;
+    int32_t k;
+    int32_t scorer;
+    int32_t act;
+    int32_t dtype;
+    int32_t renorm;
+    float alpha;
+    float eps;
+} moe_desc;
+
+typedef struct moe_handle moe_handle;
+
+/* Create a handle bound to HIP device `device` (it becomes current during
+ * calls).  Allocates only host state and two timing-free HIP events. */
+int moe_create(int device, moe_handle** out);
+int moe_destroy(moe_handle* h);
+
+/* Bytes of device workspace that moe_forward needs for `d`; the same size
+ * also satisfies every stage call below.  Host-only computation. */
+int moe_workspace_size(const moe_desc* d, size_t* bytes);
+
+/* Router: logits, scores, top-k selection and weights [GLaM "Sparse MoE
+ * Layer" router and TopK equations; GLM-4.5 "How it works" sigmoid router,
+ * correction bias, renormalisation and scaling].
+ *   x[T,D] (dtype), W_r[M,D] fp32, bias[M] fp32 (SIGMOID only; NULL = zero;
+ *   ignored for SOFTMAX) -> idx[T,k] int32, w[T,k] fp32.
+ * A token's k experts are distinct and stored in ascending expert order;
+ * an exactly equal selection score goes to the lower expert index. */
+int moe_route(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
+              const float* bias, int32_t* idx, float* w, void* stream);
+
+/* Dispatch: group the T*k flat slots f = t*k + j by expert, stably
+ * [GLaM "Capacity, Active Compute, and Reporting": dispatch / expert
+ * batching].
+ *   idx[T,k] -> counts[M], offsets[M+1] (exclusive prefix, offsets[M] =
+ *   number of kept slots), sorted_slot[T*k] (flat slot of sorted row r),
+ *   sorted_token[T*k] (= sorted_slot / k), slot_row[T*k] (row of slot f).
+ * Rows of one expert are in ascending slot order.  An index equal to M (or
+ * outside [0,M)) is a dropped slot, the extra one-hot class of the GLM-5
+ * routed-experts excerpt: counted nowhere, slot_row = -1, and the unused
+ * tail rows r >= offsets[M] of sorted_slot/sorted_token are -1.
+ * Precondition: a token's kept entries are distinct experts (the router
+ * guarantees it); repeated entries leave the order unspecified (no access
+ * goes out of bounds).  Uses workspace. */
+int moe_permute(moe_handle* h, const moe_desc* d, const int32_t* idx, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_token, int32_t* sorted_slot,
+                int32_t* slot_row, void* ws, size_t ws_bytes, void* stream);
+
+/* Routed experts over the dispatched rows [GLaM dense FFN equation; GLM-5
+ * "All 5 steps"]: for every sorted row r of expert e, with t =
+ * sorted_token[r] and f = sorted_slot[r],
+ *   O[r,:] = w[f] * E_e(x[t,:])
+ * W1[M,G*F,D] (SWIGLU: G = 2, gate rows 0..F-1 then up rows F..2F-1;
+ * GELU: G = 1), b1[M,F] and b2[M,D] (GELU only, NULL = zero), W2[M,D,F],
+ * w[T*k] fp32 indexed by flat slot, O[T*k,D] (dtype; rows >= offsets[M]
+ * untouched).  Uses workspace for the hidden activations. */
+int moe_expert_ffn(moe_handle* h, const moe_desc* d, const void* x,
+                   const int32_t* sorted_token, const int32_t* sorted_slot,
+                   const int32_t* offsets, const float* w, const void* W1,
+                   const void* b1, const void* W2, const void* b2, void* O,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Shared expert on every token's pre-routing x ["Shared Expert" GLM-4.5
+ * note, shared-expert equation; GLM-5 "All 5 steps"]:
+ *   Ysh[t,:] = Wsh_dn (SiLU(Wsh_gate x_t) * (Wsh_up x_t))
+ * Wsh_gu[2*F_shared, D] (gate rows then up rows), Wsh_dn[D, F_shared],
+ * Ysh[T,D] fp32.  Requires F_shared > 0.  Uses workspace. */
+int moe_shared_expert(moe_handle* h, const moe_desc* d, const void* x,
+                      const void* Wsh_gu, const void* Wsh_dn, float* Ysh, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Combine [GLaM MoE output sum; GLM-4.5 "How it works" output equation]:
+ *   y[t,:] = sum_{j<k} O[slot_row[t*k+j], :]  (+ Ysh[t,:] if Ysh != NULL)
+ * summed in fp32 in fixed j order, then rounded once to dtype.  A slot with
+ * slot_row < 0 contributes nothing.  No atomics.  y must not alias O or Ysh. */
+int moe_combine(moe_handle* h, const moe_desc* d, const void* O, const int32_t* slot_row,
+                const float* Ysh, void* y, void* stream);
+
+/* Whole layer: route, permute, expert FFNs, shared expert, combine.
+ * The shared expert runs on `aux_stream` (forked from and joined back into
+ * `stream` with events) so it overlaps the routed path; aux_stream == NULL
+ * runs it on `stream`, with bitwise-identical results.  y[T,D] (dtype) must
+ * not alias x.  Shared weights may be NULL only when F_shared == 0. */
+int moe_forward(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
+                const float* bias, const void* W1, const void* b1, const void* W2,
+                const void* b2, const void* Wsh_gu, const void* Wsh_dn, void* y,
+                void* ws, size_t ws_bytes, void* stream, void* aux_stream);
+
+/* Per-kernel timing for measurement harnesses.  While enabled, every kernel
+ * the handle launches whose label contains `filter` (NULL or "" = all) is
+ * bracketed by a pair of HIP timing events on the stream it runs on, up to
+ * `capacity` launches.  moe_profile_stop() waits for those events and folds
+ * them into per-label totals readable with moe_profile_results().  Labels:
+ * route, perm_count, perm_scan, perm_scatter, tile_table, ffn_up, ffn_down,
+ * shared_up, shared_down, combine. */
+typedef struct moe_kernel_time {
+    char label[32];
+    int64_t launches;
+    double total_ms;
+} moe_kernel_time;
+
+int moe_profile_start(moe_handle* h, int capacity, const char* filter);
+int moe_profile_stop(moe_handle* h);
+int moe_profile_results(moe_handle* h, moe_kernel_time* out, int max_entries, int* n_entries);
+
+const char* moe_status_string(int status);
+const char* moe_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

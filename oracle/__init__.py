@@ -64,7 +64,7 @@ def _load():
         lib = ctypes.CDLL(build())
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         cp = ctypes.POINTER(_Cfg)
-        lib.oracle_route.argtypes = [cp, vp, vp, vp, i64, vp, vp, vp, vp, vp]
+        lib.oracle_route.argtypes = [cp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp]
         lib.oracle_dispatch.argtypes = [i64, i32, i64, vp, vp, vp, vp, vp, vp]
         lib.oracle_expert.argtypes = [cp, vp, i64, i64, vp, vp, vp, vp, vp]
         lib.oracle_shared.argtypes = [cp, vp, i64, vp, vp, vp]
@@ -121,10 +121,11 @@ def _tokens(cfg, tokens):
     return np.ascontiguousarray(tokens, dtype=np.int64)
 
 
-def route(cfg, x, W_r, bias=None, tokens=None, want_logits=False):
+def route(cfg, x, W_r, bias=None, tokens=None, want_logits=False, want_sel=False):
     """Router for the listed tokens (default: all T).  Returns idx[n,k]
     int32, w[n,k] fp64, gap[n] fp64 (k-th minus (k+1)-th selection score)
-    and, if asked, logits[n,M] fp64."""
+    and, if asked, logits[n,M] and selection scores sel[n,M] (fp64), in
+    that order."""
     c = make_cfg(cfg)
     _check_storage(c, x=x)
     tok = _tokens(cfg, tokens)
@@ -133,9 +134,15 @@ def route(cfg, x, W_r, bias=None, tokens=None, want_logits=False):
     w = np.zeros((n, cfg.k), np.float64)
     gap = np.zeros(n, np.float64)
     logits = np.zeros((n, cfg.M), np.float64) if want_logits else None
+    sel = np.zeros((n, cfg.M), np.float64) if want_sel else None
     _load().oracle_route(ctypes.byref(c), _ptr(x), _ptr(_f32(W_r)), _ptr(_f32(bias)), n,
-                         _ptr(tok), _ptr(idx), _ptr(w), _ptr(gap), _ptr(logits))
-    return (idx, w, gap, logits) if want_logits else (idx, w, gap)
+                         _ptr(tok), _ptr(idx), _ptr(w), _ptr(gap), _ptr(logits), _ptr(sel))
+    res = [idx, w, gap]
+    if want_logits:
+        res.append(logits)
+    if want_sel:
+        res.append(sel)
+    return tuple(res)
 
 
 def dispatch(T: int, k: int, M: int, idx):

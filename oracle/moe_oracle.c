@@ -74,7 +74,8 @@ int oracle_num_threads(void)
 /* Router for one token [GLaM router and TopK; GLM45 sigmoid router]. */
 static void route_token(const moe_oracle_cfg* c, const void* x, const float* W_r,
                         const float* bias, int64_t t, int32_t* idx_out,
-                        double* w_out, double* gap_out, double* logit_out)
+                        double* w_out, double* gap_out, double* logit_out,
+                        double* sel_out)
 {
     const int64_t D = c->D, M = c->M;
     const int32_t k = c->k;
@@ -117,6 +118,10 @@ static void route_token(const moe_oracle_cfg* c, const void* x, const float* W_r
             sel[e] = g[e] + (bias ? (double)bias[e] : 0.0);
         }
     }
+
+    if (sel_out)
+        for (int64_t e = 0; e < M; ++e)
+            sel_out[e] = sel[e];
 
     /* TopK: k times, take the not-yet-taken expert with the largest
      * selection score; scanning upward with a strict comparison keeps the
@@ -165,12 +170,12 @@ static void route_token(const moe_oracle_cfg* c, const void* x, const float* W_r
 
 void oracle_route(const moe_oracle_cfg* c, const void* x, const float* W_r,
                   const float* bias, int64_t ntok, const int64_t* tokens,
-                  int32_t* idx, double* w, double* gap, double* logits)
+                  int32_t* idx, double* w, double* gap, double* logits, double* sel)
 {
     #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t i = 0; i < ntok; ++i)
         route_token(c, x, W_r, bias, tokens[i], idx + i * c->k, w + i * c->k, gap + i,
-                    logits ? logits + i * c->M : NULL);
+                    logits ? logits + i * c->M : NULL, sel ? sel + i * c->M : NULL);
 }
 
 /* Dispatch: group the flat slots f = t*k + j by expert, keeping slot order
@@ -357,7 +362,7 @@ void oracle_forward(const moe_oracle_cfg* c, const void* x, const float* W_r,
     #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < ntok; ++i) {
         double gap;
-        route_token(c, x, W_r, bias, tokens[i], idx + i * k, w + i * k, &gap, NULL);
+        route_token(c, x, W_r, bias, tokens[i], idx + i * k, w + i * k, &gap, NULL, NULL);
         layer_token(c, x, idx + i * k, w + i * k, W1, b1, W2, b2, Wsh_gu, Wsh_dn,
                     tokens[i], y + i * D, NULL, NULL);
     }

@@ -38,10 +38,11 @@ typedef struct {
  * Outputs are indexed by position in the token list:
  *   idx[i*k+j] expert of slot j (ascending expert order), w[i*k+j] weight,
  *   gap[i] = (k-th largest selection score) - ((k+1)-th largest), +inf if k == M,
- *   logits[i*M+e] (nullable).  bias is nullable (zero bias). */
+ *   logits[i*M+e] and the selection scores sel[i*M+e] (both nullable).
+ *   bias is nullable (zero bias). */
 void oracle_route(const moe_oracle_cfg* c, const void* x, const float* W_r,
                   const float* bias, int64_t ntok, const int64_t* tokens,
-                  int32_t* idx, double* w, double* gap, double* logits);
+                  int32_t* idx, double* w, double* gap, double* logits, double* sel);
 
 /* Dispatch over all T*k flat slots f = t*k + j: per-expert counts, their
  * exclusive prefix sum offsets[0..M] and a stable counting sort of the slots

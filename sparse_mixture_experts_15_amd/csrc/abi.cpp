@@ -1,0 +1,537 @@
+// C ABI of the MoE layer: descriptor validation, workspace plan, stream
+// fork/join and kernel launches.  Every check runs before the first
+// launch, so an error leaves the outputs and the streams untouched.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "common.hpp"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_detail;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_detail = buf;
+    return code;
+}
+
+const char* kLabels[L_COUNT] = {"route",     "perm_count", "perm_scan",  "perm_scatter",
+                                "tile_table", "ffn_up",     "ffn_down",   "shared_up",
+                                "shared_down", "combine"};
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Device workspace layout shared by every entry point.
+struct Plan {
+    int64_t S = 0, nblk = 0, max_tiles = 0;
+    int bm = 0;
+    size_t esz = 0;
+    size_t idx = 0, w = 0, counts = 0, offsets = 0, sorted_token = 0, sorted_slot = 0,
+           slot_row = 0, hist = 0, tiles = 0, H = 0, O = 0, Hsh = 0, Ysh = 0, total = 0;
+};
+
+Plan make_plan(const moe_desc* d) {
+    Plan p;
+    p.esz = d->dtype == MOE_DTYPE_BF16 ? 2 : 4;
+    p.S = d->T * d->k;
+    p.nblk = (d->T + kPermBlock - 1) / kPermBlock;
+    p.bm = gemm_block_m(d->dtype);
+    p.max_tiles = (p.S + p.bm - 1) / p.bm + (d->M < p.S ? d->M : p.S);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    p.idx = take(p.S * 4);
+    p.w = take(p.S * 4);
+    p.counts = take(d->M * 4);
+    p.offsets = take((d->M + 1) * 4);
+    p.sorted_token = take(p.S * 4);
+    p.sorted_slot = take(p.S * 4);
+    p.slot_row = take(p.S * 4);
+    p.hist = take((size_t)p.nblk * d->M * 4);
+    p.tiles = take((size_t)p.max_tiles * 2 * 4);
+    p.H = take((size_t)p.S * d->F * p.esz);
+    p.O = take((size_t)p.S * d->D * p.esz);
+    p.Hsh = take((size_t)d->T * d->F_shared * p.esz);
+    p.Ysh = take(d->F_shared > 0 ? (size_t)d->T * d->D * 4 : 0);
+    p.total = off;
+    return p;
+}
+
+int validate(const moe_desc* d) {
+    if (!d) return fail(MOE_ERR_INVALID, "descriptor is NULL");
+    if (d->T < 0) return fail(MOE_ERR_INVALID, "T=%lld < 0", (long long)d->T);
+    if (d->D <= 0 || d->M <= 0 || d->F <= 0 || d->F_shared < 0)
+        return fail(MOE_ERR_INVALID, "D, M, F must be > 0 and F_shared >= 0");
+    if (d->k < 1 || d->k > d->M)
+        return fail(MOE_ERR_INVALID, "k=%d must be in [1, M=%lld]", d->k, (long long)d->M);
+    if (d->scorer != MOE_SCORER_SOFTMAX && d->scorer != MOE_SCORER_SIGMOID)
+        return fail(MOE_ERR_INVALID, "unknown scorer %d", d->scorer);
+    if (d->act != MOE_ACT_SWIGLU && d->act != MOE_ACT_GELU)
+        return fail(MOE_ERR_INVALID, "unknown activation %d", d->act);
+    if (d->dtype != MOE_DTYPE_F32 && d->dtype != MOE_DTYPE_BF16)
+        return fail(MOE_ERR_INVALID, "unknown dtype %d", d->dtype);
+    if (d->renorm != 0 && d->renorm != 1) return fail(MOE_ERR_INVALID, "renorm must be 0 or 1");
+    if (!(d->eps >= 0.f) || d->alpha != d->alpha)
+        return fail(MOE_ERR_INVALID, "eps must be >= 0 and alpha a number");
+    if (d->k > MOE_MAX_K) return fail(MOE_ERR_UNSUPPORTED, "k=%d > %d", d->k, MOE_MAX_K);
+    if (d->M > MOE_MAX_EXPERTS)
+        return fail(MOE_ERR_UNSUPPORTED, "M=%lld > %d", (long long)d->M, MOE_MAX_EXPERTS);
+    if (d->D % 8 || d->F % 8 || d->F_shared % 8)
+        return fail(MOE_ERR_UNSUPPORTED, "D, F and F_shared must be multiples of 8");
+    const int64_t lim = 0x7fffffffLL;
+    if (d->T * (int64_t)d->k > lim || d->T > lim / 2)
+        return fail(MOE_ERR_UNSUPPORTED, "T*k exceeds int32 indexing");
+    if (d->D > lim / 16 || d->F > lim / 16 || d->F_shared > lim / 16)
+        return fail(MOE_ERR_UNSUPPORTED, "D/F too large");
+    return MOE_OK;
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev) {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+}  // namespace
+
+struct moe_handle {
+    int device = 0;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    // profiling
+    bool prof_on = false;
+    std::string prof_filter;
+    std::vector<hipEvent_t> prof_events;   // 2 per record
+    std::vector<int> prof_labels;
+    int prof_used = 0;
+    int64_t launches[L_COUNT] = {};
+    double total_ms[L_COUNT] = {};
+};
+
+namespace {
+
+// Launch through `fn` with optional timing events around it.
+template <class Fn>
+int run(moe_handle* h, hipStream_t s, int label, Fn&& fn) {
+    const bool rec = h->prof_on && h->prof_used < (int)h->prof_labels.size() &&
+                     (h->prof_filter.empty() ||
+                      std::strstr(kLabels[label], h->prof_filter.c_str()) != nullptr);
+    if (rec) {
+        if (hipEventRecord(h->prof_events[2 * h->prof_used], s) != hipSuccess)
+            return fail(MOE_ERR_HIP, "hipEventRecord failed");
+    }
+    const hipError_t e = fn();
+    if (e != hipSuccess)
+        return fail(MOE_ERR_HIP, "%s launch: %s", kLabels[label], hipGetErrorString(e));
+    if (rec) {
+        if (hipEventRecord(h->prof_events[2 * h->prof_used + 1], s) != hipSuccess)
+            return fail(MOE_ERR_HIP, "hipEventRecord failed");
+        h->prof_labels[h->prof_used++] = label;
+    }
+    return MOE_OK;
+}
+
+#define TRY(x)                        \
+    do {                              \
+        const int _rc = (x);          \
+        if (_rc != MOE_OK) return _rc; \
+    } while (0)
+
+int check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
+    if (ws_bytes < p.total)
+        return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.total);
+    if (p.total > 0 && !ws) return fail(MOE_ERR_INVALID, "workspace pointer is NULL");
+    return MOE_OK;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// Stage bodies (no validation).
+int do_route(moe_handle* h, const moe_desc* d, const void* x, const float* W_r, const float* bias,
+             int32_t* idx, float* w, hipStream_t s) {
+    return run(h, s, L_ROUTE, [&] {
+        return launch_route(s, d->dtype, d->scorer, x, W_r, bias, idx, w, d->T, d->D, d->M, d->k,
+                            d->renorm, d->alpha, d->eps);
+    });
+}
+
+int do_permute(moe_handle* h, const moe_desc* d, const Plan& p, const int32_t* idx,
+               int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* sorted_slot,
+               int32_t* slot_row, void* ws, hipStream_t s) {
+    int32_t* hist = at<int32_t>(ws, p.hist);
+    TRY(run(h, s, L_PERM_COUNT, [&] { return launch_perm_count(s, idx, hist, d->T, d->k, d->M); }));
+    TRY(run(h, s, L_PERM_SCAN, [&] {
+        return launch_perm_scan(s, hist, p.nblk, d->T, d->k, d->M, counts, offsets, sorted_token,
+                                sorted_slot);
+    }));
+    return run(h, s, L_PERM_SCATTER, [&] {
+        return launch_perm_scatter(s, idx, hist, offsets, d->T, d->k, d->M, sorted_token,
+                                   sorted_slot, slot_row);
+    });
+}
+
+int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x,
+                  const int32_t* sorted_token, const int32_t* sorted_slot, const int32_t* offsets,
+                  const float* w, const void* W1, const void* b1, const void* W2, const void* b2,
+                  void* O, void* ws, hipStream_t s) {
+    int32_t* tiles = at<int32_t>(ws, p.tiles);
+    void* H = at<char>(ws, p.H);
+    TRY(run(h, s, L_TILE_TABLE,
+            [&] { return launch_tile_table(s, offsets, d->M, p.bm, p.max_tiles, tiles); }));
+    const bool swiglu = d->act == MOE_ACT_SWIGLU;
+    GemmArgs up{};
+    up.a = x;
+    up.gather = sorted_token;
+    up.b = W1;
+    up.b_stride = (swiglu ? 2 : 1) * d->F * d->D;
+    up.bias = swiglu ? nullptr : b1;
+    up.c = H;
+    up.tiles = tiles;
+    up.offsets = offsets;
+    up.K = (int)d->D;
+    up.N = (int)d->F;
+    up.F_split = (int)d->F;
+    TRY(run(h, s, L_FFN_UP, [&] {
+        return launch_gemm(s, d->dtype, swiglu ? EPI_SWIGLU : EPI_GELU, up, p.max_tiles);
+    }));
+    GemmArgs dn{};
+    dn.a = H;
+    dn.b = W2;
+    dn.b_stride = d->D * d->F;
+    dn.bias = swiglu ? nullptr : b2;
+    dn.row_w = w;
+    dn.row_slot = sorted_slot;
+    dn.c = O;
+    dn.tiles = tiles;
+    dn.offsets = offsets;
+    dn.K = (int)d->F;
+    dn.N = (int)d->D;
+    return run(h, s, L_FFN_DOWN,
+               [&] { return launch_gemm(s, d->dtype, EPI_DOWN_SCALED, dn, p.max_tiles); });
+}
+
+int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, const void* Wgu,
+              const void* Wdn, float* Ysh, void* ws, hipStream_t s) {
+    void* Hsh = at<char>(ws, p.Hsh);
+    const int64_t mt = (d->T + p.bm - 1) / p.bm;
+    GemmArgs up{};
+    up.a = x;
+    up.b = Wgu;
+    up.c = Hsh;
+    up.dense_rows = d->T;
+    up.K = (int)d->D;
+    up.N = (int)d->F_shared;
+    up.F_split = (int)d->F_shared;
+    TRY(run(h, s, L_SHARED_UP, [&] { return launch_gemm(s, d->dtype, EPI_SWIGLU, up, mt); }));
+    GemmArgs dn{};
+    dn.a = Hsh;
+    dn.b = Wdn;
+    dn.c = Ysh;
+    dn.dense_rows = d->T;
+    dn.K = (int)d->F_shared;
+    dn.N = (int)d->D;
+    return run(h, s, L_SHARED_DOWN, [&] { return launch_gemm(s, d->dtype, EPI_DOWN_F32, dn, mt); });
+}
+
+int do_combine(moe_handle* h, const moe_desc* d, const void* O, const int32_t* slot_row,
+               const float* Ysh, void* y, hipStream_t s) {
+    return run(h, s, L_COMBINE,
+               [&] { return launch_combine(s, d->dtype, O, slot_row, Ysh, y, d->T, d->k, d->D); });
+}
+
+#define CHECK_HANDLE(h)                                                      \
+    do {                                                                     \
+        if (!(h)) return fail(MOE_ERR_INVALID, "handle is NULL");            \
+    } while (0)
+#define NEED(p, name)                                                        \
+    do {                                                                     \
+        if (!(p)) return fail(MOE_ERR_INVALID, "%s is NULL", name);          \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID: return "MOE_ERR_INVALID";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+const char* moe_last_error_detail(void) { return g_detail.c_str(); }
+
+int moe_create(int device, moe_handle** out) {
+    if (!out) return fail(MOE_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDeviceCount: %s", hipGetErrorString(e));
+    if (device < 0 || device >= n)
+        return fail(MOE_ERR_INVALID, "device %d not in [0, %d)", device, n);
+    DeviceGuard g(device);
+    if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+    moe_handle* h = new moe_handle();
+    h->device = device;
+    if ((e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming)) != hipSuccess) {
+        if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+        delete h;
+        return fail(MOE_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+    *out = h;
+    return MOE_OK;
+}
+
+int moe_destroy(moe_handle* h) {
+    if (!h) return MOE_OK;
+    {
+        DeviceGuard g(h->device);
+        if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+        if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+        for (hipEvent_t ev : h->prof_events) (void)hipEventDestroy(ev);
+    }
+    delete h;
+    return MOE_OK;
+}
+
+int moe_workspace_size(const moe_desc* d, size_t* bytes) {
+    if (!bytes) return fail(MOE_ERR_INVALID, "bytes is NULL");
+    TRY(validate(d));
+    *bytes = make_plan(d).total;
+    return MOE_OK;
+}
+
+int moe_route(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
+              const float* bias, int32_t* idx, float* w, void* stream) {
+    CHECK_HANDLE(h);
+    TRY(validate(d));
+    if (d->T == 0) return MOE_OK;
+    NEED(x, "x");
+    NEED(W_r, "W_r");
+    NEED(idx, "idx");
+    NEED(w, "w");
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+    return do_route(h, d, x, W_r, bias, idx, w, static_cast<hipStream_t>(stream));
+}
+
+int moe_permute(moe_handle* h, const moe_desc* d, const int32_t* idx, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_token, int32_t* sorted_slot, int32_t* slot_row,
+                void* ws, size_t ws_bytes, void* stream) {
+    CHECK_HANDLE(h);
+    TRY(validate(d));
+    if (d->T == 0) return MOE_OK;
+    NEED(idx, "idx");
+    NEED(counts, "counts");
+    NEED(offsets, "offsets");
+    NEED(sorted_token, "sorted_token");
+    NEED(sorted_slot, "sorted_slot");
+    NEED(slot_row, "slot_row");
+    const Plan p = make_plan(d);
+    TRY(check_ws(p, ws, ws_bytes));
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+    return do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws,
+                      static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_ffn(moe_handle* h, const moe_desc* d, const void* x, const int32_t* sorted_token,
+                   const int32_t* sorted_slot, const int32_t* offsets, const float* w,
+                   const void* W1, const void* b1, const void* W2, const void* b2, void* O,
+                   void* ws, size_t ws_bytes, void* stream) {
+    CHECK_HANDLE(h);
+    TRY(validate(d));
+    if (d->T == 0) return MOE_OK;
+    NEED(x, "x");
+    NEED(sorted_token, "sorted_token");
+    NEED(sorted_slot, "sorted_slot");
+    NEED(offsets, "offsets");
+    NEED(w, "w");
+    NEED(W1, "W1");
+    NEED(W2, "W2");
+    NEED(O, "O");
+    const Plan p = make_plan(d);
+    TRY(check_ws(p, ws, ws_bytes));
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+    return do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O, ws,
+                         static_cast<hipStream_t>(stream));
+}
+
+int moe_shared_expert(moe_handle* h, const moe_desc* d, const void* x, const void* Wsh_gu,
+                      const void* Wsh_dn, float* Ysh, void* ws, size_t ws_bytes, void* stream) {
+    CHECK_HANDLE(h);
+    TRY(validate(d));
+    if (d->F_shared <= 0) return fail(MOE_ERR_INVALID, "F_shared is 0: no shared expert");
+    if (d->T == 0) return MOE_OK;
+    NEED(x, "x");
+    NEED(Wsh_gu, "Wsh_gu");
+    NEED(Wsh_dn, "Wsh_dn");
+    NEED(Ysh, "Ysh");
+    const Plan p = make_plan(d);
+    TRY(check_ws(p, ws, ws_bytes));
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+    return do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, static_cast<hipStream_t>(stream));
+}
+
+int moe_combine(moe_handle* h, const moe_desc* d, const void* O, const int32_t* slot_row,
+                const float* Ysh, void* y, void* stream) {
+    CHECK_HANDLE(h);
+    TRY(validate(d));
+    if (d->T == 0) return MOE_OK;
+    NEED(O, "O");
+    NEED(slot_row, "slot_row");
+    NEED(y, "y");
+    if (y == O || y == Ysh) return fail(MOE_ERR_INVALID, "y aliases O or Ysh");
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+    return do_combine(h, d, O, slot_row, Ysh, y, static_cast<hipStream_t>(stream));
+}
+
+int moe_forward(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
+                const float* bias, const void* W1, const void* b1, const void* W2, const void* b2,
+                const void* Wsh_gu, const void* Wsh_dn, void* y, void* ws, size_t ws_bytes,
+                void* stream, void* aux_stream) {
+    CHECK_HANDLE(h);
+    TRY(validate(d));
+    if (d->T == 0) return MOE_OK;
+    NEED(x, "x");
+    NEED(W_r, "W_r");
+    NEED(W1, "W1");
+    NEED(W2, "W2");
+    NEED(y, "y");
+    if (d->F_shared > 0) {
+        NEED(Wsh_gu, "Wsh_gu");
+        NEED(Wsh_dn, "Wsh_dn");
+    }
+    if (y == x) return fail(MOE_ERR_INVALID, "y aliases x");
+    const Plan p = make_plan(d);
+    TRY(check_ws(p, ws, ws_bytes));
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t aux = static_cast<hipStream_t>(aux_stream);
+    int32_t* idx = at<int32_t>(ws, p.idx);
+    float* w = at<float>(ws, p.w);
+    int32_t* counts = at<int32_t>(ws, p.counts);
+    int32_t* offsets = at<int32_t>(ws, p.offsets);
+    int32_t* sorted_token = at<int32_t>(ws, p.sorted_token);
+    int32_t* sorted_slot = at<int32_t>(ws, p.sorted_slot);
+    int32_t* slot_row = at<int32_t>(ws, p.slot_row);
+    void* O = at<char>(ws, p.O);
+    float* Ysh = d->F_shared > 0 ? at<float>(ws, p.Ysh) : nullptr;
+
+    const bool fork = Ysh && aux && aux != s;
+    if (Ysh) {
+        if (fork) {
+            hipError_t e;
+            if ((e = hipEventRecord(h->ev_fork, s)) != hipSuccess ||
+                (e = hipStreamWaitEvent(aux, h->ev_fork, 0)) != hipSuccess)
+                return fail(MOE_ERR_HIP, "stream fork: %s", hipGetErrorString(e));
+            TRY(do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, aux));
+            if ((e = hipEventRecord(h->ev_join, aux)) != hipSuccess)
+                return fail(MOE_ERR_HIP, "stream join: %s", hipGetErrorString(e));
+        } else {
+            TRY(do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, s));
+        }
+    }
+    TRY(do_route(h, d, x, W_r, bias, idx, w, s));
+    TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
+    TRY(do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O, ws, s));
+    if (fork) {
+        const hipError_t e = hipStreamWaitEvent(s, h->ev_join, 0);
+        if (e != hipSuccess) return fail(MOE_ERR_HIP, "stream join: %s", hipGetErrorString(e));
+    }
+    return do_combine(h, d, O, slot_row, Ysh, y, s);
+}
+
+int moe_profile_start(moe_handle* h, int capacity, const char* filter) {
+    CHECK_HANDLE(h);
+    if (capacity < 0) return fail(MOE_ERR_INVALID, "capacity < 0");
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+    while ((int)h->prof_events.size() < 2 * capacity) {
+        hipEvent_t ev;
+        const hipError_t e = hipEventCreate(&ev);
+        if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+        h->prof_events.push_back(ev);
+    }
+    h->prof_labels.assign(capacity, 0);
+    h->prof_used = 0;
+    h->prof_filter = filter ? filter : "";
+    for (int i = 0; i < L_COUNT; ++i) {
+        h->launches[i] = 0;
+        h->total_ms[i] = 0.0;
+    }
+    h->prof_on = true;
+    return MOE_OK;
+}
+
+int moe_profile_stop(moe_handle* h) {
+    CHECK_HANDLE(h);
+    h->prof_on = false;
+    DeviceGuard g(h->device);
+    for (int i = 0; i < h->prof_used; ++i) {
+        hipError_t e = hipEventSynchronize(h->prof_events[2 * i + 1]);
+        float ms = 0.f;
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&ms, h->prof_events[2 * i], h->prof_events[2 * i + 1]);
+        if (e != hipSuccess) return fail(MOE_ERR_HIP, "profile events: %s", hipGetErrorString(e));
+        h->launches[h->prof_labels[i]] += 1;
+        h->total_ms[h->prof_labels[i]] += ms;
+    }
+    h->prof_used = 0;
+    return MOE_OK;
+}
+
+int moe_profile_results(moe_handle* h, moe_kernel_time* out, int max_entries, int* n_entries) {
+    CHECK_HANDLE(h);
+    if (!n_entries || (max_entries > 0 && !out)) return fail(MOE_ERR_INVALID, "NULL output");
+    int n = 0;
+    for (int i = 0; i < L_COUNT; ++i) {
+        if (h->launches[i] == 0) continue;
+        if (n < max_entries) {
+            std::memset(out[n].label, 0, sizeof out[n].label);
+            std::strncpy(out[n].label, kLabels[i], sizeof out[n].label - 1);
+            out[n].launches = h->launches[i];
+            out[n].total_ms = h->total_ms[i];
+        }
+        ++n;
+    }
+    *n_entries = n;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Internal definitions shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bf16 bit pattern
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 1024;   // MOE_MAX_EXPERTS
+constexpr int kMaxK = 16;           // MOE_MAX_K
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+    return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
+        return static_cast<bf16_t>((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Activations in fp32.
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float gelu_erf_f32(float z) {
+    return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+
+// Kernel labels (indices into the profiling table).
+enum Label : int {
+    L_ROUTE = 0, L_PERM_COUNT, L_PERM_SCAN, L_PERM_SCATTER, L_TILE_TABLE,
+    L_FFN_UP, L_FFN_DOWN, L_SHARED_UP, L_SHARED_DOWN, L_COMBINE, L_COUNT
+};
+
+// Epilogues of the expert GEMMs.
+enum Epi : int {
+    EPI_SWIGLU = 0,      // out[r, n] = silu(gate) * up            -> dtype
+    EPI_GELU = 1,        // out[r, n] = gelu(acc + b1[e, n])       -> dtype
+    EPI_DOWN_SCALED = 2, // out[r, n] = w[slot(r)] * (acc + b2[e, n]) -> dtype
+    EPI_DOWN_F32 = 3     // out[r, n] = acc                         -> fp32
+};
+
+// One expert GEMM launch: C[rows, N] = epi(A[rows, K] . B[e]^T), where
+// A rows come from `a` (through `gather` when non-null) and B[e] is the
+// expert's [NB, K] row-major weight block.
+struct GemmArgs {
+    const void* a;            // [*, K] dtype
+    const int32_t* gather;    // A row of sorted row r = gather[r]; NULL: r itself
+    const void* b;            // [E, NB, K] dtype
+    int64_t b_stride;         // elements between experts in b
+    const void* bias;         // [E, N] dtype, nullable (GELU b1 or DOWN b2)
+    const float* row_w;       // per flat slot weight (DOWN_SCALED)
+    const int32_t* row_slot;  // flat slot of sorted row r (DOWN_SCALED)
+    void* c;                  // [rows, N]
+    const int32_t* tiles;     // grouped: per m-tile (expert, row0); NULL: dense
+    const int32_t* offsets;   // grouped: expert row ranges [M+1]
+    int64_t dense_rows;       // dense: total rows
+    int K;                    // reduction length
+    int N;                    // output columns
+    int F_split;              // SWIGLU: row offset of the up block in B (= N)
+};
+
+}  // namespace moe
+
+// Host-side launchers (defined in the .hip files, called by the ABI layer).
+namespace moe {
+hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, const float* W_r,
+                        const float* bias, int32_t* idx, float* w, int64_t T, int64_t D,
+                        int64_t M, int k, int renorm, float alpha, float eps);
+hipError_t launch_perm_count(hipStream_t s, const int32_t* idx, int32_t* hist, int64_t T, int k,
+                             int64_t M);
+hipError_t launch_perm_scan(hipStream_t s, int32_t* hist, int64_t nblk, int64_t T, int k,
+                            int64_t M, int32_t* counts, int32_t* offsets, int32_t* sorted_token,
+                            int32_t* sorted_slot);
+hipError_t launch_perm_scatter(hipStream_t s, const int32_t* idx, const int32_t* hist,
+                               const int32_t* offsets, int64_t T, int k, int64_t M,
+                               int32_t* sorted_token, int32_t* sorted_slot, int32_t* slot_row);
+hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M, int bm,
+                             int64_t max_tiles, int32_t* tiles);
+hipError_t launch_gemm(hipStream_t s, int dtype, int epi, const GemmArgs& g, int64_t m_tiles);
+hipError_t launch_combine(hipStream_t s, int dtype, const void* O, const int32_t* slot_row,
+                          const float* Ysh, void* y, int64_t T, int k, int64_t D);
+
+// Tile geometry of the expert GEMMs (rows per m-tile) for a dtype.
+int gemm_block_m(int dtype);
+// Token block of the permute kernels.
+constexpr int kPermBlock = 256;
+}  // namespace moe

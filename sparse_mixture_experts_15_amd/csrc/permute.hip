@@ -1,0 +1,209 @@
+// Dispatch: group the T*k flat routing slots f = t*k + j by expert, stably
+// (the "dispatch / expert batching" part of the routing overhead in the
+// GLaM study note's "Capacity, Active Compute, and Reporting" table; the
+// GLM-5 routed-experts excerpt gathers each expert's tokens the same way,
+// with an extra one-hot class, index M, that is skipped).
+//
+// Three kernels, no global atomics:
+//  1. count:   per block of 256 tokens, an LDS histogram over experts.
+//  2. scan:    one workgroup turns the block histograms into per-block
+//              bases (exclusive over blocks) and the expert counts into
+//              offsets (exclusive over experts); marks unused tail rows.
+//  3. scatter: per block, each wave sets bit `lane` of a 64-bit LDS mask
+//              per expert its token picked; a slot's rank among earlier
+//              slots of the same expert is the popcount of the lower lanes'
+//              bits plus the masks of the lower waves.  A token picks an
+//              expert at most once, so this is exactly the stable order.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(kPermBlock) void perm_count(const int32_t* __restrict__ idx,
+                                                        int32_t* __restrict__ hist, int T, int k,
+                                                        int M) {
+    extern __shared__ int32_t s_cnt[];   // [M]
+    for (int e = threadIdx.x; e < M; e += kPermBlock) s_cnt[e] = 0;
+    __syncthreads();
+    const int t = blockIdx.x * kPermBlock + threadIdx.x;
+    if (t < T) {
+        for (int j = 0; j < k; ++j) {
+            const int e = idx[(int64_t)t * k + j];
+            if (e >= 0 && e < M) atomicAdd(&s_cnt[e], 1);
+        }
+    }
+    __syncthreads();
+    int32_t* h = hist + (int64_t)blockIdx.x * M;
+    for (int e = threadIdx.x; e < M; e += kPermBlock) h[e] = s_cnt[e];
+}
+
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void perm_scan(int32_t* __restrict__ hist, int nblk,
+                                                         int T, int k, int M,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ sorted_token,
+                                                         int32_t* __restrict__ sorted_slot) {
+    __shared__ int32_t s_tot[kMaxExperts];
+    __shared__ int32_t s_warp[kScanThreads / 64];
+    const int tid = threadIdx.x;
+    // per expert: exclusive running sum over blocks, in block order
+    for (int e = tid; e < M; e += kScanThreads) {
+        int32_t run = 0;
+        for (int b = 0; b < nblk; ++b) {
+            int32_t* p = hist + (int64_t)b * M + e;
+            const int32_t v = *p;
+            *p = run;
+            run += v;
+        }
+        counts[e] = run;
+        s_tot[e] = run;
+    }
+    __syncthreads();
+    // exclusive scan of counts over experts (M <= 1024: one value per thread)
+    const int32_t v = (tid < M) ? s_tot[tid] : 0;
+    int32_t incl = v;
+    const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_warp[wv] = incl;
+    __syncthreads();
+    int32_t base = 0;
+    for (int i = 0; i < wv; ++i) base += s_warp[i];
+    incl += base;
+    if (tid < M) offsets[tid] = incl - v;
+    if (tid == M - 1) offsets[M] = incl;
+    __syncthreads();
+    // rows past the kept slots (dropped slots only) are marked -1
+    int32_t total = 0;
+    for (int i = 0; i < kScanThreads / 64; ++i) total += s_warp[i];
+    const int64_t S = (int64_t)T * k;
+    for (int64_t r = total + tid; r < S; r += kScanThreads) {
+        sorted_token[r] = -1;
+        sorted_slot[r] = -1;
+    }
+}
+
+__global__ __launch_bounds__(kPermBlock) void perm_scatter(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ hist,
+    const int32_t* __restrict__ offsets, int T, int k, int M, int32_t* __restrict__ sorted_token,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row) {
+    extern __shared__ unsigned long long s_mask[];   // [4][M]
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    for (int i = tid; i < 4 * M; i += kPermBlock) s_mask[i] = 0ull;
+    __syncthreads();
+    const int t = blockIdx.x * kPermBlock + tid;
+    int e_of[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) e_of[j] = -1;
+    if (t < T) {
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j < k) {
+                const int e = idx[(int64_t)t * k + j];
+                if (e >= 0 && e < M) {
+                    e_of[j] = e;
+                    atomicOr(&s_mask[wv * M + e], 1ull << lane);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (t >= T) return;
+    const int32_t* hb = hist + (int64_t)blockIdx.x * M;
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j >= k) break;
+        const int64_t f = (int64_t)t * k + j;
+        const int e = e_of[j];
+        if (e < 0) {
+            slot_row[f] = -1;
+            continue;
+        }
+        int rank = __popcll(s_mask[wv * M + e] & below);
+        for (int w2 = 0; w2 < wv; ++w2) rank += __popcll(s_mask[w2 * M + e]);
+        const int32_t r = offsets[e] + hb[e] + rank;
+        sorted_slot[r] = (int32_t)f;
+        sorted_token[r] = t;
+        slot_row[f] = r;
+    }
+}
+
+// Per m-tile of `bm` rows: (expert, first row).  Tiles are laid out expert
+// after expert; entries past the last tile are (-1, 0).  One thread per
+// expert writes its own tiles after a scan of the tile counts.
+__global__ __launch_bounds__(kScanThreads) void tile_table(const int32_t* __restrict__ offsets,
+                                                          int M, int bm, int max_tiles,
+                                                          int32_t* __restrict__ tiles) {
+    __shared__ int32_t s_warp[kScanThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int32_t nt = 0, r0 = 0;
+    if (tid < M) {
+        r0 = offsets[tid];
+        nt = (offsets[tid + 1] - r0 + bm - 1) / bm;
+    }
+    int32_t incl = nt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_warp[wv] = incl;
+    __syncthreads();
+    int32_t base = 0, total = 0;
+    for (int i = 0; i < kScanThreads / 64; ++i) {
+        if (i < wv) base += s_warp[i];
+        total += s_warp[i];
+    }
+    const int32_t first = base + incl - nt;
+    for (int i = 0; i < nt; ++i) {
+        tiles[2 * (first + i)] = tid;
+        tiles[2 * (first + i) + 1] = r0 + i * bm;
+    }
+    for (int i = total + tid; i < max_tiles; i += kScanThreads) {
+        tiles[2 * i] = -1;
+        tiles[2 * i + 1] = 0;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_perm_count(hipStream_t s, const int32_t* idx, int32_t* hist, int64_t T, int k,
+                             int64_t M) {
+    const int nblk = (int)((T + kPermBlock - 1) / kPermBlock);
+    hipLaunchKernelGGL(perm_count, dim3(nblk), dim3(kPermBlock), M * sizeof(int32_t), s, idx,
+                       hist, (int)T, k, (int)M);
+    return hipGetLastError();
+}
+
+hipError_t launch_perm_scan(hipStream_t s, int32_t* hist, int64_t nblk, int64_t T, int k,
+                            int64_t M, int32_t* counts, int32_t* offsets, int32_t* sorted_token,
+                            int32_t* sorted_slot) {
+    hipLaunchKernelGGL(perm_scan, dim3(1), dim3(kScanThreads), 0, s, hist, (int)nblk, (int)T, k,
+                       (int)M, counts, offsets, sorted_token, sorted_slot);
+    return hipGetLastError();
+}
+
+hipError_t launch_perm_scatter(hipStream_t s, const int32_t* idx, const int32_t* hist,
+                               const int32_t* offsets, int64_t T, int k, int64_t M,
+                               int32_t* sorted_token, int32_t* sorted_slot, int32_t* slot_row) {
+    const int nblk = (int)((T + kPermBlock - 1) / kPermBlock);
+    hipLaunchKernelGGL(perm_scatter, dim3(nblk), dim3(kPermBlock),
+                       4 * M * sizeof(unsigned long long), s, idx, hist, offsets, (int)T, k,
+                       (int)M, sorted_token, sorted_slot, slot_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M, int bm,
+                             int64_t max_tiles, int32_t* tiles) {
+    hipLaunchKernelGGL(tile_table, dim3(1), dim3(kScanThreads), 0, s, offsets, (int)M, bm,
+                       (int)max_tiles, tiles);
+    return hipGetLastError();
+}
+
+}  // namespace moe

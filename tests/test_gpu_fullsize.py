@@ -1,0 +1,75 @@
+"""Parity at the full layer sizes, through moe_forward with the shared
+expert on a second stream (the configuration the benchmark times).
+
+Every token's top-k and the whole dispatch are compared bit-exactly with
+the oracle (tie rule aside); the layer output is compared on a sample of
+tokens the oracle evaluates one by one: the first token of each of several
+experts (cold and hot) plus a seeded random fill.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import (assert_close_rms, check_dispatch_props, check_route, forward,
+                            gpu_permute, new_layer, run_route, to_np, tol)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_tokens(cfg, disp, n_random=24, n_expert=24, seed=0):
+    offs, st = disp["offsets"], disp["sorted_token"]
+    touched = [e for e in range(cfg.M) if offs[e + 1] > offs[e]]
+    by_count = sorted(touched, key=lambda e: offs[e + 1] - offs[e])
+    pick = by_count[: n_expert // 2] + by_count[-(n_expert // 2):]
+    toks = {int(st[offs[e]]) for e in pick}
+    toks |= {int(st[offs[e + 1] - 1]) for e in pick}
+    rng = np.random.default_rng(seed)
+    toks |= set(rng.choice(cfg.T, size=min(n_random, cfg.T), replace=False).tolist())
+    toks |= {0, cfg.T - 1}
+    return np.array(sorted(toks), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "glm45", "glam", "glm5"])
+def test_full_size_forward(name):
+    cfg = workloads.get(name)
+    print(f"full-size parity: {cfg.name}", flush=True)
+    t = workloads.generate(cfg, seed=0, device="cuda")
+    L = new_layer(cfg)
+    aux = torch.cuda.Stream()
+    y = forward(L, t, aux=aux)
+    idx_g, w_g = run_route(L, L.desc, t)
+    pg = gpu_permute(L, L.desc, idx_g)
+    torch.cuda.synchronize()
+    yh = to_np(y.float()).reshape(cfg.T, cfg.D)
+    assert np.isfinite(yh).all()
+    pg = {k: to_np(v) for k, v in pg.items()}
+    idx_gh = to_np(idx_g).reshape(cfg.T, cfg.k)
+    w_gh = to_np(w_g)
+    del y
+    h = workloads.host_inputs(t)
+    del t
+    gc.collect()
+    torch.cuda.empty_cache()
+
+    idx_o, w_o, gap_o, sel_o = oracle.route(cfg, h["x"], h["W_r"], h["bias"], want_sel=True)
+    mism = check_route(cfg, idx_gh, w_gh, idx_o, w_o, gap_o, sel_o)
+    check_dispatch_props(cfg, idx_gh, pg)
+    disp_o = oracle.dispatch(cfg.T, cfg.k, cfg.M, idx_o)
+    if not mism.any():
+        for key in disp_o:
+            assert (pg[key] == disp_o[key]).all(), key
+    print(f"  touched experts {int((disp_o['counts'] > 0).sum())}/{cfg.M}, max count "
+          f"{int(disp_o['counts'].max())}, tie-exempt mismatches {int(mism.sum())}", flush=True)
+
+    toks = _sample_tokens(cfg, disp_o)
+    toks = toks[~mism[toks]]
+    y_o = oracle.layer(cfg, h["x"], idx_o, w_o, h["W1"], h["b1"], h["W2"], h["b2"],
+                       h["Wsh_gu"], h["Wsh_dn"], tokens=toks)
+    err, scale = assert_close_rms(yh[toks], y_o, tol(cfg), f"{cfg.name} y on {len(toks)} tokens")
+    print(f"  y max|err| {err:.3e}  RMS {scale:.3e}  ratio {err / scale:.2e}", flush=True)
+    del h
+    gc.collect()
