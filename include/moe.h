@@ -25,10 +25,11 @@
  * - Every data pointer is a DEVICE pointer to a dense, row-major, contiguous
  *   buffer that the caller allocated and owns, 16-byte aligned.  The library
  *   never allocates, frees or keeps a caller pointer past the call.
- * - `dtype` types x, the expert weights W1/b1/W2/b2, the shared weights, the
- *   sorted expert outputs O and y: fp32 (MOE_DTYPE_F32) or bf16
- *   (MOE_DTYPE_BF16, stored as raw uint16 bit patterns).  W_r, bias, w and
- *   Ysh are always fp32; indices are int32.
+ * - `dtype` types x, the expert weights W1/b1/W2/b2 and the shared weights:
+ *   fp32 (MOE_DTYPE_F32) or bf16 (MOE_DTYPE_BF16, stored as raw uint16 bit
+ *   patterns).  `out_dtype` types y.  W_r, bias, w, the sorted expert
+ *   outputs O and the shared-expert output Ysh are always fp32; indices are
+ *   int32.
  * - `stream` / `aux_stream` are hipStream_t values passed as void*; NULL is
  *   the null stream.  All work is enqueued asynchronously; no call copies
  *   between host and device or synchronises the host, so results are valid
@@ -74,7 +75,9 @@ enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
  *   D        hidden size;  M routed experts;  F routed expert width
  *   F_shared shared SwiGLU width (n_shared * expert width; 0 = none)
  *   k        experts per token (1..min(M,16))
- *   scorer   MOE_SCORER_*;  act MOE_ACT_*;  dtype MOE_DTYPE_*
+ *   scorer   MOE_SCORER_*;  act MOE_ACT_*;  dtype MOE_DTYPE_* (inputs)
+ *   out_dtype MOE_DTYPE_* of y (the reference layer returns y in the input
+ *            dtype; fp32 keeps the fp32 accumulation unrounded)
  *   renorm   1: divide the selected gate values by their sum + eps
  *   alpha    routed scaling factor (multiplies every routed weight)
  *   eps      renormalisation epsilon (1e-20 in the GLM-4.5 note)          */
@@ -84,6 +87,7 @@ typedef struct moe_desc {
     int32_t scorer;
     int32_t act;
     int32_t dtype;
+    int32_t out_dtype;
     int32_t renorm;
     float alpha;
     float eps;
@@ -133,12 +137,12 @@ int moe_permute(moe_handle* h, const moe_desc* d, const int32_t* idx, int32_t* c
  *   O[r,:] = w[f] * E_e(x[t,:])
  * W1[M,G*F,D] (SWIGLU: G = 2, gate rows 0..F-1 then up rows F..2F-1;
  * GELU: G = 1), b1[M,F] and b2[M,D] (GELU only, NULL = zero), W2[M,D,F],
- * w[T*k] fp32 indexed by flat slot, O[T*k,D] (dtype; rows >= offsets[M]
- * untouched).  Uses workspace for the hidden activations. */
+ * w[T*k] fp32 indexed by flat slot, O[T*k,D] fp32 (rows >= offsets[M]
+ * untouched).  The hidden activations (dtype) live in the workspace. */
 int moe_expert_ffn(moe_handle* h, const moe_desc* d, const void* x,
                    const int32_t* sorted_token, const int32_t* sorted_slot,
                    const int32_t* offsets, const float* w, const void* W1,
-                   const void* b1, const void* W2, const void* b2, void* O,
+                   const void* b1, const void* W2, const void* b2, float* O,
                    void* ws, size_t ws_bytes, void* stream);
 
 /* Shared expert on every token's pre-routing x ["Shared Expert" GLM-4.5
@@ -152,16 +156,17 @@ int moe_shared_expert(moe_handle* h, const moe_desc* d, const void* x,
 
 /* Combine [GLaM MoE output sum; GLM-4.5 "How it works" output equation]:
  *   y[t,:] = sum_{j<k} O[slot_row[t*k+j], :]  (+ Ysh[t,:] if Ysh != NULL)
- * summed in fp32 in fixed j order, then rounded once to dtype.  A slot with
- * slot_row < 0 contributes nothing.  No atomics.  y must not alias O or Ysh. */
-int moe_combine(moe_handle* h, const moe_desc* d, const void* O, const int32_t* slot_row,
+ * summed in fp32 in fixed j order, then rounded once to out_dtype.  O[T*k,D]
+ * fp32.  A slot with slot_row < 0 contributes nothing.  No atomics.  y must
+ * not alias O or Ysh. */
+int moe_combine(moe_handle* h, const moe_desc* d, const float* O, const int32_t* slot_row,
                 const float* Ysh, void* y, void* stream);
 
 /* Whole layer: route, permute, expert FFNs, shared expert, combine.
  * The shared expert runs on `aux_stream` (forked from and joined back into
  * `stream` with events) so it overlaps the routed path; aux_stream == NULL
- * runs it on `stream`, with bitwise-identical results.  y[T,D] (dtype) must
- * not alias x.  Shared weights may be NULL only when F_shared == 0. */
+ * runs it on `stream`, with bitwise-identical results.  y[T,D] (out_dtype)
+ * must not alias x.  Shared weights may be NULL only when F_shared == 0. */
 int moe_forward(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
                 const float* bias, const void* W1, const void* b1, const void* W2,
                 const void* b2, const void* Wsh_gu, const void* Wsh_dn, void* y,

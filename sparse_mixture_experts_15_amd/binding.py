@@ -33,7 +33,7 @@ class moe_desc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("D", ctypes.c_int64), ("M", ctypes.c_int64),
                 ("F", ctypes.c_int64), ("F_shared", ctypes.c_int64), ("k", ctypes.c_int32),
                 ("scorer", ctypes.c_int32), ("act", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("renorm", ctypes.c_int32), ("alpha", ctypes.c_float), ("eps", ctypes.c_float)]
+                ("out_dtype", ctypes.c_int32), ("renorm", ctypes.c_int32), ("alpha", ctypes.c_float), ("eps", ctypes.c_float)]
 
 
 class moe_kernel_time(ctypes.Structure):
@@ -105,7 +105,8 @@ def _check(fn: str, rc: int):
 def make_desc(cfg=None, **kw) -> moe_desc:
     """Descriptor from a layer config object (T, D, M, F, F_shared, k,
     scorer, act, dtype, renorm, alpha, eps) with keyword overrides; enum
-    fields accept their names ("softmax", "swiglu", "bf16", ...)."""
+    fields accept their names ("softmax", "swiglu", "bf16", ...).  out_dtype
+    defaults to dtype."""
     f = {}
     if cfg is not None:
         for n in ("T", "D", "M", "F", "F_shared", "k", "scorer", "act", "dtype", "renorm",
@@ -113,9 +114,11 @@ def make_desc(cfg=None, **kw) -> moe_desc:
             f[n] = getattr(cfg, n)
     f.update(kw)
     sc, ac, dt = f["scorer"], f["act"], f["dtype"]
+    od = f.get("out_dtype", dt)
     return moe_desc(T=int(f["T"]), D=int(f["D"]), M=int(f["M"]), F=int(f["F"]),
                     F_shared=int(f.get("F_shared", 0)), k=int(f["k"]),
                     scorer=SCORER.get(sc, sc), act=ACT.get(ac, ac), dtype=DTYPE.get(dt, dt),
+                    out_dtype=DTYPE.get(od, od),
                     renorm=int(bool(f.get("renorm", 1))), alpha=float(f.get("alpha", 1.0)),
                     eps=float(f.get("eps", 1e-20)))
 
@@ -144,6 +147,10 @@ def _stream(s):
 
 def _dt(d: moe_desc):
     return _TORCH_OF[d.dtype]
+
+
+def _odt(d: moe_desc):
+    return _TORCH_OF[d.out_dtype]
 
 
 # ---------------------------------------------------------------- entry points
@@ -195,7 +202,8 @@ def moe_expert_ffn(h, d, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b
         _ptr(sorted_slot, "sorted_slot", torch.int32, S),
         _ptr(offsets, "offsets", torch.int32, M + 1), _ptr(w, "w", torch.float32, S),
         _ptr(W1, "W1", dt, M * G * F * D), _ptr(b1, "b1", dt, M * F),
-        _ptr(W2, "W2", dt, M * D * F), _ptr(b2, "b2", dt, M * D), _ptr(O, "O", dt, S * D),
+        _ptr(W2, "W2", dt, M * D * F), _ptr(b2, "b2", dt, M * D),
+        _ptr(O, "O", torch.float32, S * D),
         _ptr(ws, "ws", torch.uint8), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
@@ -210,10 +218,10 @@ def moe_shared_expert(h, d, x, Wsh_gu, Wsh_dn, Ysh, ws, stream=None):
 
 def moe_combine(h, d, O, slot_row, Ysh, y, stream=None):
     T, D, k = d.T, d.D, d.k
-    dt = _dt(d)
     _check("moe_combine", load_library().moe_combine(
-        h, ctypes.byref(d), _ptr(O, "O", dt, T * k * D), _ptr(slot_row, "slot_row", torch.int32, T * k),
-        _ptr(Ysh, "Ysh", torch.float32, T * D), _ptr(y, "y", dt, T * D), _stream(stream)))
+        h, ctypes.byref(d), _ptr(O, "O", torch.float32, T * k * D),
+        _ptr(slot_row, "slot_row", torch.int32, T * k),
+        _ptr(Ysh, "Ysh", torch.float32, T * D), _ptr(y, "y", _odt(d), T * D), _stream(stream)))
 
 
 def moe_forward(h, d, x, W_r, bias, W1, b1, W2, b2, Wsh_gu, Wsh_dn, y, ws, stream=None,
@@ -227,7 +235,7 @@ def moe_forward(h, d, x, W_r, bias, W1, b1, W2, b2, Wsh_gu, Wsh_dn, y, ws, strea
         _ptr(bias, "bias", torch.float32, M), _ptr(W1, "W1", dt, M * G * F * D),
         _ptr(b1, "b1", dt, M * F), _ptr(W2, "W2", dt, M * D * F), _ptr(b2, "b2", dt, M * D),
         _ptr(Wsh_gu, "Wsh_gu", dt, 2 * Fs * D), _ptr(Wsh_dn, "Wsh_dn", dt, D * Fs),
-        _ptr(y, "y", dt, T * D), _ptr(ws, "ws", torch.uint8),
+        _ptr(y, "y", _odt(d), T * D), _ptr(ws, "ws", torch.uint8),
         ws.numel() if ws is not None else 0, _stream(stream), aux))
 
 

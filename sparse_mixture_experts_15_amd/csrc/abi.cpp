@@ -66,7 +66,7 @@ Plan make_plan(const moe_desc* d) {
     p.hist = take((size_t)p.nblk * d->M * 4);
     p.tiles = take((size_t)p.max_tiles * 2 * 4);
     p.H = take((size_t)p.S * d->F * p.esz);
-    p.O = take((size_t)p.S * d->D * p.esz);
+    p.O = take((size_t)p.S * d->D * 4);
     p.Hsh = take((size_t)d->T * d->F_shared * p.esz);
     p.Ysh = take(d->F_shared > 0 ? (size_t)d->T * d->D * 4 : 0);
     p.total = off;
@@ -86,6 +86,8 @@ int validate(const moe_desc* d) {
         return fail(MOE_ERR_INVALID, "unknown activation %d", d->act);
     if (d->dtype != MOE_DTYPE_F32 && d->dtype != MOE_DTYPE_BF16)
         return fail(MOE_ERR_INVALID, "unknown dtype %d", d->dtype);
+    if (d->out_dtype != MOE_DTYPE_F32 && d->out_dtype != MOE_DTYPE_BF16)
+        return fail(MOE_ERR_INVALID, "unknown out_dtype %d", d->out_dtype);
     if (d->renorm != 0 && d->renorm != 1) return fail(MOE_ERR_INVALID, "renorm must be 0 or 1");
     if (!(d->eps >= 0.f) || d->alpha != d->alpha)
         return fail(MOE_ERR_INVALID, "eps must be >= 0 and alpha a number");
@@ -198,7 +200,7 @@ int do_permute(moe_handle* h, const moe_desc* d, const Plan& p, const int32_t* i
 int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x,
                   const int32_t* sorted_token, const int32_t* sorted_slot, const int32_t* offsets,
                   const float* w, const void* W1, const void* b1, const void* W2, const void* b2,
-                  void* O, void* ws, hipStream_t s) {
+                  float* O, void* ws, hipStream_t s) {
     int32_t* tiles = at<int32_t>(ws, p.tiles);
     void* H = at<char>(ws, p.H);
     TRY(run(h, s, L_TILE_TABLE,
@@ -258,10 +260,11 @@ int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, co
     return run(h, s, L_SHARED_DOWN, [&] { return launch_gemm(s, d->dtype, EPI_DOWN_F32, dn, mt); });
 }
 
-int do_combine(moe_handle* h, const moe_desc* d, const void* O, const int32_t* slot_row,
+int do_combine(moe_handle* h, const moe_desc* d, const float* O, const int32_t* slot_row,
                const float* Ysh, void* y, hipStream_t s) {
-    return run(h, s, L_COMBINE,
-               [&] { return launch_combine(s, d->dtype, O, slot_row, Ysh, y, d->T, d->k, d->D); });
+    return run(h, s, L_COMBINE, [&] {
+        return launch_combine(s, d->out_dtype, O, slot_row, Ysh, y, d->T, d->k, d->D);
+    });
 }
 
 #define CHECK_HANDLE(h)                                                      \
@@ -367,7 +370,7 @@ int moe_permute(moe_handle* h, const moe_desc* d, const int32_t* idx, int32_t* c
 
 int moe_expert_ffn(moe_handle* h, const moe_desc* d, const void* x, const int32_t* sorted_token,
                    const int32_t* sorted_slot, const int32_t* offsets, const float* w,
-                   const void* W1, const void* b1, const void* W2, const void* b2, void* O,
+                   const void* W1, const void* b1, const void* W2, const void* b2, float* O,
                    void* ws, size_t ws_bytes, void* stream) {
     CHECK_HANDLE(h);
     TRY(validate(d));
@@ -405,7 +408,7 @@ int moe_shared_expert(moe_handle* h, const moe_desc* d, const void* x, const voi
     return do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, static_cast<hipStream_t>(stream));
 }
 
-int moe_combine(moe_handle* h, const moe_desc* d, const void* O, const int32_t* slot_row,
+int moe_combine(moe_handle* h, const moe_desc* d, const float* O, const int32_t* slot_row,
                 const float* Ysh, void* y, void* stream) {
     CHECK_HANDLE(h);
     TRY(validate(d));
@@ -413,7 +416,8 @@ int moe_combine(moe_handle* h, const moe_desc* d, const void* O, const int32_t* 
     NEED(O, "O");
     NEED(slot_row, "slot_row");
     NEED(y, "y");
-    if (y == O || y == Ysh) return fail(MOE_ERR_INVALID, "y aliases O or Ysh");
+    if (y == static_cast<const void*>(O) || y == static_cast<const void*>(Ysh))
+        return fail(MOE_ERR_INVALID, "y aliases O or Ysh");
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
     return do_combine(h, d, O, slot_row, Ysh, y, static_cast<hipStream_t>(stream));
@@ -450,7 +454,7 @@ int moe_forward(moe_handle* h, const moe_desc* d, const void* x, const float* W_
     int32_t* sorted_token = at<int32_t>(ws, p.sorted_token);
     int32_t* sorted_slot = at<int32_t>(ws, p.sorted_slot);
     int32_t* slot_row = at<int32_t>(ws, p.slot_row);
-    void* O = at<char>(ws, p.O);
+    float* O = at<float>(ws, p.O);
     float* Ysh = d->F_shared > 0 ? at<float>(ws, p.Ysh) : nullptr;
 
     const bool fork = Ysh && aux && aux != s;

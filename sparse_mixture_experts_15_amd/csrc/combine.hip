@@ -1,7 +1,7 @@
 // Combine: y[t] = sum_j O[slot_row[t*k + j]] + Ysh[t]  (the GLaM study note's
 // MoE output sum over the selected experts; the GLM-4.5 note's output
-// equation adds the shared expert).  The sorted rows O already carry their
-// gate weights.  One wave per token, fp32 sum in fixed slot order, one
+// equation adds the shared expert).  The sorted rows O (fp32) already carry
+// their gate weights.  One wave per token, fp32 sum in fixed slot order, one
 // rounding to the output dtype, 16-byte vector loads and stores.  It is a
 // gather, not a scatter: no atomics, so the result is deterministic.
 #include "common.hpp"
@@ -9,19 +9,20 @@
 namespace moe {
 namespace {
 
-template <typename T>
-struct Vec;
-template <>
-struct Vec<bf16_t> {
-    static constexpr int N = 8;
-    __device__ static void load(const bf16_t* p, float* v) {
-        const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+template <int V>
+__device__ __forceinline__ void load_f32(const float* p, float* v) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(u[i] << 16);
-            v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-        }
+    for (int i = 0; i < V; i += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(p + i);
+        v[i] = f.x; v[i + 1] = f.y; v[i + 2] = f.z; v[i + 3] = f.w;
     }
+}
+
+template <typename TY>
+struct Out;
+template <>
+struct Out<bf16_t> {
+    static constexpr int V = 8;   // 8 outputs = one 16-byte store
     __device__ static void store(bf16_t* p, const float* v) {
         u32x4 u;
 #pragma unroll
@@ -30,23 +31,19 @@ struct Vec<bf16_t> {
     }
 };
 template <>
-struct Vec<float> {
-    static constexpr int N = 4;
-    __device__ static void load(const float* p, float* v) {
-        const float4 f = *reinterpret_cast<const float4*>(p);
-        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-    }
+struct Out<float> {
+    static constexpr int V = 4;
     __device__ static void store(float* p, const float* v) {
         *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     }
 };
 
-template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ O,
+template <typename TY>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ O,
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ Ysh,
-                                                      T* __restrict__ y, int Tn, int k, int D) {
-    constexpr int V = Vec<T>::N;
+                                                      TY* __restrict__ y, int Tn, int k, int D) {
+    constexpr int V = Out<TY>::V;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= Tn) return;
@@ -61,36 +58,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ O,
         for (int j = 0; j < kMaxK; ++j) {
             if (rows[j] < 0) continue;
             float v[V];
-            Vec<T>::load(O + (int64_t)rows[j] * D + d0, v);
+            load_f32<V>(O + (int64_t)rows[j] * D + d0, v);
 #pragma unroll
             for (int i = 0; i < V; ++i) acc[i] += v[i];
         }
         if (Ysh) {
-            const float* ys = Ysh + (int64_t)t * D + d0;
+            float v[V];
+            load_f32<V>(Ysh + (int64_t)t * D + d0, v);
 #pragma unroll
-            for (int i = 0; i < V; i += 4) {
-                const float4 f = *reinterpret_cast<const float4*>(ys + i);
-                acc[i] += f.x; acc[i + 1] += f.y; acc[i + 2] += f.z; acc[i + 3] += f.w;
-            }
+            for (int i = 0; i < V; ++i) acc[i] += v[i];
         }
-        Vec<T>::store(y + (int64_t)t * D + d0, acc);
+        Out<TY>::store(y + (int64_t)t * D + d0, acc);
     }
 }
 
 }  // namespace
 
-hipError_t launch_combine(hipStream_t s, int dtype, const void* O, const int32_t* slot_row,
+hipError_t launch_combine(hipStream_t s, int out_dtype, const float* O, const int32_t* slot_row,
                           const float* Ysh, void* y, int64_t T, int k, int64_t D) {
     if (T == 0) return hipSuccess;
     dim3 grid((unsigned)((T + 3) / 4));
-    if (dtype == 1)
-        hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s,
-                           static_cast<const bf16_t*>(O), slot_row, Ysh, static_cast<bf16_t*>(y),
-                           (int)T, k, (int)D);
+    if (out_dtype == 1)
+        hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s, O, slot_row, Ysh,
+                           static_cast<bf16_t*>(y), (int)T, k, (int)D);
     else
-        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s,
-                           static_cast<const float*>(O), slot_row, Ysh, static_cast<float*>(y),
-                           (int)T, k, (int)D);
+        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, O, slot_row, Ysh,
+                           static_cast<float*>(y), (int)T, k, (int)D);
     return hipGetLastError();
 }
 

@@ -49,7 +49,7 @@ enum Label : int {
 enum Epi : int {
     EPI_SWIGLU = 0,      // out[r, n] = silu(gate) * up            -> dtype
     EPI_GELU = 1,        // out[r, n] = gelu(acc + b1[e, n])       -> dtype
-    EPI_DOWN_SCALED = 2, // out[r, n] = w[slot(r)] * (acc + b2[e, n]) -> dtype
+    EPI_DOWN_SCALED = 2, // out[r, n] = w[slot(r)] * (acc + b2[e, n]) -> fp32
     EPI_DOWN_F32 = 3     // out[r, n] = acc                         -> fp32
 };
 
@@ -91,7 +91,7 @@ hipError_t launch_perm_scatter(hipStream_t s, const int32_t* idx, const int32_t*
 hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M, int bm,
                              int64_t max_tiles, int32_t* tiles);
 hipError_t launch_gemm(hipStream_t s, int dtype, int epi, const GemmArgs& g, int64_t m_tiles);
-hipError_t launch_combine(hipStream_t s, int dtype, const void* O, const int32_t* slot_row,
+hipError_t launch_combine(hipStream_t s, int out_dtype, const float* O, const int32_t* slot_row,
                           const float* Ysh, void* y, int64_t T, int k, int64_t D);
 
 // Tile geometry of the expert GEMMs (rows per m-tile) for a dtype.

@@ -9,7 +9,7 @@
 //
 //   up   (SWIGLU):  H[r, n] = silu(A[r] . Wg[e, n]) * (A[r] . Wu[e, n])
 //   up   (GELU):    H[r, n] = gelu(A[r] . W1[e, n] + b1[e, n])
-//   down (scaled):  O[r, n] = w[slot(r)] * (H[r] . W2[e, n] + b2[e, n])
+//   down (scaled):  O[r, n] = w[slot(r)] * (H[r] . W2[e, n] + b2[e, n])   (fp32)
 //   down (fp32):    Y[r, n] = H[r] . W2[n]            (shared expert)
 //
 // bf16 path: 128 x 128 workgroup tile (128 A rows x 128 B rows), K step 64,
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16(GemmArgs g) {
                     if (EPI == EPI_GELU)
                         static_cast<bf16_t*>(g.c)[rr[q] * N + n] = f32_to_bf16(gelu_erf_f32(v + bv));
                     else if (EPI == EPI_DOWN_SCALED)
-                        static_cast<bf16_t*>(g.c)[rr[q] * N + n] = f32_to_bf16(wrow[q] * (v + bv));
+                        static_cast<float*>(g.c)[rr[q] * N + n] = wrow[q] * (v + bv);
                     else
                         static_cast<float*>(g.c)[rr[q] * N + n] = v;
                 }

@@ -18,7 +18,7 @@ class MoELayer:
     def forward(self, x, W_r, bias, W1, b1, W2, b2, Wsh_gu=None, Wsh_dn=None, y=None,
                 stream=None, aux_stream=None):
         if y is None:
-            y = torch.empty_like(x)
+            y = torch.empty(x.shape, dtype=B._odt(self.desc), device=x.device)
         B.moe_forward(self.handle, self.desc, x, W_r, bias, W1, b1, W2, b2, Wsh_gu, Wsh_dn, y,
                       self.ws, stream=stream, aux_stream=aux_stream)
         return y

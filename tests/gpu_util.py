@@ -85,6 +85,82 @@ def assert_close_rms(got, ref, rel, what):
     return err, scale
 
 
+BF16_REL = 2.0 ** -8     # largest relative error of one bf16 rounding
+PLAIN_MIN_WIDTH = 512    # widths at which the plain 2e-2 * RMS bar is asserted
+SLACK = 1e-3             # fp32 accumulation and activation error, as a fraction of RMS
+
+
+def _act(cfg, Z, b1=None):
+    from scipy import special
+    if cfg.act == "swiglu":
+        g, u = Z[:, :cfg.F], Z[:, cfg.F:]
+        return g * special.expit(g) * u
+    if b1 is not None:
+        Z = Z + b1
+    return 0.5 * Z * (1.0 + special.erf(Z / np.sqrt(2.0)))
+
+
+def rounding_bounds(cfg, h, idx, w):
+    """Forward-error bound of the bf16 path's one unavoidable rounding: the
+    hidden activation H is rounded to bf16 (relative error <= 2^-8) before
+    the bf16 down projection, so an output element O_i = w sum_f H_f W2_if
+    can be off by up to 2^-8 w sum_f |H_f| |W2_if|.  Returns that bound per
+    (token, slot) row [T, k, D] and for the shared expert [T, D] (or None).
+    Computed with numpy from the same inputs; it is an error allowance, never
+    an expected value."""
+    X = widen(h["x"])
+    W1, W2 = widen(h["W1"]), widen(h["W2"])
+    b1 = widen(h["b1"]) if h.get("b1") is not None else None
+    T, k, D = cfg.T, cfg.k, cfg.D
+    bnd = np.zeros((T, k, D))
+    for e in np.unique(idx):
+        if e < 0 or e >= cfg.M:
+            continue
+        tt, jj = np.nonzero(idx == e)
+        Hm = np.abs(_act(cfg, X[tt] @ W1[e].T, None if b1 is None else b1[e]))
+        bnd[tt, jj] = BF16_REL * np.abs(w[tt, jj])[:, None] * (Hm @ np.abs(W2[e]).T)
+    bsh = None
+    if cfg.F_shared:
+        gu, dn = widen(h["Wsh_gu"]), widen(h["Wsh_dn"])
+        Z = X @ gu.T
+        from scipy import special
+        g, u = Z[:, :cfg.F_shared], Z[:, cfg.F_shared:]
+        bsh = BF16_REL * (np.abs(g * special.expit(g) * u) @ np.abs(dn).T)
+    return bnd, bsh
+
+
+def check_float(cfg, got, ref, what, bound=None, plain=True, out_bf16=False):
+    """Floating-point parity.
+
+    fp32 layer: max|err| <= 1e-4 * RMS(oracle).
+    bf16 layer: with `plain`, max|err| <= 2e-2 * RMS(oracle) (the bar for
+    bf16 inputs with fp32 accumulation), allowing in addition, when
+    `out_bf16`, the final rounding of each value to bf16 (2^-8 |ref|); with
+    a `bound` (narrow shapes), per element |err| <= bound + 1e-3 * RMS
+    (+ the same output rounding).
+    """
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    if ref.size == 0:
+        return 0.0, 0.0
+    if cfg.dtype != "bf16":
+        return assert_close_rms(got, ref, tol(cfg), what)
+    scale = float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(got - ref)
+    out_round = BF16_REL * np.abs(ref) if out_bf16 else 0.0
+    if bound is not None:
+        allow = bound + SLACK * scale + out_round
+        worst = float((err - allow).max())
+        assert worst <= 0.0, (f"{what}: error exceeds the bf16 rounding bound by {worst:.3e} "
+                              f"(max|err| {err.max():.3e}, RMS {scale:.3e})")
+    if plain:
+        worst = float((err - out_round - tol(cfg) * scale).max())
+        assert worst <= 0.0, (f"{what}: max|err| {err.max():.3e} exceeds {tol(cfg)} * RMS "
+                              f"{scale:.3e}" + (" + bf16 output rounding" if out_bf16 else ""))
+    return float(err.max()), scale
+
+
 def gpu_permute(L, d, idx):
     S = d.T * d.k
     out = {"counts": dev_i32(d.M), "offsets": dev_i32(d.M + 1), "sorted_token": dev_i32(S),

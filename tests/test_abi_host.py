@@ -58,7 +58,7 @@ def test_workspace_size_covers_intermediates():
         n = _ws(d)
         esz = 2 if cfg.dtype == "bf16" else 4
         S = cfg.T * cfg.k
-        need = S * (cfg.F + cfg.D) * esz + cfg.T * cfg.F_shared * esz
+        need = S * cfg.F * esz + S * cfg.D * 4 + cfg.T * cfg.F_shared * esz
         if cfg.F_shared:
             need += cfg.T * cfg.D * 4
         assert need <= n <= need + 64 * 2**20
