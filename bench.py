@@ -138,7 +138,7 @@ def main():
     # realised routing (touched experts) for the algorithmic byte counts
     idx = torch.empty(cfg.T * cfg.k, dtype=torch.int32, device="cuda")
     w = torch.empty(cfg.T * cfg.k, dtype=torch.float32, device="cuda")
-    B.moe_route(L.handle, d, t["x"], t["W_r"], t["bias"], idx, w)
+    B.moe_route(L.handle, d, t["x"], t["W_r"], t["bias"], idx, w, L.ws)
     counts = torch.bincount(idx.long(), minlength=cfg.M).cpu().tolist()
     kw, U = kernel_work(cfg, counts)
     log(f"touched experts {U}/{cfg.M}, max rows {max(counts)}")

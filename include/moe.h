@@ -110,9 +110,11 @@ int moe_workspace_size(const moe_desc* d, size_t* bytes);
  *   x[T,D] (dtype), W_r[M,D] fp32, bias[M] fp32 (SIGMOID only; NULL = zero;
  *   ignored for SOFTMAX) -> idx[T,k] int32, w[T,k] fp32.
  * A token's k experts are distinct and stored in ascending expert order;
- * an exactly equal selection score goes to the lower expert index. */
+ * an exactly equal selection score goes to the lower expert index.
+ * Uses workspace (the split router weights and partial logits). */
 int moe_route(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
-              const float* bias, int32_t* idx, float* w, void* stream);
+              const float* bias, int32_t* idx, float* w, void* ws, size_t ws_bytes,
+              void* stream);
 
 /* Dispatch: group the T*k flat slots f = t*k + j by expert, stably
  * [GLaM "Capacity, Active Compute, and Reporting": dispatch / expert

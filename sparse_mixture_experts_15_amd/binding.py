@@ -66,7 +66,7 @@ def load_library() -> ctypes.CDLL:
         "moe_create": [i32, ctypes.POINTER(vp)],
         "moe_destroy": [vp],
         "moe_workspace_size": [dp, ctypes.POINTER(sz)],
-        "moe_route": [vp, dp, vp, vp, vp, vp, vp, vp],
+        "moe_route": [vp, dp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_permute": [vp, dp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_expert_ffn": [vp, dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_shared_expert": [vp, dp, vp, vp, vp, vp, vp, sz, vp],
@@ -171,12 +171,13 @@ def moe_workspace_size(d: moe_desc) -> int:
     return n.value
 
 
-def moe_route(h, d, x, W_r, bias, idx, w, stream=None):
+def moe_route(h, d, x, W_r, bias, idx, w, ws, stream=None):
     T, D, M, k = d.T, d.D, d.M, d.k
     _check("moe_route", load_library().moe_route(
         h, ctypes.byref(d), _ptr(x, "x", _dt(d), T * D), _ptr(W_r, "W_r", torch.float32, M * D),
         _ptr(bias, "bias", torch.float32, M), _ptr(idx, "idx", torch.int32, T * k),
-        _ptr(w, "w", torch.float32, T * k), _stream(stream)))
+        _ptr(w, "w", torch.float32, T * k), _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def moe_permute(h, d, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws,

@@ -37,10 +37,11 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 // Device workspace layout shared by every entry point.
 struct Plan {
     int64_t S = 0, nblk = 0, max_tiles = 0;
-    int bm = 0;
+    int bm = 0, bm_sh = 0;
     size_t esz = 0;
     size_t idx = 0, w = 0, counts = 0, offsets = 0, sorted_token = 0, sorted_slot = 0,
-           slot_row = 0, hist = 0, tiles = 0, H = 0, O = 0, Hsh = 0, Ysh = 0, total = 0;
+           slot_row = 0, hist = 0, tiles = 0, H = 0, O = 0, Hsh = 0, Ysh = 0, route = 0,
+           total = 0;
 };
 
 Plan make_plan(const moe_desc* d) {
@@ -48,7 +49,8 @@ Plan make_plan(const moe_desc* d) {
     p.esz = d->dtype == MOE_DTYPE_BF16 ? 2 : 4;
     p.S = d->T * d->k;
     p.nblk = (d->T + kPermBlock - 1) / kPermBlock;
-    p.bm = gemm_block_m(d->dtype);
+    p.bm = gemm_block_m(d->dtype, p.S, d->M);
+    p.bm_sh = gemm_block_m(d->dtype, d->T, 1);
     p.max_tiles = (p.S + p.bm - 1) / p.bm + (d->M < p.S ? d->M : p.S);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -64,11 +66,12 @@ Plan make_plan(const moe_desc* d) {
     p.sorted_slot = take(p.S * 4);
     p.slot_row = take(p.S * 4);
     p.hist = take((size_t)p.nblk * d->M * 4);
-    p.tiles = take((size_t)p.max_tiles * 2 * 4);
+    p.tiles = take(((size_t)p.max_tiles * 2 + 1) * 4);
     p.H = take((size_t)p.S * d->F * p.esz);
     p.O = take((size_t)p.S * d->D * 4);
     p.Hsh = take((size_t)d->T * d->F_shared * p.esz);
     p.Ysh = take(d->F_shared > 0 ? (size_t)d->T * d->D * 4 : 0);
+    p.route = take(route_workspace(d->dtype, d->T, d->D, d->M));
     p.total = off;
     return p;
 }
@@ -101,6 +104,13 @@ int validate(const moe_desc* d) {
         return fail(MOE_ERR_UNSUPPORTED, "T*k exceeds int32 indexing");
     if (d->D > lim / 16 || d->F > lim / 16 || d->F_shared > lim / 16)
         return fail(MOE_ERR_UNSUPPORTED, "D/F too large");
+    // bf16 operands are read through 32-bit buffer offsets
+    const int64_t G = d->act == MOE_ACT_SWIGLU ? 2 : 1;
+    const int64_t S = d->T * (int64_t)d->k;
+    if (d->dtype == MOE_DTYPE_BF16 &&
+        (d->T * d->D * 2 > lim || S * d->F * 2 > lim || G * d->F * d->D * 2 > lim ||
+         d->T * d->F_shared * 2 > lim || 2 * d->F_shared * d->D * 2 > lim))
+        return fail(MOE_ERR_UNSUPPORTED, "an operand exceeds 2 GiB");
     return MOE_OK;
 }
 
@@ -174,11 +184,11 @@ T* at(void* ws, size_t off) {
 }
 
 // Stage bodies (no validation).
-int do_route(moe_handle* h, const moe_desc* d, const void* x, const float* W_r, const float* bias,
-             int32_t* idx, float* w, hipStream_t s) {
+int do_route(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, const float* W_r,
+             const float* bias, int32_t* idx, float* w, void* ws, hipStream_t s) {
     return run(h, s, L_ROUTE, [&] {
         return launch_route(s, d->dtype, d->scorer, x, W_r, bias, idx, w, d->T, d->D, d->M, d->k,
-                            d->renorm, d->alpha, d->eps);
+                            d->renorm, d->alpha, d->eps, at<char>(ws, p.route));
     });
 }
 
@@ -215,11 +225,13 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     up.c = H;
     up.tiles = tiles;
     up.offsets = offsets;
+    up.a_rows = d->T;
+    up.b_rows = (int)((swiglu ? 2 : 1) * d->F);
     up.K = (int)d->D;
     up.N = (int)d->F;
     up.F_split = (int)d->F;
     TRY(run(h, s, L_FFN_UP, [&] {
-        return launch_gemm(s, d->dtype, swiglu ? EPI_SWIGLU : EPI_GELU, up, p.max_tiles);
+        return launch_gemm(s, d->dtype, p.bm, swiglu ? EPI_SWIGLU : EPI_GELU, up, p.max_tiles);
     }));
     GemmArgs dn{};
     dn.a = H;
@@ -231,33 +243,41 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     dn.c = O;
     dn.tiles = tiles;
     dn.offsets = offsets;
+    dn.a_rows = p.S;
+    dn.b_rows = (int)d->D;
     dn.K = (int)d->F;
     dn.N = (int)d->D;
     return run(h, s, L_FFN_DOWN,
-               [&] { return launch_gemm(s, d->dtype, EPI_DOWN_SCALED, dn, p.max_tiles); });
+               [&] { return launch_gemm(s, d->dtype, p.bm, EPI_DOWN_SCALED, dn, p.max_tiles); });
 }
 
 int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, const void* Wgu,
               const void* Wdn, float* Ysh, void* ws, hipStream_t s) {
     void* Hsh = at<char>(ws, p.Hsh);
-    const int64_t mt = (d->T + p.bm - 1) / p.bm;
+    const int64_t mt = (d->T + p.bm_sh - 1) / p.bm_sh;
     GemmArgs up{};
     up.a = x;
     up.b = Wgu;
     up.c = Hsh;
     up.dense_rows = d->T;
+    up.a_rows = d->T;
+    up.b_rows = (int)(2 * d->F_shared);
     up.K = (int)d->D;
     up.N = (int)d->F_shared;
     up.F_split = (int)d->F_shared;
-    TRY(run(h, s, L_SHARED_UP, [&] { return launch_gemm(s, d->dtype, EPI_SWIGLU, up, mt); }));
+    TRY(run(h, s, L_SHARED_UP,
+            [&] { return launch_gemm(s, d->dtype, p.bm_sh, EPI_SWIGLU, up, mt); }));
     GemmArgs dn{};
     dn.a = Hsh;
     dn.b = Wdn;
     dn.c = Ysh;
     dn.dense_rows = d->T;
+    dn.a_rows = d->T;
+    dn.b_rows = (int)d->D;
     dn.K = (int)d->F_shared;
     dn.N = (int)d->D;
-    return run(h, s, L_SHARED_DOWN, [&] { return launch_gemm(s, d->dtype, EPI_DOWN_F32, dn, mt); });
+    return run(h, s, L_SHARED_DOWN,
+               [&] { return launch_gemm(s, d->dtype, p.bm_sh, EPI_DOWN_F32, dn, mt); });
 }
 
 int do_combine(moe_handle* h, const moe_desc* d, const float* O, const int32_t* slot_row,
@@ -335,7 +355,8 @@ int moe_workspace_size(const moe_desc* d, size_t* bytes) {
 }
 
 int moe_route(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
-              const float* bias, int32_t* idx, float* w, void* stream) {
+              const float* bias, int32_t* idx, float* w, void* ws, size_t ws_bytes,
+              void* stream) {
     CHECK_HANDLE(h);
     TRY(validate(d));
     if (d->T == 0) return MOE_OK;
@@ -343,9 +364,11 @@ int moe_route(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
     NEED(W_r, "W_r");
     NEED(idx, "idx");
     NEED(w, "w");
+    const Plan p = make_plan(d);
+    TRY(check_ws(p, ws, ws_bytes));
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
-    return do_route(h, d, x, W_r, bias, idx, w, static_cast<hipStream_t>(stream));
+    return do_route(h, d, p, x, W_r, bias, idx, w, ws, static_cast<hipStream_t>(stream));
 }
 
 int moe_permute(moe_handle* h, const moe_desc* d, const int32_t* idx, int32_t* counts,
@@ -471,7 +494,7 @@ int moe_forward(moe_handle* h, const moe_desc* d, const void* x, const float* W_
             TRY(do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, s));
         }
     }
-    TRY(do_route(h, d, x, W_r, bias, idx, w, s));
+    TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
     TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
     TRY(do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O, ws, s));
     if (fork) {

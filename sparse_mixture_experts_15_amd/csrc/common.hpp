@@ -68,6 +68,8 @@ struct GemmArgs {
     const int32_t* tiles;     // grouped: per m-tile (expert, row0); NULL: dense
     const int32_t* offsets;   // grouped: expert row ranges [M+1]
     int64_t dense_rows;       // dense: total rows
+    int64_t a_rows;           // rows of the matrix `a` points to (gathered loads)
+    int b_rows;               // rows of one expert's weight block
     int K;                    // reduction length
     int N;                    // output columns
     int F_split;              // SWIGLU: row offset of the up block in B (= N)
@@ -79,7 +81,10 @@ struct GemmArgs {
 namespace moe {
 hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, const float* W_r,
                         const float* bias, int32_t* idx, float* w, int64_t T, int64_t D,
-                        int64_t M, int k, int renorm, float alpha, float eps);
+                        int64_t M, int k, int renorm, float alpha, float eps, void* ws);
+// Router workspace (bytes) and its K-split count.
+size_t route_workspace(int dtype, int64_t T, int64_t D, int64_t M);
+int route_ksplit(int64_t T, int64_t D, int64_t M);
 hipError_t launch_perm_count(hipStream_t s, const int32_t* idx, int32_t* hist, int64_t T, int k,
                              int64_t M);
 hipError_t launch_perm_scan(hipStream_t s, int32_t* hist, int64_t nblk, int64_t T, int k,
@@ -90,12 +95,14 @@ hipError_t launch_perm_scatter(hipStream_t s, const int32_t* idx, const int32_t*
                                int32_t* sorted_token, int32_t* sorted_slot, int32_t* slot_row);
 hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M, int bm,
                              int64_t max_tiles, int32_t* tiles);
-hipError_t launch_gemm(hipStream_t s, int dtype, int epi, const GemmArgs& g, int64_t m_tiles);
+hipError_t launch_gemm(hipStream_t s, int dtype, int bm, int epi, const GemmArgs& g,
+                       int64_t m_tiles);
 hipError_t launch_combine(hipStream_t s, int out_dtype, const float* O, const int32_t* slot_row,
                           const float* Ysh, void* y, int64_t T, int k, int64_t D);
 
-// Tile geometry of the expert GEMMs (rows per m-tile) for a dtype.
-int gemm_block_m(int dtype);
+// Rows per m-tile of the expert GEMMs for a dtype, given the total rows and
+// the number of groups sharing them.
+int gemm_block_m(int dtype, int64_t rows, int64_t groups);
 // Token block of the permute kernels.
 constexpr int kPermBlock = 256;
 }  // namespace moe

@@ -135,8 +135,9 @@ __global__ __launch_bounds__(kPermBlock) void perm_scatter(
 }
 
 // Per m-tile of `bm` rows: (expert, first row).  Tiles are laid out expert
-// after expert; entries past the last tile are (-1, 0).  One thread per
-// expert writes its own tiles after a scan of the tile counts.
+// after expert; entries past the last tile are (-1, 0), and the number of
+// valid tiles is stored after the table, at tiles[2 * max_tiles].  One
+// thread per expert writes its own tiles after a scan of the tile counts.
 __global__ __launch_bounds__(kScanThreads) void tile_table(const int32_t* __restrict__ offsets,
                                                           int M, int bm, int max_tiles,
                                                           int32_t* __restrict__ tiles) {
@@ -169,6 +170,7 @@ __global__ __launch_bounds__(kScanThreads) void tile_table(const int32_t* __rest
         tiles[2 * i] = -1;
         tiles[2 * i + 1] = 0;
     }
+    if (tid == 0) tiles[2 * max_tiles] = total;
 }
 
 }  // namespace

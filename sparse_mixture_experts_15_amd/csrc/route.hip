@@ -6,14 +6,15 @@
 // selection, renormalisation by the selected scores' sum plus eps, routed
 // scaling factor alpha).
 //
-// bf16 x (prefill / decode layers): a block of 32 tokens x all experts is a
-// small GEMM on bf16 MFMA.  W_r is fp32, so each weight is split exactly
-// into three bf16 parts (w = hi + mid + lo, by truncation); x is already
-// bf16, so every partial product is exact and the logits carry fp32
-// accumulation error only, far below the 1e-6 selection-score gap that
-// decides ties.  fp32 x (the tiny fp32 layer): one wave per token with fp64
-// dot products.  Both paths leave fp32 logits in LDS and share one
-// wavefront top-k epilogue.
+// bf16 x (prefill / decode layers): the logits are a GEMM x . W_r^T on bf16
+// MFMA.  W_r is fp32, so a pre-pass splits it exactly into three bf16
+// planes (w = hi + mid + lo, by truncation); x is already bf16, so every
+// partial product is exact and the logits carry fp32 accumulation error
+// only, far below the 1e-6 selection-score gap that decides ties.  The
+// GEMM is tiled 64 tokens x 64 experts with split-K (so even 64 tokens fill
+// the GPU); a top-k kernel sums the K-chunk partials in fixed order.  fp32 x
+// (the tiny fp32 layer): one wave per token with fp64 dot products.  Both
+// paths share one wavefront top-k epilogue.
 #include "common.hpp"
 
 #include <math.h>
@@ -21,7 +22,6 @@
 namespace moe {
 namespace {
 
-constexpr int kRouteTB = 32;            // tokens per workgroup (MFMA path)
 constexpr int kMaxLanesJ = 1024 / 64;   // expert registers per lane
 
 // Split 8 fp32 values into three bf16x8 vectors whose sum is exact.
@@ -139,89 +139,158 @@ __device__ void topk_epilogue(const float* lrow, int M, int k, int scorer, const
     }
 }
 
-// MFMA router for bf16 x.  Wave w owns expert fragments w, w+4, ... (16
-// experts each) for both 16-token groups of the block.
-template <int FPW>
-__global__ __launch_bounds__(256) void route_bf16_mfma(
-    const bf16_t* __restrict__ x, const float* __restrict__ W_r, const float* __restrict__ bias,
-    int32_t* __restrict__ idx, float* __restrict__ w, int T, int D, int M, int k, int scorer,
-    int renorm, float alpha, float eps) {
-    extern __shared__ float s_logit[];   // [kRouteTB][ldl]
+// ---- bf16 x: exact three-way split of W_r, MFMA partial logits, top-k ----
+
+constexpr int kRB = 64;          // tokens per tile
+constexpr int kRE = 64;          // experts per tile
+constexpr int kRK = 64;          // K per stage
+constexpr int kRL = kRK + 8;     // padded LDS row (bf16): 144 bytes
+
+// W_r = hi + mid + lo exactly, each a bf16 plane of W3[3][M][D].
+__global__ __launch_bounds__(256) void router_split(const float* __restrict__ W_r,
+                                                    bf16_t* __restrict__ W3, int64_t n) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i >= n) return;
+    float v[8];
+    const float4 a = *reinterpret_cast<const float4*>(W_r + i);
+    const float4 b = *reinterpret_cast<const float4*>(W_r + i + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    bf16x8 hi, mid, lo;
+    split3(v, hi, mid, lo);
+    *reinterpret_cast<bf16x8*>(W3 + i) = hi;
+    *reinterpret_cast<bf16x8*>(W3 + n + i) = mid;
+    *reinterpret_cast<bf16x8*>(W3 + 2 * n + i) = lo;
+}
+
+// Partial logits P[z][t][e] = sum over the z-th K chunk of x[t,k] W_r[e,k],
+// as x.lo + x.mid + x.hi on bf16 MFMA (each product exact, fp32 sums).
+// Tile: 64 tokens x 64 experts; wave w owns tokens 16w..16w+15 and all four
+// 16-expert fragments.  x and the three W planes are staged through
+// double-buffered LDS.
+__global__ __launch_bounds__(256, 2) void route_logits(const bf16_t* __restrict__ x,
+                                                       const bf16_t* __restrict__ W3,
+                                                       float* __restrict__ P, int T, int D,
+                                                       int M, int KC) {
+    __shared__ __attribute__((aligned(16))) bf16_t sx[2][kRB * kRL];
+    __shared__ __attribute__((aligned(16))) bf16_t sw[2][3 * kRE * kRL];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.x * kRB, e0 = blockIdx.y * kRE;
+    const int kbeg = blockIdx.z * KC;
+    const int kend = min(D, kbeg + KC);
+    const int64_t plane = (int64_t)M * D;
+
+    // global sources: x chunks c = tid, tid+256 (row c/8, 16-byte column c%8);
+    // W chunks c = tid + 256 i, i < 6 (plane c/512, row (c%512)/8, column c%8)
+    const int lc = tid & 7;
+    const bf16_t* xs[2];
+    bool xv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = (tid >> 3) + 32 * i;
+        xv[i] = t0 + row < T;
+        xs[i] = x + (int64_t)(xv[i] ? t0 + row : 0) * D + lc * 8;
+    }
+    const bf16_t* wsrc[6];
+    bool wv[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+        const int c = tid + 256 * i;
+        const int p = c >> 9, row = (c & 511) >> 3;
+        wv[i] = e0 + row < M;
+        wsrc[i] = W3 + p * plane + (int64_t)(wv[i] ? e0 + row : 0) * D + lc * 8;
+    }
+    u32x4 rx[2], rw[6];
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    auto gload = [&](int k0) {
+        const bool kv = k0 + lc * 8 < kend;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            rx[i] = (xv[i] && kv) ? *reinterpret_cast<const u32x4*>(xs[i] + k0) : zero;
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+            rw[i] = (wv[i] && kv) ? *reinterpret_cast<const u32x4*>(wsrc[i] + k0) : zero;
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = (tid >> 3) + 32 * i;
+            *reinterpret_cast<u32x4*>(&sx[buf][row * kRL + lc * 8]) = rx[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const int c = tid + 256 * i;
+            const int p = c >> 9, row = (c & 511) >> 3;
+            *reinterpret_cast<u32x4*>(&sw[buf][(p * kRE + row) * kRL + lc * 8]) = rw[i];
+        }
+    };
+
+    floatx4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int fr = lane & 15, fk = (lane >> 4) * 8;
+    const int nk = (kend - kbeg + kRK - 1) / kRK;
+    if (nk > 0) {
+        gload(kbeg);
+        sstore(0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) gload(kbeg + (kt + 1) * kRK);
+#pragma unroll
+        for (int kk = 0; kk < kRK; kk += 32) {
+            const bf16x8 a =
+                *reinterpret_cast<const bf16x8*>(&sx[cur][(16 * wave + fr) * kRL + kk + fk]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int p = 2; p >= 0; --p) {   // lo, mid, hi
+                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(
+                        &sw[cur][(p * kRE + 16 * j + fr) * kRL + kk + fk]);
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+                }
+            }
+        }
+        if (kt + 1 < nk) sstore(cur ^ 1);
+        __syncthreads();
+    }
+    // MFMA 16x16 result: lane holds expert column lane%16, token rows 4*(lane/16)+q
+    float* Pz = P + (int64_t)blockIdx.z * T * M;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 16 * j + fr;
+        if (e >= M) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int t = t0 + 16 * wave + 4 * (lane >> 4) + q;
+            if (t < T) Pz[(int64_t)t * M + e] = acc[j][q];
+        }
+    }
+}
+
+// One wave per token: logits = sum of the K-chunk partials in chunk order,
+// then the top-k epilogue.
+__global__ __launch_bounds__(256) void route_topk(const float* __restrict__ P, int nK,
+                                                  const float* __restrict__ bias,
+                                                  int32_t* __restrict__ idx, float* __restrict__ w,
+                                                  int T, int M, int k, int scorer, int renorm,
+                                                  float alpha, float eps) {
+    extern __shared__ float s_logit[];   // [4][M]
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * kRouteTB;
-    const int NF = (M + 15) >> 4;
-    const int ldl = NF * 16;
-    const int r16 = lane & 15;
-    const int kq = lane >> 4;
-
-    floatx4 acc[2][FPW];
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int i = 0; i < FPW; ++i) acc[g][i] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    const int ta0 = t0 + r16, ta1 = t0 + 16 + r16;
-    const bool va0 = ta0 < T, va1 = ta1 < T;
-    const bf16_t* xa0 = x + (int64_t)(va0 ? ta0 : 0) * D;
-    const bf16_t* xa1 = x + (int64_t)(va1 ? ta1 : 0) * D;
-
-    for (int k0 = 0; k0 < D; k0 += 32) {
-        const int kk = k0 + 8 * kq;
-        const bool kv = kk < D;
-        u32x4 z = {0u, 0u, 0u, 0u};
-        const u32x4 a0u = (va0 && kv) ? *reinterpret_cast<const u32x4*>(xa0 + kk) : z;
-        const u32x4 a1u = (va1 && kv) ? *reinterpret_cast<const u32x4*>(xa1 + kk) : z;
-        const bf16x8 a0 = __builtin_bit_cast(bf16x8, a0u);
-        const bf16x8 a1 = __builtin_bit_cast(bf16x8, a1u);
-#pragma unroll
-        for (int i = 0; i < FPW; ++i) {
-            const int fr = wave + 4 * i;
-            if (fr < NF) {
-                const int e = fr * 16 + r16;
-                float wv[8];
-                if (e < M && kv) {
-                    const float4* p = reinterpret_cast<const float4*>(W_r + (int64_t)e * D + kk);
-                    const float4 p0 = p[0], p1 = p[1];
-                    wv[0] = p0.x; wv[1] = p0.y; wv[2] = p0.z; wv[3] = p0.w;
-                    wv[4] = p1.x; wv[5] = p1.y; wv[6] = p1.z; wv[7] = p1.w;
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) wv[q] = 0.f;
-                }
-                bf16x8 bh, bm, bl;
-                split3(wv, bh, bm, bl);
-                acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl, acc[0][i], 0, 0, 0);
-                acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bm, acc[0][i], 0, 0, 0);
-                acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bh, acc[0][i], 0, 0, 0);
-                acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl, acc[1][i], 0, 0, 0);
-                acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bm, acc[1][i], 0, 0, 0);
-                acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bh, acc[1][i], 0, 0, 0);
-            }
-        }
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;   // whole wave leaves; no block barrier follows
+    float* lrow = s_logit + wave * M;
+    for (int e = lane; e < M; e += 64) {
+        float s = 0.f;
+        for (int z = 0; z < nK; ++z) s += P[((int64_t)z * T + t) * M + e];
+        lrow[e] = s;
     }
-    // MFMA 16x16 result: lane holds column (expert) lane%16, rows (tokens)
-    // 4*(lane/16) + q.
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int i = 0; i < FPW; ++i) {
-            const int fr = wave + 4 * i;
-            if (fr < NF) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int tl = g * 16 + 4 * kq + q;
-                    s_logit[tl * ldl + fr * 16 + r16] = acc[g][i][q];
-                }
-            }
-        }
-    __syncthreads();
-    for (int tl = wave; tl < kRouteTB; tl += 4) {
-        const int t = t0 + tl;
-        if (t >= T) break;
-        topk_epilogue(s_logit + tl * ldl, M, k, scorer, bias, renorm, (double)alpha, (double)eps,
-                      idx + (int64_t)t * k, w + (int64_t)t * k);
-    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    topk_epilogue(lrow, M, k, scorer, bias, renorm, (double)alpha, (double)eps,
+                  idx + (int64_t)t * k, w + (int64_t)t * k);
 }
 
 // Generic router: one wave per token, fp64 dot products (fp32 or bf16 x).
@@ -256,44 +325,52 @@ __global__ __launch_bounds__(256) void route_simple(
                   idx + (int64_t)t * k, w + (int64_t)t * k);
 }
 
-template <int FPW>
-hipError_t launch_mfma(hipStream_t s, const void* x, const float* W_r, const float* bias,
-                       int32_t* idx, float* w, int T, int D, int M, int k, int scorer, int renorm,
-                       float alpha, float eps) {
-    const int NF = (M + 15) / 16;
-    const size_t lds = (size_t)kRouteTB * NF * 16 * sizeof(float);
-    dim3 grid((T + kRouteTB - 1) / kRouteTB);
-    hipLaunchKernelGGL(route_bf16_mfma<FPW>, grid, dim3(256), lds, s,
-                       static_cast<const bf16_t*>(x), W_r, bias, idx, w, T, D, M, k, scorer,
-                       renorm, alpha, eps);
-    return hipGetLastError();
+}  // namespace
+
+int route_ksplit(int64_t T, int64_t D, int64_t M) {
+    // enough K chunks for >= 512 workgroups, each chunk >= 256 long
+    const int64_t base = ((T + kRB - 1) / kRB) * ((M + kRE - 1) / kRE);
+    if (base <= 0 || D <= 0) return 1;
+    int64_t nk = (512 + base - 1) / base;
+    const int64_t maxk = (D + 255) / 256;
+    if (nk > maxk) nk = maxk;
+    if (nk < 1) nk = 1;
+    const int64_t kc = ((D + nk - 1) / nk + kRK - 1) / kRK * kRK;
+    return (int)((D + kc - 1) / kc);
 }
 
-}  // namespace
+size_t route_workspace(int dtype, int64_t T, int64_t D, int64_t M) {
+    if (dtype != 1) return 0;
+    return (size_t)3 * M * D * 2 + 256 + (size_t)route_ksplit(T, D, M) * T * M * 4;
+}
 
 hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, const float* W_r,
                         const float* bias, int32_t* idx, float* w, int64_t T, int64_t D,
-                        int64_t M, int k, int renorm, float alpha, float eps) {
+                        int64_t M, int k, int renorm, float alpha, float eps, void* ws) {
     if (T == 0) return hipSuccess;
     const float* b = (scorer == 1) ? bias : nullptr;
-    const int NF = (int)((M + 15) / 16);
-    if (dtype == 1 && M <= 512) {
-        const int fpw = (NF + 3) / 4;
-        if (fpw <= 1) return launch_mfma<1>(s, x, W_r, b, idx, w, T, D, M, k, scorer, renorm, alpha, eps);
-        if (fpw <= 2) return launch_mfma<2>(s, x, W_r, b, idx, w, T, D, M, k, scorer, renorm, alpha, eps);
-        if (fpw <= 4) return launch_mfma<4>(s, x, W_r, b, idx, w, T, D, M, k, scorer, renorm, alpha, eps);
-        return launch_mfma<8>(s, x, W_r, b, idx, w, T, D, M, k, scorer, renorm, alpha, eps);
+    if (dtype == 1) {
+        const int nK = route_ksplit(T, D, M);
+        const int64_t kc0 = ((D + nK - 1) / nK + kRK - 1) / kRK * kRK;
+        bf16_t* W3 = static_cast<bf16_t*>(ws);
+        float* P = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                            (((size_t)3 * M * D * 2 + 255) & ~size_t(255)));
+        const int64_t n = M * D;
+        hipLaunchKernelGGL(router_split, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s,
+                           W_r, W3, n);
+        dim3 grid((unsigned)((T + kRB - 1) / kRB), (unsigned)((M + kRE - 1) / kRE), (unsigned)nK);
+        hipLaunchKernelGGL(route_logits, grid, dim3(256), 0, s, static_cast<const bf16_t*>(x), W3,
+                           P, (int)T, (int)D, (int)M, (int)kc0);
+        hipLaunchKernelGGL(route_topk, dim3((unsigned)((T + 3) / 4)), dim3(256),
+                           4 * (size_t)M * sizeof(float), s, P, nK, b, idx, w, (int)T, (int)M, k,
+                           scorer, renorm, alpha, eps);
+        return hipGetLastError();
     }
     dim3 grid((unsigned)((T + 3) / 4));
     const size_t lds = 4 * (size_t)M * sizeof(float);
-    if (dtype == 0)
-        hipLaunchKernelGGL(route_simple<float>, grid, dim3(256), lds, s,
-                           static_cast<const float*>(x), W_r, b, idx, w, (int)T, (int)D, (int)M,
-                           k, scorer, renorm, alpha, eps);
-    else
-        hipLaunchKernelGGL(route_simple<bf16_t>, grid, dim3(256), lds, s,
-                           static_cast<const bf16_t*>(x), W_r, b, idx, w, (int)T, (int)D, (int)M,
-                           k, scorer, renorm, alpha, eps);
+    hipLaunchKernelGGL(route_simple<float>, grid, dim3(256), lds, s,
+                       static_cast<const float*>(x), W_r, b, idx, w, (int)T, (int)D, (int)M, k,
+                       scorer, renorm, alpha, eps);
     return hipGetLastError();
 }
 

@@ -173,7 +173,7 @@ def gpu_permute(L, d, idx):
 def run_route(L, d, t):
     idx = dev_i32(d.T * d.k)
     w = torch.empty(d.T * d.k, dtype=torch.float32, device="cuda")
-    B.moe_route(L.handle, d, t["x"], t["W_r"], t["bias"], idx, w)
+    B.moe_route(L.handle, d, t["x"], t["W_r"], t["bias"], idx, w, L.ws)
     return idx, w
 
 

@@ -83,6 +83,12 @@ def test_bad_descriptor_rejected(field, value, status):
     assert B.last_error_detail()
 
 
+def test_empty_batch_workspace_query():
+    for cfg in workloads.CONFIGS:
+        d = B.make_desc(cfg, T=0)
+        assert B.moe_workspace_size(d) >= 0
+
+
 def test_limits_unsupported():
     lib = B.load_library()
     n = ctypes.c_size_t()
@@ -98,8 +104,8 @@ def test_null_handle_and_null_outputs_rejected():
     lib = B.load_library()
     d = B.make_desc(workloads.GLM45_DECODE)
     vp = ctypes.c_void_p
-    assert lib.moe_route(None, ctypes.byref(d), vp(16), vp(16), None, vp(16), vp(16), None) \
-        == B.MOE_ERR_INVALID
+    assert lib.moe_route(None, ctypes.byref(d), vp(16), vp(16), None, vp(16), vp(16), None, 0,
+                         None) == B.MOE_ERR_INVALID
     assert lib.moe_workspace_size(ctypes.byref(d), None) == B.MOE_ERR_INVALID
     assert lib.moe_workspace_size(None, ctypes.byref(ctypes.c_size_t())) == B.MOE_ERR_INVALID
     assert lib.moe_forward(None, ctypes.byref(d), *([None] * 11), 0, None, None) \
