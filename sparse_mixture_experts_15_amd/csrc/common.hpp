@@ -73,6 +73,8 @@ struct GemmArgs {
     int K;                    // reduction length
     int N;                    // output columns
     int F_split;              // SWIGLU: row offset of the up block in B (= N)
+    int k_split;              // dense DOWN_F32 only: K chunks, each writing its own
+                              // [rows, N] partial at c + chunk * rows * N (0 = 1)
 };
 
 }  // namespace moe

@@ -119,9 +119,8 @@ __device__ __forceinline__ int swz(int row, int c) { return row * BK + ((c ^ (ro
 // slabs in that XCD's L2.  `m_tiles` is the number of valid m-tiles (the
 // grid may be larger; ids past m_tiles x n_tiles return false), so every
 // XCD gets real work.
-__device__ __forceinline__ bool tile_coords(int m_tiles, int n_tiles, int& mt, int& nt) {
+__device__ __forceinline__ bool tile_coords(int m_tiles, int n_tiles, int p, int& mt, int& nt) {
     const int G = m_tiles * n_tiles;
-    int p = blockIdx.x;
     if (p >= G) return false;
     const int per = G / 8;
     if (p < per * 8) p = (p & 7) * per + (p >> 3);
@@ -155,8 +154,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
 
     // grouped: the valid m-tile count follows the tile table
     const int m_valid = g.tiles ? min(m_tiles, g.tiles[2 * m_tiles]) : m_tiles;
+    // split-K (dense fp32 output only): chunk kc of g.k_split covers a K range
+    const int nsplit = g.k_split > 1 ? g.k_split : 1;
+    const int per_split = m_valid * n_tiles;
+    const int kc_id = (int)blockIdx.x / max(per_split, 1);
     int mt, nt;
-    if (!tile_coords(m_valid, n_tiles, mt, nt)) return;
+    if (kc_id >= nsplit || !tile_coords(m_valid, n_tiles, (int)blockIdx.x - kc_id * per_split, mt, nt))
+        return;
     Tile tl;
     if (!tile_of(g, mt, BM, tl)) return;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -214,11 +218,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
         for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // STAGES-deep ring: stages kt+1 .. kt+STAGES-1 load while stage kt is
-    // multiplied.
-    const int nk = (K + BK - 1) / BK;
+    // multiplied.  With split-K this workgroup runs stages [k_first, k_last).
+    const int nk_all = (K + BK - 1) / BK;
+    const int k_first = (int)((int64_t)nk_all * kc_id / nsplit);
+    const int k_last = (int)((int64_t)nk_all * (kc_id + 1) / nsplit);
+    const int nk = k_last - k_first;
 #pragma unroll
     for (int s0 = 0; s0 < STAGES - 1; ++s0)
-        if (s0 < nk) issue(s0);
+        if (s0 < nk) issue(k_first + s0);
     const int fr = lane & 15, fc = lane >> 4;
     for (int kt = 0; kt < nk; ++kt) {
         // stage kt has landed once only later stages' loads are pending
@@ -234,8 +241,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             wait_vmcnt<0>();
         }
         __builtin_amdgcn_s_barrier();     // every wave's loads landed; stage kt-1 fully read
-        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-        const bf16_t* st = sm + (kt % STAGES) * STAGE;
+        if (kt + STAGES - 1 < nk) issue(k_first + kt + STAGES - 1);
+        const bf16_t* st = sm + ((k_first + kt) % STAGES) * STAGE;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 af[TM], bfr[TN];
@@ -258,54 +265,88 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
         }
     }
 
-    // Epilogue.  MFMA 16x16 layout: lane holds column lane%16 and rows
+    // Epilogue: the output tile is staged through the (now idle) LDS ring in
+    // passes of up to EP_ROWS rows, then written as whole rows with 16-byte
+    // vector stores.  MFMA 16x16 layout: lane holds column lane%16 and rows
     // 4*(lane/16) + q of each 16x16 block.
+    constexpr bool OUT_BF16 = (EPI == EPI_SWIGLU || EPI == EPI_GELU);
+    constexpr int ESZ = OUT_BF16 ? 2 : 4;
+    constexpr int OUTC = (EPI == EPI_SWIGLU) ? BNB / 2 : BNB;   // output columns in the tile
+    constexpr int LDC = OUTC + 16 / ESZ;                        // +16 bytes per row: no write conflicts
+    constexpr int LDS_BYTES = STAGES * STAGE * 2;
+    constexpr int EP_FIT = LDS_BYTES / (LDC * ESZ);
+    constexpr int EP_ROWS = EP_FIT >= BM ? BM : (EP_FIT >= WROWS ? (EP_FIT / WROWS) * WROWS : 0);
+    static_assert(EP_ROWS >= WROWS && BM % EP_ROWS == 0, "epilogue staging must hold whole waves");
+    constexpr int CPR = OUTC * ESZ / 16;                        // 16-byte chunks per tile row
     const int rq = 4 * (lane >> 4);
     const int rbase = wm * WROWS;
-    if (EPI == EPI_SWIGLU) {
-        bf16_t* C = static_cast<bf16_t*>(g.c);
+    const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
+    __syncthreads();   // every wave is done with the operand stages
+#pragma unroll 1
+    for (int p0 = 0; p0 < BM; p0 += EP_ROWS) {
+        if (rbase >= p0 && rbase < p0 + EP_ROWS) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int n = n_base + 32 * wn + 16 * j + fr;
+            for (int i = 0; i < TM; ++i) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
+                    const int lr = rbase - p0 + 16 * i + rq + q;   // row within the pass
                     const int64_t r = tl.r0 + rbase + 16 * i + rq + q;
-                    if (r < tl.rend && n < N)
-                        C[r * N + n] = f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + 2][q]);
-                }
-            }
-    } else {
-        const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
+                    if (EPI == EPI_SWIGLU) {
+                        bf16_t* sc = reinterpret_cast<bf16_t*>(sm) + lr * LDC;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            float wrow[4];
-            int64_t rr[4];
+                        for (int j = 0; j < 2; ++j)
+                            sc[32 * wn + 16 * j + fr] =
+                                f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + 2][q]);
+                    } else if (EPI == EPI_GELU) {
+                        bf16_t* sc = reinterpret_cast<bf16_t*>(sm) + lr * LDC;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                rr[q] = tl.r0 + rbase + 16 * i + rq + q;
-                wrow[q] = 1.f;
-                if (EPI == EPI_DOWN_SCALED && rr[q] < tl.rend) wrow[q] = g.row_w[g.row_slot[rr[q]]];
-            }
+                        for (int j = 0; j < TN; ++j) {
+                            const int n = n_base + 64 * wn + 16 * j + fr;
+                            const float bv =
+                                (bias && n < N) ? bf16_to_f32(bias[(int64_t)tl.e * N + n]) : 0.f;
+                            sc[64 * wn + 16 * j + fr] = f32_to_bf16(gelu_erf_f32(acc[i][j][q] + bv));
+                        }
+                    } else {
+                        float* sc = reinterpret_cast<float*>(sm) + lr * LDC;
+                        float wr = 1.f;
+                        if (EPI == EPI_DOWN_SCALED && r < tl.rend) wr = g.row_w[g.row_slot[r]];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int n = n_base + 64 * wn + 16 * j + fr;
-                if (n >= N) continue;
-                const float bv = bias ? bf16_to_f32(bias[(int64_t)tl.e * N + n]) : 0.f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (rr[q] >= tl.rend) continue;
-                    const float v = acc[i][j][q];
-                    if (EPI == EPI_GELU)
-                        static_cast<bf16_t*>(g.c)[rr[q] * N + n] = f32_to_bf16(gelu_erf_f32(v + bv));
-                    else if (EPI == EPI_DOWN_SCALED)
-                        static_cast<float*>(g.c)[rr[q] * N + n] = wrow[q] * (v + bv);
-                    else
-                        static_cast<float*>(g.c)[rr[q] * N + n] = v;
+                        for (int j = 0; j < TN; ++j) {
+                            const int n = n_base + 64 * wn + 16 * j + fr;
+                            float v = acc[i][j][q];
+                            if (EPI == EPI_DOWN_SCALED) {
+                                const float bv = (bias && n < N)
+                                                     ? bf16_to_f32(bias[(int64_t)tl.e * N + n]) : 0.f;
+                                v = wr * (v + bv);
+                            }
+                            sc[64 * wn + 16 * j + fr] = v;
+                        }
+                    }
                 }
             }
         }
+        __syncthreads();
+        // whole rows out: chunk c of the pass -> row c / CPR, 16 bytes at column
+        // (c % CPR) * 16 / ESZ.  The expert GEMMs have N % 8 == 0 (whole
+        // chunks); the router's N = 3M may end mid-chunk: that chunk is
+        // written element by element.
+        constexpr int VE = 16 / ESZ;
+        for (int c = tid; c < EP_ROWS * CPR; c += NT) {
+            const int lr = c / CPR, ch = c % CPR;
+            const int64_t r = tl.r0 + p0 + lr;
+            const int n = n_base + ch * VE;
+            if (r >= tl.rend || n >= N) continue;
+            const char* src = reinterpret_cast<const char*>(sm) + (lr * LDC) * ESZ + ch * 16;
+            char* dst = static_cast<char*>(g.c) +
+                        ((int64_t)kc_id * g.dense_rows * N + r * N + n) * ESZ;
+            if (n + VE <= N && (N % VE) == 0) {
+                *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+            } else {
+                for (int e = 0; e < VE && n + e < N; ++e)
+                    for (int b = 0; b < ESZ; ++b) dst[e * ESZ + b] = src[e * ESZ + b];
+            }
+        }
+        if (p0 + EP_ROWS < BM) __syncthreads();
     }
 }
 
@@ -399,7 +440,7 @@ template <int EPI, int BMv, int BNv, int STv>
 hipError_t launch_bf16(hipStream_t s, const GemmArgs& g, int64_t m_tiles) {
     const int opt = (EPI == EPI_SWIGLU) ? BNv / 2 : BNv;
     const int n_tiles = (g.N + opt - 1) / opt;
-    const int64_t total = m_tiles * n_tiles;
+    const int64_t total = m_tiles * n_tiles * (g.k_split > 1 ? g.k_split : 1);
     hipLaunchKernelGGL((gemm_bf16<EPI, BMv, BNv, STv>), dim3((unsigned)total), dim3(NT), 0, s, g,
                        (int)m_tiles, n_tiles);
     return hipGetLastError();

@@ -8,13 +8,14 @@
 //
 // bf16 x (prefill / decode layers): the logits are a GEMM x . W_r^T on bf16
 // MFMA.  W_r is fp32, so a pre-pass splits it exactly into three bf16
-// planes (w = hi + mid + lo, by truncation); x is already bf16, so every
-// partial product is exact and the logits carry fp32 accumulation error
-// only, far below the 1e-6 selection-score gap that decides ties.  The
-// GEMM is tiled 64 tokens x 64 experts with split-K (so even 64 tokens fill
-// the GPU); a top-k kernel sums the K-chunk partials in fixed order.  fp32 x
-// (the tiny fp32 layer): one wave per token with fp64 dot products.  Both
-// paths share one wavefront top-k epilogue.
+// planes (w = hi + mid + lo, by truncation) stacked as a [3M, D] matrix; x is
+// already bf16, so every partial product is exact and the logits carry fp32
+// accumulation error only, far below the 1e-6 selection-score gap that
+// decides ties.  The GEMM is the expert GEMM kernel in dense mode with
+// split-K (so even 64 tokens fill the GPU); a top-k kernel sums the planes
+// and K chunks in fixed order.  fp32 x (the tiny fp32 layer): one wave per
+// token with fp64 dot products.  Both paths share one wavefront top-k
+// epilogue.
 #include "common.hpp"
 
 #include <math.h>
@@ -141,11 +142,6 @@ __device__ void topk_epilogue(const float* lrow, int M, int k, int scorer, const
 
 // ---- bf16 x: exact three-way split of W_r, MFMA partial logits, top-k ----
 
-constexpr int kRB = 64;          // tokens per tile
-constexpr int kRE = 64;          // experts per tile
-constexpr int kRK = 64;          // K per stage
-constexpr int kRL = kRK + 8;     // padded LDS row (bf16): 144 bytes
-
 // W_r = hi + mid + lo exactly, each a bf16 plane of W3[3][M][D].
 __global__ __launch_bounds__(256) void router_split(const float* __restrict__ W_r,
                                                     bf16_t* __restrict__ W3, int64_t n) {
@@ -162,114 +158,10 @@ __global__ __launch_bounds__(256) void router_split(const float* __restrict__ W_
     *reinterpret_cast<bf16x8*>(W3 + 2 * n + i) = lo;
 }
 
-// Partial logits P[z][t][e] = sum over the z-th K chunk of x[t,k] W_r[e,k],
-// as x.lo + x.mid + x.hi on bf16 MFMA (each product exact, fp32 sums).
-// Tile: 64 tokens x 64 experts; wave w owns tokens 16w..16w+15 and all four
-// 16-expert fragments.  x and the three W planes are staged through
-// double-buffered LDS.
-__global__ __launch_bounds__(256, 2) void route_logits(const bf16_t* __restrict__ x,
-                                                       const bf16_t* __restrict__ W3,
-                                                       float* __restrict__ P, int T, int D,
-                                                       int M, int KC) {
-    __shared__ __attribute__((aligned(16))) bf16_t sx[2][kRB * kRL];
-    __shared__ __attribute__((aligned(16))) bf16_t sw[2][3 * kRE * kRL];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int t0 = blockIdx.x * kRB, e0 = blockIdx.y * kRE;
-    const int kbeg = blockIdx.z * KC;
-    const int kend = min(D, kbeg + KC);
-    const int64_t plane = (int64_t)M * D;
-
-    // global sources: x chunks c = tid, tid+256 (row c/8, 16-byte column c%8);
-    // W chunks c = tid + 256 i, i < 6 (plane c/512, row (c%512)/8, column c%8)
-    const int lc = tid & 7;
-    const bf16_t* xs[2];
-    bool xv[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = (tid >> 3) + 32 * i;
-        xv[i] = t0 + row < T;
-        xs[i] = x + (int64_t)(xv[i] ? t0 + row : 0) * D + lc * 8;
-    }
-    const bf16_t* wsrc[6];
-    bool wv[6];
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-        const int c = tid + 256 * i;
-        const int p = c >> 9, row = (c & 511) >> 3;
-        wv[i] = e0 + row < M;
-        wsrc[i] = W3 + p * plane + (int64_t)(wv[i] ? e0 + row : 0) * D + lc * 8;
-    }
-    u32x4 rx[2], rw[6];
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    auto gload = [&](int k0) {
-        const bool kv = k0 + lc * 8 < kend;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            rx[i] = (xv[i] && kv) ? *reinterpret_cast<const u32x4*>(xs[i] + k0) : zero;
-#pragma unroll
-        for (int i = 0; i < 6; ++i)
-            rw[i] = (wv[i] && kv) ? *reinterpret_cast<const u32x4*>(wsrc[i] + k0) : zero;
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int row = (tid >> 3) + 32 * i;
-            *reinterpret_cast<u32x4*>(&sx[buf][row * kRL + lc * 8]) = rx[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            const int c = tid + 256 * i;
-            const int p = c >> 9, row = (c & 511) >> 3;
-            *reinterpret_cast<u32x4*>(&sw[buf][(p * kRE + row) * kRL + lc * 8]) = rw[i];
-        }
-    };
-
-    floatx4 acc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int fr = lane & 15, fk = (lane >> 4) * 8;
-    const int nk = (kend - kbeg + kRK - 1) / kRK;
-    if (nk > 0) {
-        gload(kbeg);
-        sstore(0);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kbeg + (kt + 1) * kRK);
-#pragma unroll
-        for (int kk = 0; kk < kRK; kk += 32) {
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8*>(&sx[cur][(16 * wave + fr) * kRL + kk + fk]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                for (int p = 2; p >= 0; --p) {   // lo, mid, hi
-                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(
-                        &sw[cur][(p * kRE + 16 * j + fr) * kRL + kk + fk]);
-                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
-                }
-            }
-        }
-        if (kt + 1 < nk) sstore(cur ^ 1);
-        __syncthreads();
-    }
-    // MFMA 16x16 result: lane holds expert column lane%16, token rows 4*(lane/16)+q
-    float* Pz = P + (int64_t)blockIdx.z * T * M;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = e0 + 16 * j + fr;
-        if (e >= M) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int t = t0 + 16 * wave + 4 * (lane >> 4) + q;
-            if (t < T) Pz[(int64_t)t * M + e] = acc[j][q];
-        }
-    }
-}
-
-// One wave per token: logits = sum of the K-chunk partials in chunk order,
-// then the top-k epilogue.
+// One wave per token: logit[e] = sum over K chunks z (in order) of the hi
+// plane's partial, plus the same sums of the mid and lo planes:
+// P[z][t][p*M + e] is x_t . plane_p[e] over chunk z.  Then the top-k
+// epilogue.
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ P, int nK,
                                                   const float* __restrict__ bias,
                                                   int32_t* __restrict__ idx, float* __restrict__ w,
@@ -281,10 +173,16 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ P, i
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;   // whole wave leaves; no block barrier follows
     float* lrow = s_logit + wave * M;
+    const int64_t ld = 3 * (int64_t)M;
     for (int e = lane; e < M; e += 64) {
-        float s = 0.f;
-        for (int z = 0; z < nK; ++z) s += P[((int64_t)z * T + t) * M + e];
-        lrow[e] = s;
+        float h = 0.f, m = 0.f, l = 0.f;
+        for (int z = 0; z < nK; ++z) {
+            const float* row = P + ((int64_t)z * T + t) * ld;
+            h += row[e];
+            m += row[M + e];
+            l += row[2 * M + e];
+        }
+        lrow[e] = h + (m + l);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
@@ -328,20 +226,21 @@ __global__ __launch_bounds__(256) void route_simple(
 }  // namespace
 
 int route_ksplit(int64_t T, int64_t D, int64_t M) {
-    // enough K chunks for >= 512 workgroups, each chunk >= 256 long
-    const int64_t base = ((T + kRB - 1) / kRB) * ((M + kRE - 1) / kRE);
+    // the logits GEMM (T x 3M, K = D) in 128 x 256 tiles: enough K chunks for
+    // a few hundred workgroups, each chunk at least 512 long (256 when the
+    // tile grid is tiny, as at decode)
+    const int64_t base = ((T + 127) / 128) * ((3 * M + 255) / 256);
     if (base <= 0 || D <= 0) return 1;
-    int64_t nk = (512 + base - 1) / base;
-    const int64_t maxk = (D + 255) / 256;
+    int64_t nk = (384 + base - 1) / base;
+    const int64_t maxk = D / (base < 32 ? 256 : 512);
     if (nk > maxk) nk = maxk;
     if (nk < 1) nk = 1;
-    const int64_t kc = ((D + nk - 1) / nk + kRK - 1) / kRK * kRK;
-    return (int)((D + kc - 1) / kc);
+    return (int)nk;
 }
 
 size_t route_workspace(int dtype, int64_t T, int64_t D, int64_t M) {
     if (dtype != 1) return 0;
-    return (size_t)3 * M * D * 2 + 256 + (size_t)route_ksplit(T, D, M) * T * M * 4;
+    return (size_t)3 * M * D * 2 + 256 + (size_t)route_ksplit(T, D, M) * T * 3 * M * 4;
 }
 
 hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, const float* W_r,
@@ -351,16 +250,25 @@ hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, con
     const float* b = (scorer == 1) ? bias : nullptr;
     if (dtype == 1) {
         const int nK = route_ksplit(T, D, M);
-        const int64_t kc0 = ((D + nK - 1) / nK + kRK - 1) / kRK * kRK;
         bf16_t* W3 = static_cast<bf16_t*>(ws);
         float* P = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                             (((size_t)3 * M * D * 2 + 255) & ~size_t(255)));
         const int64_t n = M * D;
         hipLaunchKernelGGL(router_split, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s,
                            W_r, W3, n);
-        dim3 grid((unsigned)((T + kRB - 1) / kRB), (unsigned)((M + kRE - 1) / kRE), (unsigned)nK);
-        hipLaunchKernelGGL(route_logits, grid, dim3(256), 0, s, static_cast<const bf16_t*>(x), W3,
-                           P, (int)T, (int)D, (int)M, (int)kc0);
+        // partial logits P[z][T][3M] = x . W3^T over K chunk z, on the expert GEMM
+        GemmArgs g{};
+        g.a = x;
+        g.b = W3;
+        g.c = P;
+        g.dense_rows = T;
+        g.a_rows = T;
+        g.b_rows = (int)(3 * M);
+        g.K = (int)D;
+        g.N = (int)(3 * M);
+        g.k_split = nK;
+        hipError_t e = launch_gemm(s, 1, 128, EPI_DOWN_F32, g, (T + 127) / 128);
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(route_topk, dim3((unsigned)((T + 3) / 4)), dim3(256),
                            4 * (size_t)M * sizeof(float), s, P, nK, b, idx, w, (int)T, (int)M, k,
                            scorer, renorm, alpha, eps);
