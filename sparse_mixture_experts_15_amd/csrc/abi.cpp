@@ -36,11 +36,11 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Device workspace layout shared by every entry point.
 struct Plan {
-    int64_t S = 0, nblk = 0, max_tiles = 0;
-    int bm = 0, bm_sh = 0;
+    int64_t S = 0, nblk = 0, max_tiles_up = 0, max_tiles_dn = 0;
+    int bm_up = 0, bm_dn = 0, bm_sh_up = 0, bm_sh_dn = 0;
     size_t esz = 0;
     size_t idx = 0, w = 0, counts = 0, offsets = 0, sorted_token = 0, sorted_slot = 0,
-           slot_row = 0, hist = 0, tiles = 0, H = 0, O = 0, Hsh = 0, Ysh = 0, route = 0,
+           slot_row = 0, hist = 0, tiles_up = 0, tiles_dn = 0, H = 0, O = 0, Hsh = 0, Ysh = 0, route = 0,
            total = 0;
 };
 
@@ -49,9 +49,15 @@ Plan make_plan(const moe_desc* d) {
     p.esz = d->dtype == MOE_DTYPE_BF16 ? 2 : 4;
     p.S = d->T * d->k;
     p.nblk = (d->T + kPermBlock - 1) / kPermBlock;
-    p.bm = gemm_block_m(d->dtype, p.S, d->M);
-    p.bm_sh = gemm_block_m(d->dtype, d->T, 1);
-    p.max_tiles = (p.S + p.bm - 1) / p.bm + (d->M < p.S ? d->M : p.S);
+    const int64_t G = d->act == MOE_ACT_SWIGLU ? 2 : 1;   // up-projection weight rows per F
+    p.bm_up = gemm_block_m(d->dtype, p.S, d->M, false, G * d->F);
+    p.bm_dn = gemm_block_m(d->dtype, p.S, d->M, true, d->D);
+    p.bm_sh_up = gemm_block_m(d->dtype, d->T, 1, false, 2 * d->F_shared);
+    p.bm_sh_dn = gemm_block_m(d->dtype, d->T, 1, true, d->D);
+    // ceil(S / bm) tiles plus at most one partial tile per non-empty expert
+    const int64_t partial = d->M < p.S ? d->M : p.S;
+    p.max_tiles_up = (p.S + p.bm_up - 1) / p.bm_up + partial;
+    p.max_tiles_dn = (p.S + p.bm_dn - 1) / p.bm_dn + partial;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -66,7 +72,8 @@ Plan make_plan(const moe_desc* d) {
     p.sorted_slot = take(p.S * 4);
     p.slot_row = take(p.S * 4);
     p.hist = take((size_t)p.nblk * d->M * 4);
-    p.tiles = take(((size_t)p.max_tiles * 2 + 1) * 4);
+    p.tiles_up = take(((size_t)p.max_tiles_up * 2 + 1) * 4);
+    p.tiles_dn = p.bm_dn == p.bm_up ? p.tiles_up : take(((size_t)p.max_tiles_dn * 2 + 1) * 4);
     p.H = take((size_t)p.S * d->F * p.esz);
     p.O = take((size_t)p.S * d->D * 4);
     p.Hsh = take((size_t)d->T * d->F_shared * p.esz);
@@ -211,10 +218,15 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
                   const int32_t* sorted_token, const int32_t* sorted_slot, const int32_t* offsets,
                   const float* w, const void* W1, const void* b1, const void* W2, const void* b2,
                   float* O, void* ws, hipStream_t s) {
-    int32_t* tiles = at<int32_t>(ws, p.tiles);
+    int32_t* tiles_up = at<int32_t>(ws, p.tiles_up);
+    int32_t* tiles_dn = at<int32_t>(ws, p.tiles_dn);
     void* H = at<char>(ws, p.H);
+    TileTables tt{{p.bm_up, p.bm_dn},
+                  {(int)p.max_tiles_up, (int)p.max_tiles_dn},
+                  {tiles_up, tiles_dn}};
+    const int ntables = tiles_dn == tiles_up ? 1 : 2;
     TRY(run(h, s, L_TILE_TABLE,
-            [&] { return launch_tile_table(s, offsets, d->M, p.bm, p.max_tiles, tiles); }));
+            [&] { return launch_tile_table(s, offsets, d->M, tt, ntables); }));
     const bool swiglu = d->act == MOE_ACT_SWIGLU;
     GemmArgs up{};
     up.a = x;
@@ -223,7 +235,7 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     up.b_stride = (swiglu ? 2 : 1) * d->F * d->D;
     up.bias = swiglu ? nullptr : b1;
     up.c = H;
-    up.tiles = tiles;
+    up.tiles = tiles_up;
     up.offsets = offsets;
     up.a_rows = d->T;
     up.b_rows = (int)((swiglu ? 2 : 1) * d->F);
@@ -231,7 +243,8 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     up.N = (int)d->F;
     up.F_split = (int)d->F;
     TRY(run(h, s, L_FFN_UP, [&] {
-        return launch_gemm(s, d->dtype, p.bm, swiglu ? EPI_SWIGLU : EPI_GELU, up, p.max_tiles);
+        return launch_gemm(s, d->dtype, p.bm_up, swiglu ? EPI_SWIGLU : EPI_GELU, up,
+                           p.max_tiles_up);
     }));
     GemmArgs dn{};
     dn.a = H;
@@ -241,20 +254,21 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     dn.row_w = w;
     dn.row_slot = sorted_slot;
     dn.c = O;
-    dn.tiles = tiles;
+    dn.tiles = tiles_dn;
     dn.offsets = offsets;
     dn.a_rows = p.S;
     dn.b_rows = (int)d->D;
     dn.K = (int)d->F;
     dn.N = (int)d->D;
     return run(h, s, L_FFN_DOWN,
-               [&] { return launch_gemm(s, d->dtype, p.bm, EPI_DOWN_SCALED, dn, p.max_tiles); });
+               [&] { return launch_gemm(s, d->dtype, p.bm_dn, EPI_DOWN_SCALED, dn, p.max_tiles_dn); });
 }
 
 int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, const void* Wgu,
               const void* Wdn, float* Ysh, void* ws, hipStream_t s) {
     void* Hsh = at<char>(ws, p.Hsh);
-    const int64_t mt = (d->T + p.bm_sh - 1) / p.bm_sh;
+    const int64_t mt_up = (d->T + p.bm_sh_up - 1) / p.bm_sh_up;
+    const int64_t mt_dn = (d->T + p.bm_sh_dn - 1) / p.bm_sh_dn;
     GemmArgs up{};
     up.a = x;
     up.b = Wgu;
@@ -266,7 +280,7 @@ int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, co
     up.N = (int)d->F_shared;
     up.F_split = (int)d->F_shared;
     TRY(run(h, s, L_SHARED_UP,
-            [&] { return launch_gemm(s, d->dtype, p.bm_sh, EPI_SWIGLU, up, mt); }));
+            [&] { return launch_gemm(s, d->dtype, p.bm_sh_up, EPI_SWIGLU, up, mt_up); }));
     GemmArgs dn{};
     dn.a = Hsh;
     dn.b = Wdn;
@@ -277,7 +291,7 @@ int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, co
     dn.K = (int)d->F_shared;
     dn.N = (int)d->D;
     return run(h, s, L_SHARED_DOWN,
-               [&] { return launch_gemm(s, d->dtype, p.bm_sh, EPI_DOWN_F32, dn, mt); });
+               [&] { return launch_gemm(s, d->dtype, p.bm_sh_dn, EPI_DOWN_F32, dn, mt_dn); });
 }
 
 int do_combine(moe_handle* h, const moe_desc* d, const float* O, const int32_t* slot_row,

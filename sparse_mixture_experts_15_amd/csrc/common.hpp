@@ -95,16 +95,23 @@ hipError_t launch_perm_scan(hipStream_t s, int32_t* hist, int64_t nblk, int64_t 
 hipError_t launch_perm_scatter(hipStream_t s, const int32_t* idx, const int32_t* hist,
                                const int32_t* offsets, int64_t T, int k, int64_t M,
                                int32_t* sorted_token, int32_t* sorted_slot, int32_t* slot_row);
-hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M, int bm,
-                             int64_t max_tiles, int32_t* tiles);
+// Up to two tile tables built by one launch (table y uses bm[y]).
+struct TileTables {
+    int bm[2];
+    int max_tiles[2];
+    int32_t* tiles[2];
+};
+hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M,
+                             const TileTables& tt, int count);
 hipError_t launch_gemm(hipStream_t s, int dtype, int bm, int epi, const GemmArgs& g,
                        int64_t m_tiles);
 hipError_t launch_combine(hipStream_t s, int out_dtype, const float* O, const int32_t* slot_row,
                           const float* Ysh, void* y, int64_t T, int k, int64_t D);
 
-// Rows per m-tile of the expert GEMMs for a dtype, given the total rows and
-// the number of groups sharing them.
-int gemm_block_m(int dtype, int64_t rows, int64_t groups);
+// Rows per m-tile of a GEMM for a dtype, given its total rows, the number of
+// groups (experts) sharing them, whether it is a down projection and the
+// rows of its weight matrix (output columns, both halves for SwiGLU).
+int gemm_block_m(int dtype, int64_t rows, int64_t groups, bool down, int64_t b_rows);
 // Token block of the permute kernels.
 constexpr int kPermBlock = 256;
 }  // namespace moe

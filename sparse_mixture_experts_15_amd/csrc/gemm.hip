@@ -26,6 +26,8 @@
 // few m-tiles x all n-tiles, so those resident together on one XCD share
 // operand K slabs in its L2.  fp32 path: a plain SIMT tile kernel (64 x 64,
 // K step 16).
+#include <cstdlib>
+
 #include "common.hpp"
 
 namespace moe {
@@ -105,6 +107,21 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt(0x0f70 | N);
 }
 
+// Wait until at most `later` stages of L loads each are still in flight.
+template <int L, int STAGES>
+__device__ __forceinline__ void wait_stages(int later) {
+    if constexpr (STAGES >= 4) {
+        if (later >= 2) wait_vmcnt<2 * L>();
+        else if (later == 1) wait_vmcnt<L>();
+        else wait_vmcnt<0>();
+    } else if constexpr (STAGES == 3) {
+        if (later >= 1) wait_vmcnt<L>();
+        else wait_vmcnt<0>();
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
 // LDS tile rows are 128 bytes (64 bf16 = 8 chunks of 16 bytes); chunk c of
 // row r lives at chunk c ^ (r & 7).  Measured on gfx950 this makes the
 // 16-byte MFMA fragment reads (16 rows x 4 chunks per wave) conflict-free,
@@ -140,15 +157,19 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     constexpr int ROWS_PER_LOAD = 1024 / (BK * 2);     // 8 rows per 1 KB wave load
     constexpr int A_LOADS = BM / ROWS_PER_LOAD;
     constexpr int B_LOADS = BNB / ROWS_PER_LOAD;
-    constexpr int LPW = (A_LOADS + B_LOADS) / 8;       // loads per wave per stage
-    constexpr int QA = A_LOADS / 8;                    // the first QA are A loads
+    constexpr int LOADS = A_LOADS + B_LOADS;
+    // load ins = wave + 8 q: the first B_LOADS fill B blocks, the rest A
+    // blocks; when LOADS % 8 != 0 the first LOADS % 8 waves issue one more
+    constexpr int LPW = (LOADS + 7) / 8;               // most loads of a wave per stage
+    constexpr int LPW_LO = LOADS / 8;
+    constexpr int QB = B_LOADS / 8;                    // loads q < QB are B loads
     constexpr int STAGE = (BM + BNB) * BK;             // bf16 elements per stage
     constexpr int WN = BNB / 64, WM = 8 / WN;          // wave grid
     constexpr int WROWS = BM / WM;                     // A rows per wave
     constexpr int TM = WROWS / 16;                     // 16-row fragments per wave
     constexpr int TN = 4;                              // 16-column fragments per wave
-    static_assert(A_LOADS % 8 == 0 && B_LOADS % 8 == 0, "loads must split evenly over 8 waves");
-    static_assert(WM * WN == 8 && TM >= 1, "eight waves");
+    static_assert(BM % 16 == 0 && B_LOADS % 8 == 0, "whole fragments; B loads split evenly");
+    static_assert(WM * WN == 8 && TM >= 1 && WROWS % 16 == 0, "eight waves");
     static_assert(STAGES >= 2 && STAGES <= 4 && LPW * (STAGES - 2) < 16, "pipeline depth");
     __shared__ __attribute__((aligned(1024))) bf16_t sm[STAGES * STAGE];
 
@@ -176,22 +197,24 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     const bf16_t* Bp = static_cast<const bf16_t*>(g.b) + (int64_t)tl.e * g.b_stride;
     const i32x4 rb = make_rsrc(Bp, (uint32_t)((int64_t)g.b_rows * K * 2));
 
-    // Load q of wave w fills tile rows 8 (w + 8 q) .. +7 (A rows for q < QA,
-    // then B rows); lane l -> row l/8, stored chunk l%8, which holds logical
-    // chunk (l%8) ^ (row & 7).  Invalid rows get offset kOOB.
+    // Load q of wave w (ins = w + 8 q) fills 8 rows: B rows 8 ins .. +7 for
+    // q < QB, else A rows 8 (ins - B_LOADS) .. +7; lane l -> row l/8, stored
+    // chunk l%8, which holds logical chunk (l%8) ^ (row & 7).  Invalid rows
+    // get offset kOOB.
     const int lrow = lane >> 3, pc = lane & 7;
     const int lchunk = pc ^ (lrow & 7);   // rows 8 ins + lrow: (row & 7) == lrow
     uint32_t rowoff[LPW];
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
         const int ins = wave + 8 * q;
-        if (q < QA) {
-            const int64_t r = tl.r0 + ROWS_PER_LOAD * ins + lrow;
+        if (q >= QB) {
+            const int64_t r = tl.r0 + ROWS_PER_LOAD * (ins - B_LOADS) + lrow;
             uint32_t off = kOOB;
-            if (r < tl.rend) off = (uint32_t)((g.gather ? (int64_t)g.gather[r] : r) * K * 2);
+            if (ins < LOADS && r < tl.rend)
+                off = (uint32_t)((g.gather ? (int64_t)g.gather[r] : r) * K * 2);
             rowoff[q] = off;
         } else {
-            const int row = ROWS_PER_LOAD * (ins - A_LOADS) + lrow;
+            const int row = ROWS_PER_LOAD * ins + lrow;
             int oc, br;
             brow_map<EPI>(row, n_base, g.F_split, oc, br);
             rowoff[q] = oc < N ? (uint32_t)br * (uint32_t)K * 2u : kOOB;
@@ -206,8 +229,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             // an invalid row stays >= kOOB (offsets are < 2^31); a K-tail chunk -> kOOB
             uint32_t off = rowoff[q] + (uint32_t)kc * 2u;
             off = kc < K ? off : kOOB;
-            llvm_amdgcn_raw_buffer_load_lds(q < QA ? ra : rb, (lds_u32_ptr)(st + ins * 512), 16,
-                                            (int)off, 0, 0, 0);
+            if (q < QB)
+                llvm_amdgcn_raw_buffer_load_lds(rb, (lds_u32_ptr)(st + BM * BK + ins * 512), 16,
+                                                (int)off, 0, 0, 0);
+            else if (q < LPW_LO || ins < LOADS)   // wave-uniform
+                llvm_amdgcn_raw_buffer_load_lds(ra, (lds_u32_ptr)(st + (ins - B_LOADS) * 512), 16,
+                                                (int)off, 0, 0, 0);
         }
     };
 
@@ -216,6 +243,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // 16-row fragments of this wave that hold valid rows: a group's last tile
+    // is usually partial, and fragments past its end skip their LDS reads and
+    // MFMAs (wave-uniform branches).
+    const int valid_rows = (int)min<int64_t>(tl.rend - tl.r0, (int64_t)BM);
+    const int wlive = min(TM, max(0, (valid_rows - wm * WROWS + 15) / 16));
 
     // STAGES-deep ring: stages kt+1 .. kt+STAGES-1 load while stage kt is
     // multiplied.  With split-K this workgroup runs stages [k_first, k_last).
@@ -230,38 +263,35 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     for (int kt = 0; kt < nk; ++kt) {
         // stage kt has landed once only later stages' loads are pending
         const int later = min(nk - 1, kt + STAGES - 2) - kt;
-        if constexpr (STAGES >= 4) {
-            if (later >= 2) wait_vmcnt<2 * LPW>();
-            else if (later == 1) wait_vmcnt<LPW>();
-            else wait_vmcnt<0>();
-        } else if constexpr (STAGES == 3) {
-            if (later >= 1) wait_vmcnt<LPW>();
-            else wait_vmcnt<0>();
-        } else {
-            wait_vmcnt<0>();
-        }
+        if (LPW == LPW_LO || wave < LOADS % 8) wait_stages<LPW, STAGES>(later);
+        else wait_stages<LPW_LO, STAGES>(later);
         __builtin_amdgcn_s_barrier();     // every wave's loads landed; stage kt-1 fully read
         if (kt + STAGES - 1 < nk) issue(k_first + kt + STAGES - 1);
         const bf16_t* st = sm + ((k_first + kt) % STAGES) * STAGE;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 af[TM], bfr[TN];
+            if (wlive > 0) {
+                bf16x8 af[TM], bfr[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = wm * WROWS + 16 * i + fr;
-                af[i] = *reinterpret_cast<const bf16x8*>(st + swz(row, kk * 4 + fc));
+                for (int i = 0; i < TM; ++i) {
+                    const int row = wm * WROWS + 16 * i + fr;
+                    if (i < wlive) af[i] = *reinterpret_cast<const bf16x8*>(st + swz(row, kk * 4 + fc));
+                }
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int row = wn * 64 + 16 * j + fr;
+                    bfr[j] = *reinterpret_cast<const bf16x8*>(st + BM * BK + swz(row, kk * 4 + fc));
+                }
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    if (i < wlive) {
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j],
+                                                                                acc[i][j], 0, 0, 0);
+                    }
+                }
             }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int row = wn * 64 + 16 * j + fr;
-                bfr[j] = *reinterpret_cast<const bf16x8*>(st + BM * BK + swz(row, kk * 4 + fc));
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j],
-                                                                        0, 0, 0);
         }
     }
 
@@ -275,8 +305,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     constexpr int LDC = OUTC + 16 / ESZ;                        // +16 bytes per row: no write conflicts
     constexpr int LDS_BYTES = STAGES * STAGE * 2;
     constexpr int EP_FIT = LDS_BYTES / (LDC * ESZ);
-    constexpr int EP_ROWS = EP_FIT >= BM ? BM : (EP_FIT >= WROWS ? (EP_FIT / WROWS) * WROWS : 0);
-    static_assert(EP_ROWS >= WROWS && BM % EP_ROWS == 0, "epilogue staging must hold whole waves");
+    // rows per pass: BM halved until the pass fits in the operand LDS
+    constexpr int EP_ROWS = EP_FIT >= BM ? BM
+                          : EP_FIT >= BM / 2 ? BM / 2
+                          : EP_FIT >= BM / 4 ? BM / 4
+                          : EP_FIT >= BM / 8 ? BM / 8 : 0;
+    static_assert(EP_ROWS >= 16 && EP_ROWS % 16 == 0, "epilogue pass must hold whole fragments");
     constexpr int CPR = OUTC * ESZ / 16;                        // 16-byte chunks per tile row
     const int rq = 4 * (lane >> 4);
     const int rbase = wm * WROWS;
@@ -284,9 +318,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     __syncthreads();   // every wave is done with the operand stages
 #pragma unroll 1
     for (int p0 = 0; p0 < BM; p0 += EP_ROWS) {
-        if (rbase >= p0 && rbase < p0 + EP_ROWS) {
+        if (rbase + WROWS > p0 && rbase < p0 + EP_ROWS) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
+                const int fr0 = rbase + 16 * i;   // fragment's first tile row
+                if (i >= wlive || fr0 < p0 || fr0 >= p0 + EP_ROWS) continue;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int lr = rbase - p0 + 16 * i + rq + q;   // row within the pass
@@ -449,7 +485,11 @@ hipError_t launch_bf16(hipStream_t s, const GemmArgs& g, int64_t m_tiles) {
 template <int EPI>
 hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64_t m_tiles) {
     if (m_tiles <= 0) return hipSuccess;
-    if (dtype == 1) return launch_bf16<EPI, 128, 256, 3>(s, g, m_tiles);
+    if (dtype == 1) {
+        if (bm == 256) return launch_bf16<EPI, 256, 256, 2>(s, g, m_tiles);
+        if (bm == 160) return launch_bf16<EPI, 160, 256, 3>(s, g, m_tiles);
+        return launch_bf16<EPI, 128, 256, 3>(s, g, m_tiles);
+    }
     const int opt = (EPI == EPI_SWIGLU) ? FBN / 2 : FBN;
     dim3 grid((unsigned)((g.N + opt - 1) / opt), (unsigned)m_tiles);
     hipLaunchKernelGGL(gemm_f32<EPI>, grid, dim3(256), 0, s, g);
@@ -458,12 +498,36 @@ hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64
 
 }  // namespace
 
-int gemm_block_m(int dtype, int64_t rows, int64_t groups) {
-    (void)rows;
-    (void)groups;
-    // 128 x 256 tiles with a 3-stage K = 64 ring measured fastest on every
-    // shape tried (dense up/down projections and weight-streaming groups)
-    return dtype == 1 ? 128 : FBM;
+// Tile height.  A group's weights stream from HBM once per m-tile of the
+// group, so when groups hold about a tile of rows (weight-bound: ~2 flops
+// per weight byte per row) the tile should cover a whole group with the
+// deepest ring that fits: 160-row tiles (3 stages) take groups of up to 160
+// rows, enough for a mean of ~128 rows under uniform routing.  Far smaller
+// groups leave most of any tile empty, and 128-row tiles waste the least.
+// Groups of hundreds of rows are MFMA-bound: 256-row tiles halve the LDS
+// traffic per MFMA for the up projection; the down projection keeps 128-row
+// tiles there (its short K = expert width favours the 3-stage ring), unless
+// a 256-row tile still covers the whole group.  Dense GEMMs take 256-row
+// tiles when that still leaves at least four workgroups per CU.  Measured on
+// MI355X over the layer shapes the tests use.
+int gemm_block_m(int dtype, int64_t rows, int64_t groups, bool down, int64_t b_rows) {
+    if (dtype != 1) return FBM;
+    // tuning override: MOE_GEMM_BM_{UP,DN} (grouped) / MOE_GEMM_BM_SH_{UP,DN} (dense)
+    const char* name = groups > 1 ? (down ? "MOE_GEMM_BM_DN" : "MOE_GEMM_BM_UP")
+                                  : (down ? "MOE_GEMM_BM_SH_DN" : "MOE_GEMM_BM_SH_UP");
+    if (const char* env = getenv(name)) {
+        const int v = atoi(env);
+        if (v == 128 || v == 160 || v == 256) return v;
+    }
+    if (groups <= 1) {
+        const int64_t tiles256 = (rows / 256) * ((b_rows + 255) / 256);
+        return tiles256 >= 4 * 256 ? 256 : 128;
+    }
+    const int64_t avg = rows / groups;
+    if (avg <= 96) return 128;
+    if (avg <= 136) return 160;
+    if (avg <= 224 || !down) return 256;
+    return 128;
 }
 
 hipError_t launch_gemm(hipStream_t s, int dtype, int bm, int epi, const GemmArgs& g,

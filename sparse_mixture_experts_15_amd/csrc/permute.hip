@@ -138,10 +138,13 @@ __global__ __launch_bounds__(kPermBlock) void perm_scatter(
 // after expert; entries past the last tile are (-1, 0), and the number of
 // valid tiles is stored after the table, at tiles[2 * max_tiles].  One
 // thread per expert writes its own tiles after a scan of the tile counts.
+// Workgroup y builds table y (the up and down projections may use different
+// tile heights).
 __global__ __launch_bounds__(kScanThreads) void tile_table(const int32_t* __restrict__ offsets,
-                                                          int M, int bm, int max_tiles,
-                                                          int32_t* __restrict__ tiles) {
+                                                          int M, TileTables tt) {
     __shared__ int32_t s_warp[kScanThreads / 64];
+    const int bm = tt.bm[blockIdx.y], max_tiles = tt.max_tiles[blockIdx.y];
+    int32_t* __restrict__ tiles = tt.tiles[blockIdx.y];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int32_t nt = 0, r0 = 0;
     if (tid < M) {
@@ -201,10 +204,9 @@ hipError_t launch_perm_scatter(hipStream_t s, const int32_t* idx, const int32_t*
     return hipGetLastError();
 }
 
-hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M, int bm,
-                             int64_t max_tiles, int32_t* tiles) {
-    hipLaunchKernelGGL(tile_table, dim3(1), dim3(kScanThreads), 0, s, offsets, (int)M, bm,
-                       (int)max_tiles, tiles);
+hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M,
+                             const TileTables& tt, int count) {
+    hipLaunchKernelGGL(tile_table, dim3(1, count), dim3(kScanThreads), 0, s, offsets, (int)M, tt);
     return hipGetLastError();
 }
 

@@ -36,6 +36,8 @@ PARITY = {
     # mid-size widths (>= 512), where the plain 2e-2 * RMS bar is asserted too
     "glm45_mid": S(workloads.GLM45_PREFILL, T=256, D=1024, F=512, F_shared=512),
     "glam_mid": S(workloads.GLAM_4K, T=512, D=512, F=1024).replace(M=8),
+    # ~200 rows per expert under Zipf routing: one 256-row tile per expert
+    "glm5_rows": S(workloads.GLM5_ZIPF, T=600, D=320, F=136, F_shared=136).replace(M=24),
     # fp32 SwiGLU layer with a shared expert (fp32 path of every epilogue)
     "fp32_swiglu": S(workloads.GLM45_PREFILL, T=150, D=96, F=40, F_shared=48).replace(dtype="f32"),
 }
@@ -153,6 +155,17 @@ def test_forward_deterministic_and_stream_invariant(name):
 
 
 # ------------------------------------------------------------------ edges
+
+# Every bf16 tile height on every GEMM (the library picks one per shape; the
+# MOE_GEMM_BM_* overrides force the others), covering both activations, the
+# grouped and dense GEMMs and every epilogue.
+@pytest.mark.parametrize("bm", [128, 160, 256])
+@pytest.mark.parametrize("name", ["glam_tiles", "glm45_small", "glam_mid"])
+def test_tile_heights(name, bm, monkeypatch):
+    for var in ("MOE_GEMM_BM_UP", "MOE_GEMM_BM_DN", "MOE_GEMM_BM_SH_UP", "MOE_GEMM_BM_SH_DN"):
+        monkeypatch.setenv(var, str(bm))
+    _stage_parity(PARITY[name])
+
 
 EDGE = {
     "single_token": S(workloads.GLM45_PREFILL, T=1, D=64, F=48, F_shared=48),
