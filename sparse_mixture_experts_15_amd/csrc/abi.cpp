@@ -236,6 +236,7 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     up.bias = swiglu ? nullptr : b1;
     up.c = H;
     up.tiles = tiles_up;
+    up.group_m = gemm_group_m(p.S, d->M, p.bm_up);
     up.offsets = offsets;
     up.a_rows = d->T;
     up.b_rows = (int)((swiglu ? 2 : 1) * d->F);
@@ -255,6 +256,7 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     dn.row_slot = sorted_slot;
     dn.c = O;
     dn.tiles = tiles_dn;
+    dn.group_m = gemm_group_m(p.S, d->M, p.bm_dn);
     dn.offsets = offsets;
     dn.a_rows = p.S;
     dn.b_rows = (int)d->D;

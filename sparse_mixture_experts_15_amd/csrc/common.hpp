@@ -34,9 +34,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Activations in fp32.
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU(z) = z sigmoid(z); the hardware reciprocal (1 ulp) in place of a
+// full-precision division.  z -> -inf gives -0.
+__device__ __forceinline__ float silu_f32(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+// GELU(z) = z Phi(z) with Phi(z) = erfc(-z / sqrt 2) / 2.  erfc(a), a >= 0,
+// by Abramowitz & Stegun 7.1.26 (|error| <= 1.5e-7): t P(t) exp(-a^2) with
+// t = 1 / (1 + p a) and a degree-5 polynomial P.  Branch-free, and for
+// z << 0 it yields Phi(z) directly rather than the cancellation 1 + erf.
 __device__ __forceinline__ float gelu_erf_f32(float z) {
-    return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+    const float a = fabsf(z) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, a, 1.0f));
+    float p = fmaf(1.061405429f, t, -1.453152027f);
+    p = fmaf(p, t, 1.421413741f);
+    p = fmaf(p, t, -0.284496736f);
+    p = fmaf(p, t, 0.254829592f);
+    const float lower = 0.5f * t * p * __expf(-a * a);   // Phi(-|z|)
+    return z * (z >= 0.f ? 1.0f - lower : lower);
 }
 
 // Kernel labels (indices into the profiling table).
@@ -75,7 +90,13 @@ struct GemmArgs {
     int F_split;              // SWIGLU: row offset of the up block in B (= N)
     int k_split;              // dense DOWN_F32 only: K chunks, each writing its own
                               // [rows, N] partial at c + chunk * rows * N (0 = 1)
+    int group_m;              // m-tiles per group of the tile order (0 = 4)
 };
+
+// m-tiles per group of the tile order for a grouped GEMM: about the m-tiles
+// one expert spans, so that the workgroups one XCD runs together share that
+// expert's weight tiles and rows in its L2.
+int gemm_group_m(int64_t rows, int64_t groups, int bm);
 
 }  // namespace moe
 

@@ -77,7 +77,6 @@ __device__ __forceinline__ void brow_map(int b, int n_base, int F_split, int& ou
 constexpr int BK = 64;       // K per pipeline stage: 128-byte row segments
 constexpr int NT = 512;      // 8 waves: 2 (rows) x 4 (B rows)
 constexpr uint32_t kOOB = 0x80000000u;   // byte offset past every buffer: loads zero
-constexpr int GROUP_M = 4;   // m-tiles per group in the tile order
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint32_t* lds_u32_ptr;
@@ -130,21 +129,22 @@ __device__ __forceinline__ int swz(int row, int c) { return row * BK + ((c ^ (ro
 
 // Workgroup order.  Hardware hands consecutive workgroup ids to the eight
 // XCDs in turn; the ids are first regrouped so that consecutive logical
-// tiles land on one XCD, then tiles are ordered in groups of GROUP_M m-tiles
+// tiles land on one XCD, then tiles are ordered in groups of group_m m-tiles
 // with the n-tiles inside a group, so the ~32 workgroups one XCD runs at a
 // time cover a few m-tiles x several n-tiles and share both operands' K
 // slabs in that XCD's L2.  `m_tiles` is the number of valid m-tiles (the
 // grid may be larger; ids past m_tiles x n_tiles return false), so every
 // XCD gets real work.
-__device__ __forceinline__ bool tile_coords(int m_tiles, int n_tiles, int p, int& mt, int& nt) {
+__device__ __forceinline__ bool tile_coords(int m_tiles, int n_tiles, int group_m, int p, int& mt,
+                                            int& nt) {
     const int G = m_tiles * n_tiles;
     if (p >= G) return false;
     const int per = G / 8;
     if (p < per * 8) p = (p & 7) * per + (p >> 3);
-    const int group = p / (GROUP_M * n_tiles);
-    const int first = group * GROUP_M;
-    const int gsize = min(m_tiles - first, GROUP_M);
-    const int in = p - group * GROUP_M * n_tiles;
+    const int group = p / (group_m * n_tiles);
+    const int first = group * group_m;
+    const int gsize = min(m_tiles - first, group_m);
+    const int in = p - group * group_m * n_tiles;
     mt = first + in % gsize;
     nt = in / gsize;
     return true;
@@ -180,7 +180,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     const int per_split = m_valid * n_tiles;
     const int kc_id = (int)blockIdx.x / max(per_split, 1);
     int mt, nt;
-    if (kc_id >= nsplit || !tile_coords(m_valid, n_tiles, (int)blockIdx.x - kc_id * per_split, mt, nt))
+    if (kc_id >= nsplit || !tile_coords(m_valid, n_tiles, g.group_m > 0 ? g.group_m : 4,
+                                             (int)blockIdx.x - kc_id * per_split, mt, nt))
         return;
     Tile tl;
     if (!tile_of(g, mt, BM, tl)) return;
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
                     if (i < wlive) {
 #pragma unroll
                         for (int j = 0; j < TN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j],
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i],
                                                                                 acc[i][j], 0, 0, 0);
                     }
                 }
@@ -295,94 +296,70 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
         }
     }
 
-    // Epilogue: the output tile is staged through the (now idle) LDS ring in
-    // passes of up to EP_ROWS rows, then written as whole rows with 16-byte
-    // vector stores.  MFMA 16x16 layout: lane holds column lane%16 and rows
-    // 4*(lane/16) + q of each 16x16 block.
-    constexpr bool OUT_BF16 = (EPI == EPI_SWIGLU || EPI == EPI_GELU);
-    constexpr int ESZ = OUT_BF16 ? 2 : 4;
-    constexpr int OUTC = (EPI == EPI_SWIGLU) ? BNB / 2 : BNB;   // output columns in the tile
-    constexpr int LDC = OUTC + 16 / ESZ;                        // +16 bytes per row: no write conflicts
-    constexpr int LDS_BYTES = STAGES * STAGE * 2;
-    constexpr int EP_FIT = LDS_BYTES / (LDC * ESZ);
-    // rows per pass: BM halved until the pass fits in the operand LDS
-    constexpr int EP_ROWS = EP_FIT >= BM ? BM
-                          : EP_FIT >= BM / 2 ? BM / 2
-                          : EP_FIT >= BM / 4 ? BM / 4
-                          : EP_FIT >= BM / 8 ? BM / 8 : 0;
-    static_assert(EP_ROWS >= 16 && EP_ROWS % 16 == 0, "epilogue pass must hold whole fragments");
-    constexpr int CPR = OUTC * ESZ / 16;                        // 16-byte chunks per tile row
-    const int rq = 4 * (lane >> 4);
-    const int rbase = wm * WROWS;
+    // Epilogue straight from registers.  The MFMAs take the B fragment as
+    // their first operand, so for fragment (i, j) lane l holds tile row
+    // 16 i + l % 16 of its wave and the four consecutive fragment columns
+    // 4 (l / 16) .. +3: one 8-byte (bf16) or 16-byte (fp32) store each.  The
+    // four lanes of a row write 32 / 64 contiguous bytes, and a row's
+    // fragments fill whole cache lines in L2.
+    const int lr = lane & 15, lc = 4 * (lane >> 4);
     const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
-    __syncthreads();   // every wave is done with the operand stages
-#pragma unroll 1
-    for (int p0 = 0; p0 < BM; p0 += EP_ROWS) {
-        if (rbase + WROWS > p0 && rbase < p0 + EP_ROWS) {
+    constexpr bool OUT_BF16 = (EPI == EPI_SWIGLU || EPI == EPI_GELU);
+    constexpr bool HAS_BIAS = (EPI == EPI_GELU || EPI == EPI_DOWN_SCALED);
+    constexpr int OUT_FR = (EPI == EPI_SWIGLU) ? TN / 2 : TN;   // output fragments per row
+    constexpr int OUT_W = (EPI == EPI_SWIGLU) ? 32 : 64;        // output columns per wave
+    const bool vec = (N % 4) == 0;                              // aligned 4-column groups
+    float bv[OUT_FR][4];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int fr0 = rbase + 16 * i;   // fragment's first tile row
-                if (i >= wlive || fr0 < p0 || fr0 >= p0 + EP_ROWS) continue;
+    for (int j = 0; j < OUT_FR; ++j) {
+        const int n = n_base + OUT_W * wn + 16 * j + lc;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int lr = rbase - p0 + 16 * i + rq + q;   // row within the pass
-                    const int64_t r = tl.r0 + rbase + 16 * i + rq + q;
-                    if (EPI == EPI_SWIGLU) {
-                        bf16_t* sc = reinterpret_cast<bf16_t*>(sm) + lr * LDC;
+        for (int q = 0; q < 4; ++q)
+            bv[j][q] = (HAS_BIAS && bias && n + q < N)
+                           ? bf16_to_f32(bias[(int64_t)tl.e * N + n + q]) : 0.f;
+    }
 #pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            sc[32 * wn + 16 * j + fr] =
-                                f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + 2][q]);
-                    } else if (EPI == EPI_GELU) {
-                        bf16_t* sc = reinterpret_cast<bf16_t*>(sm) + lr * LDC;
+    for (int i = 0; i < TM; ++i) {
+        if (i >= wlive) continue;
+        const int64_t r = tl.r0 + wm * WROWS + 16 * i + lr;
+        if (r >= tl.rend) continue;
+        float wr = 1.f;
+        if (EPI == EPI_DOWN_SCALED) wr = g.row_w[g.row_slot[r]];
 #pragma unroll
-                        for (int j = 0; j < TN; ++j) {
-                            const int n = n_base + 64 * wn + 16 * j + fr;
-                            const float bv =
-                                (bias && n < N) ? bf16_to_f32(bias[(int64_t)tl.e * N + n]) : 0.f;
-                            sc[64 * wn + 16 * j + fr] = f32_to_bf16(gelu_erf_f32(acc[i][j][q] + bv));
-                        }
-                    } else {
-                        float* sc = reinterpret_cast<float*>(sm) + lr * LDC;
-                        float wr = 1.f;
-                        if (EPI == EPI_DOWN_SCALED && r < tl.rend) wr = g.row_w[g.row_slot[r]];
+        for (int j = 0; j < OUT_FR; ++j) {
+            const int n = n_base + OUT_W * wn + 16 * j + lc;
+            if (n >= N) continue;
+            float v[4];
 #pragma unroll
-                        for (int j = 0; j < TN; ++j) {
-                            const int n = n_base + 64 * wn + 16 * j + fr;
-                            float v = acc[i][j][q];
-                            if (EPI == EPI_DOWN_SCALED) {
-                                const float bv = (bias && n < N)
-                                                     ? bf16_to_f32(bias[(int64_t)tl.e * N + n]) : 0.f;
-                                v = wr * (v + bv);
-                            }
-                            sc[64 * wn + 16 * j + fr] = v;
-                        }
-                    }
+            for (int q = 0; q < 4; ++q) {
+                if (EPI == EPI_SWIGLU) v[q] = silu_f32(acc[i][j][q]) * acc[i][j + 2][q];
+                else if (EPI == EPI_GELU) v[q] = gelu_erf_f32(acc[i][j][q] + bv[j][q]);
+                else if (EPI == EPI_DOWN_SCALED) v[q] = wr * (acc[i][j][q] + bv[j][q]);
+                else v[q] = acc[i][j][q];
+            }
+            if constexpr (OUT_BF16) {
+                bf16_t* dst = static_cast<bf16_t*>(g.c) + r * N + n;
+                if (vec && n + 4 <= N) {
+                    uint2 pk;
+                    pk.x = pack_bf16x2(v[0], v[1]);
+                    pk.y = pack_bf16x2(v[2], v[3]);
+                    *reinterpret_cast<uint2*>(dst) = pk;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (n + q < N) dst[q] = f32_to_bf16(v[q]);
+                }
+            } else {
+                float* dst = static_cast<float*>(g.c) + (int64_t)kc_id * g.dense_rows * N + r * N + n;
+                if (vec && n + 4 <= N) {
+                    *reinterpret_cast<floatx4*>(dst) = floatx4{v[0], v[1], v[2], v[3]};
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (n + q < N) dst[q] = v[q];
                 }
             }
         }
-        __syncthreads();
-        // whole rows out: chunk c of the pass -> row c / CPR, 16 bytes at column
-        // (c % CPR) * 16 / ESZ.  The expert GEMMs have N % 8 == 0 (whole
-        // chunks); the router's N = 3M may end mid-chunk: that chunk is
-        // written element by element.
-        constexpr int VE = 16 / ESZ;
-        for (int c = tid; c < EP_ROWS * CPR; c += NT) {
-            const int lr = c / CPR, ch = c % CPR;
-            const int64_t r = tl.r0 + p0 + lr;
-            const int n = n_base + ch * VE;
-            if (r >= tl.rend || n >= N) continue;
-            const char* src = reinterpret_cast<const char*>(sm) + (lr * LDC) * ESZ + ch * 16;
-            char* dst = static_cast<char*>(g.c) +
-                        ((int64_t)kc_id * g.dense_rows * N + r * N + n) * ESZ;
-            if (n + VE <= N && (N % VE) == 0) {
-                *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-            } else {
-                for (int e = 0; e < VE && n + e < N; ++e)
-                    for (int b = 0; b < ESZ; ++b) dst[e * ESZ + b] = src[e * ESZ + b];
-            }
-        }
-        if (p0 + EP_ROWS < BM) __syncthreads();
     }
 }
 
@@ -528,6 +505,15 @@ int gemm_block_m(int dtype, int64_t rows, int64_t groups, bool down, int64_t b_r
     if (avg <= 136) return 160;
     if (avg <= 224 || !down) return 256;
     return 128;
+}
+
+int gemm_group_m(int64_t rows, int64_t groups, int bm) {
+    if (const char* env = getenv("MOE_GEMM_GROUP_M")) {   // tuning override
+        const int v = atoi(env);
+        if (v >= 1 && v <= 16) return v;
+    }
+    const int64_t per = (rows / (groups > 0 ? groups : 1) + bm / 2) / bm;
+    return per < 1 ? 1 : per > 4 ? 4 : (int)per;
 }
 
 hipError_t launch_gemm(hipStream_t s, int dtype, int bm, int epi, const GemmArgs& g,
