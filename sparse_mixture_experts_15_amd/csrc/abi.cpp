@@ -40,7 +40,7 @@ struct Plan {
     int bm_up = 0, bm_dn = 0, bm_sh_up = 0, bm_sh_dn = 0;
     size_t esz = 0;
     size_t idx = 0, w = 0, counts = 0, offsets = 0, sorted_token = 0, sorted_slot = 0,
-           slot_row = 0, hist = 0, tiles_up = 0, tiles_dn = 0, H = 0, O = 0, Hsh = 0, Ysh = 0, route = 0,
+           slot_row = 0, hist = 0, row_scale = 0, tiles_up = 0, tiles_dn = 0, H = 0, O = 0, Hsh = 0, Ysh = 0, route = 0,
            total = 0;
 };
 
@@ -72,6 +72,7 @@ Plan make_plan(const moe_desc* d) {
     p.sorted_slot = take(p.S * 4);
     p.slot_row = take(p.S * 4);
     p.hist = take((size_t)p.nblk * d->M * 4);
+    p.row_scale = take(p.S * 4);
     p.tiles_up = take(((size_t)p.max_tiles_up * 2 + 1) * 4);
     p.tiles_dn = p.bm_dn == p.bm_up ? p.tiles_up : take(((size_t)p.max_tiles_dn * 2 + 1) * 4);
     p.H = take((size_t)p.S * d->F * p.esz);
@@ -225,8 +226,11 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
                   {(int)p.max_tiles_up, (int)p.max_tiles_dn},
                   {tiles_up, tiles_dn}};
     const int ntables = tiles_dn == tiles_up ? 1 : 2;
-    TRY(run(h, s, L_TILE_TABLE,
-            [&] { return launch_tile_table(s, offsets, d->M, tt, ntables); }));
+    float* row_scale = at<float>(ws, p.row_scale);
+    TRY(run(h, s, L_TILE_TABLE, [&] {
+        const hipError_t e = launch_tile_table(s, offsets, d->M, tt, ntables);
+        return e != hipSuccess ? e : launch_row_scales(s, sorted_slot, w, p.S, row_scale);
+    }));
     const bool swiglu = d->act == MOE_ACT_SWIGLU;
     GemmArgs up{};
     up.a = x;
@@ -236,6 +240,7 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     up.bias = swiglu ? nullptr : b1;
     up.c = H;
     up.tiles = tiles_up;
+    up.dense_rows = p.S;
     up.group_m = gemm_group_m(p.S, d->M, p.bm_up);
     up.offsets = offsets;
     up.a_rows = d->T;
@@ -252,8 +257,8 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     dn.b = W2;
     dn.b_stride = d->D * d->F;
     dn.bias = swiglu ? nullptr : b2;
-    dn.row_w = w;
-    dn.row_slot = sorted_slot;
+    dn.row_w = row_scale;
+    dn.dense_rows = p.S;
     dn.c = O;
     dn.tiles = tiles_dn;
     dn.group_m = gemm_group_m(p.S, d->M, p.bm_dn);

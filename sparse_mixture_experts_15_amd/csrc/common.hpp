@@ -20,17 +20,14 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
     return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 (NaN kept quiet).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
-        return static_cast<bf16_t>((u >> 16) | 0x0040u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<bf16_t>(u >> 16);
-}
-
+// fp32 -> bf16 with round-to-nearest-even (gfx950's v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float floatx2_v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2_v{lo, hi}, bf16x2_v));
+}
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 // Activations in fp32.
@@ -77,12 +74,11 @@ struct GemmArgs {
     const void* b;            // [E, NB, K] dtype
     int64_t b_stride;         // elements between experts in b
     const void* bias;         // [E, N] dtype, nullable (GELU b1 or DOWN b2)
-    const float* row_w;       // per flat slot weight (DOWN_SCALED)
-    const int32_t* row_slot;  // flat slot of sorted row r (DOWN_SCALED)
+    const float* row_w;       // DOWN_SCALED: scale of sorted row r (its slot's weight)
     void* c;                  // [rows, N]
     const int32_t* tiles;     // grouped: per m-tile (expert, row0); NULL: dense
     const int32_t* offsets;   // grouped: expert row ranges [M+1]
-    int64_t dense_rows;       // dense: total rows
+    int64_t dense_rows;       // total rows (dense) / sorted rows (grouped)
     int64_t a_rows;           // rows of the matrix `a` points to (gathered loads)
     int b_rows;               // rows of one expert's weight block
     int K;                    // reduction length
@@ -122,6 +118,9 @@ struct TileTables {
     int max_tiles[2];
     int32_t* tiles[2];
 };
+// row_scale[r] = w[sorted_slot[r]] for the S sorted rows.
+hipError_t launch_row_scales(hipStream_t s, const int32_t* sorted_slot, const float* w, int64_t S,
+                             float* row_scale);
 hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M,
                              const TileTables& tt, int count);
 hipError_t launch_gemm(hipStream_t s, int dtype, int bm, int epi, const GemmArgs& g,

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
         const int64_t r = tl.r0 + wm * WROWS + 16 * i + lr;
         if (r >= tl.rend) continue;
         float wr = 1.f;
-        if (EPI == EPI_DOWN_SCALED) wr = g.row_w[g.row_slot[r]];
+        if (EPI == EPI_DOWN_SCALED) wr = g.row_w[r];
 #pragma unroll
         for (int j = 0; j < OUT_FR; ++j) {
             const int n = n_base + OUT_W * wn + 16 * j + lc;
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs g) {
                 if (n < N) C[r * N + n] = silu_f32(acc[i][j]) * acc[i][j + 2];
             }
         } else {
-            const float wr = (EPI == EPI_DOWN_SCALED) ? g.row_w[g.row_slot[r]] : 1.f;
+            const float wr = (EPI == EPI_DOWN_SCALED) ? g.row_w[r] : 1.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n = n_base + tx + 16 * j;
@@ -453,6 +453,7 @@ template <int EPI, int BMv, int BNv, int STv>
 hipError_t launch_bf16(hipStream_t s, const GemmArgs& g, int64_t m_tiles) {
     const int opt = (EPI == EPI_SWIGLU) ? BNv / 2 : BNv;
     const int n_tiles = (g.N + opt - 1) / opt;
+    if (g.k_split > (g.K + BK - 1) / BK) return hipErrorInvalidValue;   // each K chunk needs a stage
     const int64_t total = m_tiles * n_tiles * (g.k_split > 1 ? g.k_split : 1);
     hipLaunchKernelGGL((gemm_bf16<EPI, BMv, BNv, STv>), dim3((unsigned)total), dim3(NT), 0, s, g,
                        (int)m_tiles, n_tiles);

@@ -176,6 +176,15 @@ __global__ __launch_bounds__(kScanThreads) void tile_table(const int32_t* __rest
     if (tid == 0) tiles[2 * max_tiles] = total;
 }
 
+// Gate weight of each sorted row, in sorted order (the down projection's
+// row scale).
+__global__ __launch_bounds__(256) void row_scales(const int32_t* __restrict__ sorted_slot,
+                                                 const float* __restrict__ w, int64_t S,
+                                                 float* __restrict__ row_scale) {
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (r < S) row_scale[r] = w[sorted_slot[r]];
+}
+
 }  // namespace
 
 hipError_t launch_perm_count(hipStream_t s, const int32_t* idx, int32_t* hist, int64_t T, int k,
@@ -201,6 +210,14 @@ hipError_t launch_perm_scatter(hipStream_t s, const int32_t* idx, const int32_t*
     hipLaunchKernelGGL(perm_scatter, dim3(nblk), dim3(kPermBlock),
                        4 * M * sizeof(unsigned long long), s, idx, hist, offsets, (int)T, k,
                        (int)M, sorted_token, sorted_slot, slot_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_scales(hipStream_t s, const int32_t* sorted_slot, const float* w, int64_t S,
+                             float* row_scale) {
+    if (S <= 0) return hipSuccess;
+    hipLaunchKernelGGL(row_scales, dim3((unsigned)((S + 255) / 256)), dim3(256), 0, s, sorted_slot,
+                       w, S, row_scale);
     return hipGetLastError();
 }
 
