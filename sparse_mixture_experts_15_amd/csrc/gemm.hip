@@ -74,7 +74,7 @@ __device__ __forceinline__ void brow_map(int b, int n_base, int F_split, int& ou
 
 // ------------------------------------------------------------ bf16 / MFMA
 
-constexpr int BK = 64;       // K per pipeline stage: 128-byte row segments
+constexpr int BK = 64;       // default K per pipeline stage: 128-byte row segments
 constexpr int NT = 512;      // 8 waves: 2 (rows) x 4 (B rows)
 constexpr uint32_t kOOB = 0x80000000u;   // byte offset past every buffer: loads zero
 
@@ -99,33 +99,53 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
 }
 
 // s_waitcnt vmcnt(n) leaving the other counters untouched (gfx9 encoding:
-// vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8).
+// vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14, expcnt bits 6:4,
+// lgkmcnt bits 11:8).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 16, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// Wait until at most `later` stages of L loads each are still in flight.
+// Wait until at most `later` (0 .. STAGES-2) stages of L loads each are
+// still in flight.
 template <int L, int STAGES>
 __device__ __forceinline__ void wait_stages(int later) {
-    if constexpr (STAGES >= 4) {
-        if (later >= 2) wait_vmcnt<2 * L>();
-        else if (later == 1) wait_vmcnt<L>();
-        else wait_vmcnt<0>();
-    } else if constexpr (STAGES == 3) {
-        if (later >= 1) wait_vmcnt<L>();
-        else wait_vmcnt<0>();
-    } else {
-        wait_vmcnt<0>();
+    if constexpr (STAGES >= 5) {
+        if (later >= 3) {
+            wait_vmcnt<3 * L>();
+            return;
+        }
     }
+    if constexpr (STAGES >= 4) {
+        if (later >= 2) {
+            wait_vmcnt<2 * L>();
+            return;
+        }
+    }
+    if constexpr (STAGES >= 3) {
+        if (later >= 1) {
+            wait_vmcnt<L>();
+            return;
+        }
+    }
+    wait_vmcnt<0>();
 }
 
-// LDS tile rows are 128 bytes (64 bf16 = 8 chunks of 16 bytes); chunk c of
-// row r lives at chunk c ^ (r & 7).  Measured on gfx950 this makes the
-// 16-byte MFMA fragment reads (16 rows x 4 chunks per wave) conflict-free,
-// as fast as contiguous reads; unswizzled or padded rows run at half rate.
-__device__ __forceinline__ int swz(int row, int c) { return row * BK + ((c ^ (row & 7)) << 3); }
+// LDS tile rows are KS bf16 (KS = 64: 128 bytes, 8 chunks of 16 bytes;
+// KS = 32: 64 bytes, 4 chunks).  Chunk c of row r lives at chunk
+// c ^ (r & 7) (128-byte rows) or c ^ ((r >> 1) & 3) (64-byte rows).
+// Measured on gfx950 these make the 16-byte MFMA fragment reads (16 rows x
+// 4 chunks per wave) conflict-free, as fast as contiguous reads; unswizzled
+// or padded rows run at half rate.
+template <int KS>
+__device__ __forceinline__ int swz_chunk(int row) {
+    return KS == 64 ? (row & 7) : ((row >> 1) & 3);
+}
+template <int KS>
+__device__ __forceinline__ int swz(int row, int c) {
+    return row * KS + ((c ^ swz_chunk<KS>(row)) << 3);
+}
 
 // Workgroup order.  Hardware hands consecutive workgroup ids to the eight
 // XCDs in turn; the ids are first regrouped so that consecutive logical
@@ -151,10 +171,13 @@ __device__ __forceinline__ bool tile_coords(int m_tiles, int n_tiles, int group_
 }
 
 // One tile configuration: BM A rows x BNB B rows per workgroup, STAGES LDS
-// stages of K = 64; the eight waves form WM x WN with 64 B rows per wave.
-template <int EPI, int BM, int BNB, int STAGES>
+// stages of K = KS (64 or 32); the eight waves form WM x WN with 64 B rows
+// per wave.
+template <int EPI, int BM, int BNB, int STAGES, int KS>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int n_tiles) {
-    constexpr int ROWS_PER_LOAD = 1024 / (BK * 2);     // 8 rows per 1 KB wave load
+    constexpr int BK = KS;
+    constexpr int CPR = BK / 8;                        // 16-byte chunks per row
+    constexpr int ROWS_PER_LOAD = 1024 / (BK * 2);     // rows per 1 KB wave load
     constexpr int A_LOADS = BM / ROWS_PER_LOAD;
     constexpr int B_LOADS = BNB / ROWS_PER_LOAD;
     constexpr int LOADS = A_LOADS + B_LOADS;
@@ -170,7 +193,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     constexpr int TN = 4;                              // 16-column fragments per wave
     static_assert(BM % 16 == 0 && B_LOADS % 8 == 0, "whole fragments; B loads split evenly");
     static_assert(WM * WN == 8 && TM >= 1 && WROWS % 16 == 0, "eight waves");
-    static_assert(STAGES >= 2 && STAGES <= 4 && LPW * (STAGES - 2) < 16, "pipeline depth");
+    static_assert(STAGES >= 2 && STAGES <= 5 && LPW * (STAGES - 2) < 64, "pipeline depth");
+    static_assert(BK == 64 || BK == 32, "stage depth");
     __shared__ __attribute__((aligned(1024))) bf16_t sm[STAGES * STAGE];
 
     // grouped: the valid m-tile count follows the tile table
@@ -198,12 +222,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     const bf16_t* Bp = static_cast<const bf16_t*>(g.b) + (int64_t)tl.e * g.b_stride;
     const i32x4 rb = make_rsrc(Bp, (uint32_t)((int64_t)g.b_rows * K * 2));
 
-    // Load q of wave w (ins = w + 8 q) fills 8 rows: B rows 8 ins .. +7 for
-    // q < QB, else A rows 8 (ins - B_LOADS) .. +7; lane l -> row l/8, stored
-    // chunk l%8, which holds logical chunk (l%8) ^ (row & 7).  Invalid rows
-    // get offset kOOB.
-    const int lrow = lane >> 3, pc = lane & 7;
-    const int lchunk = pc ^ (lrow & 7);   // rows 8 ins + lrow: (row & 7) == lrow
+    // Load q of wave w (ins = w + 8 q) fills ROWS_PER_LOAD rows: B rows of
+    // block ins for q < QB, else A rows of block ins - B_LOADS; lane l -> row
+    // l / CPR of the block, stored chunk l % CPR, which holds the logical
+    // chunk given by the swizzle.  Invalid rows get offset kOOB.
+    const int lrow = lane / CPR, pc = lane % CPR;
+    // blocks start at multiples of 8 rows, so the swizzle depends on lrow only
+    const int lchunk = pc ^ swz_chunk<BK>(lrow);
     uint32_t rowoff[LPW];
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
@@ -269,19 +294,55 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
         __builtin_amdgcn_s_barrier();     // every wave's loads landed; stage kt-1 fully read
         if (kt + STAGES - 1 < nk) issue(k_first + kt + STAGES - 1);
         const bf16_t* st = sm + ((k_first + kt) % STAGES) * STAGE;
+        if (TM <= 4 && wlive == TM) {
+            // whole fragments: one straight block (every fragment read, then
+            // the MFMAs) the scheduler can overlap freely.  Measured faster
+            // with 4 row fragments per wave; with 5 slower and with 8 it
+            // spills, so larger tiles keep the path below.
+            constexpr int KH = BK / 32;
+            constexpr int PRE = KH;
+            bf16x8 af[KH][TM], bfr[KH][TN];
+            auto read_frags = [&](int kk) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+                for (int i = 0; i < TM; ++i)
+                    af[kk][i] = *reinterpret_cast<const bf16x8*>(
+                        st + swz<BK>(wm * WROWS + 16 * i + fr, kk * 4 + fc));
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    bfr[kk][j] = *reinterpret_cast<const bf16x8*>(
+                        st + BM * BK + swz<BK>(wn * 64 + 16 * j + fr, kk * 4 + fc));
+            };
+#pragma unroll
+            for (int kk = 0; kk < PRE; ++kk) read_frags(kk);
+#pragma unroll
+            for (int kk = 0; kk < KH; ++kk) {
+                if (kk >= PRE) {
+                    __builtin_amdgcn_sched_barrier(0);   // keep this half's reads here
+                    read_frags(kk);
+                }
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[kk][j], af[kk][i],
+                                                                            acc[i][j], 0, 0, 0);
+            }
+            continue;
+        }
+#pragma unroll
+        for (int kk = 0; kk < BK / 32; ++kk) {
             if (wlive > 0) {
                 bf16x8 af[TM], bfr[TN];
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
                     const int row = wm * WROWS + 16 * i + fr;
-                    if (i < wlive) af[i] = *reinterpret_cast<const bf16x8*>(st + swz(row, kk * 4 + fc));
+                    if (i < wlive)
+                        af[i] = *reinterpret_cast<const bf16x8*>(st + swz<BK>(row, kk * 4 + fc));
                 }
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int row = wn * 64 + 16 * j + fr;
-                    bfr[j] = *reinterpret_cast<const bf16x8*>(st + BM * BK + swz(row, kk * 4 + fc));
+                    bfr[j] = *reinterpret_cast<const bf16x8*>(st + BM * BK + swz<BK>(row, kk * 4 + fc));
                 }
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
@@ -449,13 +510,13 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs g) {
     }
 }
 
-template <int EPI, int BMv, int BNv, int STv>
+template <int EPI, int BMv, int BNv, int STv, int KS = 64>
 hipError_t launch_bf16(hipStream_t s, const GemmArgs& g, int64_t m_tiles) {
     const int opt = (EPI == EPI_SWIGLU) ? BNv / 2 : BNv;
     const int n_tiles = (g.N + opt - 1) / opt;
     if (g.k_split > (g.K + BK - 1) / BK) return hipErrorInvalidValue;   // each K chunk needs a stage
     const int64_t total = m_tiles * n_tiles * (g.k_split > 1 ? g.k_split : 1);
-    hipLaunchKernelGGL((gemm_bf16<EPI, BMv, BNv, STv>), dim3((unsigned)total), dim3(NT), 0, s, g,
+    hipLaunchKernelGGL((gemm_bf16<EPI, BMv, BNv, STv, KS>), dim3((unsigned)total), dim3(NT), 0, s, g,
                        (int)m_tiles, n_tiles);
     return hipGetLastError();
 }
@@ -464,6 +525,7 @@ template <int EPI>
 hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64_t m_tiles) {
     if (m_tiles <= 0) return hipSuccess;
     if (dtype == 1) {
+        // (256 x 256 with K = 32 stages, 4 or 5 deep, measured slower than 2 x 64)
         if (bm == 256) return launch_bf16<EPI, 256, 256, 2>(s, g, m_tiles);
         if (bm == 160) return launch_bf16<EPI, 160, 256, 3>(s, g, m_tiles);
         return launch_bf16<EPI, 128, 256, 3>(s, g, m_tiles);
