@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     int rows[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) rows[j] = (j < k) ? slot_row[(int64_t)t * k + j] : -1;
+#pragma unroll 2
     for (int d0 = lane * V; d0 < D; d0 += 64 * V) {
         float acc[V];
 #pragma unroll

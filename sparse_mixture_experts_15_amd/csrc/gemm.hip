@@ -297,12 +297,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
         if (TM <= 4 && wlive == TM) {
             // whole fragments: one straight block (every fragment read, then
             // the MFMAs) the scheduler can overlap freely.  Measured faster
-            // with 4 row fragments per wave; with 5 slower and with 8 it
-            // spills, so larger tiles keep the path below.
-            constexpr int KH = BK / 32;
-            constexpr int PRE = KH;
-            bf16x8 af[KH][TM], bfr[KH][TN];
-            auto read_frags = [&](int kk) {
+            // with 4 row fragments per wave; with 5 slower and with 8 the
+            // doubled fragment registers spill, so larger tiles keep the
+            // path below.
+            bf16x8 af[BK / 32][TM], bfr[BK / 32][TN];
+#pragma unroll
+            for (int kk = 0; kk < BK / 32; ++kk) {
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
                     af[kk][i] = *reinterpret_cast<const bf16x8*>(
@@ -311,22 +311,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
                 for (int j = 0; j < TN; ++j)
                     bfr[kk][j] = *reinterpret_cast<const bf16x8*>(
                         st + BM * BK + swz<BK>(wn * 64 + 16 * j + fr, kk * 4 + fc));
-            };
+            }
 #pragma unroll
-            for (int kk = 0; kk < PRE; ++kk) read_frags(kk);
-#pragma unroll
-            for (int kk = 0; kk < KH; ++kk) {
-                if (kk >= PRE) {
-                    __builtin_amdgcn_sched_barrier(0);   // keep this half's reads here
-                    read_frags(kk);
-                }
+            for (int kk = 0; kk < BK / 32; ++kk)
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[kk][j], af[kk][i],
                                                                             acc[i][j], 0, 0, 0);
-            }
             continue;
         }
 #pragma unroll
