@@ -151,6 +151,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-aux-stream", action="store_true")
+    ap.add_argument("--weights", choices=["tiled", "rows"], default="tiled",
+                    help="expert/shared weight layout (tiled: copied once before timing)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -173,15 +175,23 @@ def main():
     cfg = workloads.get(args.config)
     log(f"workload {cfg.name}: generating inputs on the GPU")
     t = workloads.generate(cfg, seed=args.seed, device="cuda")
-    L = MoELayer(B.make_desc(cfg))
+    L = MoELayer(B.make_desc(cfg, weight_layout=args.weights))
     d = L.desc
+    tg = dict(t)   # what the GPU reads; t keeps the row-major weights for the oracle
+    if args.weights == "tiled":
+        # the weights' load-time copy into the tiled layout (not timed)
+        for name in ("W1", "W2", "Wsh_gu", "Wsh_dn"):
+            if tg.get(name) is not None:
+                tg[name] = B.tile_weights(L.handle, d, name, tg[name])
+        torch.cuda.synchronize()
     main = torch.cuda.current_stream()
     aux = None if args.no_aux_stream else torch.cuda.Stream()
     y = torch.empty_like(t["x"])
 
     def step():
-        B.moe_forward(L.handle, d, t["x"], t["W_r"], t["bias"], t["W1"], t["b1"], t["W2"],
-                      t["b2"], t["Wsh_gu"], t["Wsh_dn"], y, L.ws, stream=main, aux_stream=aux)
+        B.moe_forward(L.handle, d, tg["x"], tg["W_r"], tg["bias"], tg["W1"], tg["b1"], tg["W2"],
+                      tg["b2"], tg["Wsh_gu"], tg["Wsh_dn"], y, L.ws, stream=main,
+                      aux_stream=aux)
 
     # realised routing (touched experts) for the algorithmic byte counts
     idx = torch.empty(cfg.T * cfg.k, dtype=torch.int32, device="cuda")
@@ -253,7 +263,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "D": cfg.D, "M": cfg.M, "F": cfg.F,
                    "k": cfg.k, "F_shared": cfg.F_shared, "scorer": cfg.scorer, "act": cfg.act,
                    "alpha": cfg.alpha, "seed": args.seed, "touched_experts": U,
-                   "aux_stream": aux is not None},
+                   "aux_stream": aux is not None, "weights": args.weights},
         "active_tflops": round(active_tflops, 2),
         "alg_hbm_gbps": round(alg_gbps, 1),
         "layer_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),

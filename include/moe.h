@@ -65,6 +65,10 @@ typedef enum {
 enum { MOE_SCORER_SOFTMAX = 0, MOE_SCORER_SIGMOID = 1 };
 enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GELU = 1 };
 enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
+/* Layout of the weight matrices W1, W2, Wsh_gu, Wsh_dn (see moe_tile_weights). */
+enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 };
+/* Weight matrices, for moe_tiled_weight_size / moe_tile_weights. */
+enum { MOE_WEIGHT_W1 = 0, MOE_WEIGHT_W2 = 1, MOE_WEIGHT_SH_GU = 2, MOE_WEIGHT_SH_DN = 3 };
 
 #define MOE_MAX_K 16
 #define MOE_MAX_EXPERTS 1024
@@ -80,7 +84,10 @@ enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
  *            dtype; fp32 keeps the fp32 accumulation unrounded)
  *   renorm   1: divide the selected gate values by their sum + eps
  *   alpha    routed scaling factor (multiplies every routed weight)
- *   eps      renormalisation epsilon (1e-20 in the GLM-4.5 note)          */
+ *   eps      renormalisation epsilon (1e-20 in the GLM-4.5 note)
+ *   weight_layout MOE_LAYOUT_ROWS (the row-major layouts below) or
+ *            MOE_LAYOUT_TILED (W1, W2, Wsh_gu, Wsh_dn as moe_tile_weights
+ *            writes them; bf16 only)                                     */
 typedef struct moe_desc {
     int64_t T, D, M, F, F_shared;
     int32_t k;
@@ -91,6 +98,7 @@ typedef struct moe_desc {
     int32_t renorm;
     float alpha;
     float eps;
+    int32_t weight_layout;
 } moe_desc;
 
 typedef struct moe_handle moe_handle;
@@ -103,6 +111,40 @@ int moe_destroy(moe_handle* h);
 /* Bytes of device workspace that moe_forward needs for `d`; the same size
  * also satisfies every stage call below.  Host-only computation. */
 int moe_workspace_size(const moe_desc* d, size_t* bytes);
+
+/* Tiled weight layout.  The expert and shared weights stream from HBM once
+ * per tile of rows, which makes weight reads the layer's dominant traffic
+ * when experts hold few rows (the GLaM-shaped and decode layers).  In the
+ * row-major layouts each 64-element K stage of a 256-row weight tile is 256
+ * separate 128-byte pieces; the tiled layout stores every such stage as one
+ * contiguous 32 KB block, exactly as the GEMM keeps it in LDS, so it streams
+ * at the full sequential rate.  A one-time copy, made when weights are
+ * loaded.  For a matrix with B rows of K elements (per expert for W1, W2):
+ *   W1 SWIGLU: B = 2F rows, output columns N = F; W1 GELU: B = N = F; K = D
+ *   W2: B = N = D, K = F;  Wsh_gu: B = 2 F_shared, N = F_shared, K = D;
+ *   Wsh_dn: B = N = D, K = F_shared
+ * the tiled copy is, per expert, n_tiles = ceil(N / C) tiles (C = 128 for
+ * the gate/up matrices of a SwiGLU, else 256) by n_k = ceil(K / 64) stages,
+ * block (tile n, stage s) at element offset (n * n_k + s) * 16384 of the
+ * expert's part, experts one after another.  A block holds 256 rows of 64
+ * elements: row b is weight row R(n, b) (SwiGLU: within each group of 64
+ * rows g = b / 64, rows b % 64 < 32 are gate rows n*128 + 32 g + b % 32 and
+ * the others the matching up rows F + n*128 + 32 g + (b % 32); otherwise
+ * n*256 + b), element c of the row (column s*64 + c of the weight) sits at
+ * b*64 + 8*((c/8) ^ (b % 8)) + c % 8; rows past the matrix and columns past
+ * K are zero. */
+
+/* Bytes of the tiled copy of weight matrix `which` (MOE_WEIGHT_*, all M
+ * experts for W1/W2) for `d` (bf16; F_shared > 0 for the shared ones).
+ * Host-only computation. */
+int moe_tiled_weight_size(const moe_desc* d, int which, size_t* bytes);
+
+/* Write the tiled copy of weight matrix `which` from its row-major form
+ * `src` (the layouts documented at moe_expert_ffn / moe_shared_expert) into
+ * `dst` (moe_tiled_weight_size bytes; must not overlap src).  d's
+ * weight_layout is ignored here.  Asynchronous on `stream`. */
+int moe_tile_weights(moe_handle* h, const moe_desc* d, int which, const void* src, void* dst,
+                     void* stream);
 
 /* Router: logits, scores, top-k selection and weights [GLaM "Sparse MoE
  * Layer" router and TopK equations; GLM-4.5 "How it works" sigmoid router,
@@ -140,7 +182,9 @@ int moe_permute(moe_handle* h, const moe_desc* d, const int32_t* idx, int32_t* c
  * W1[M,G*F,D] (SWIGLU: G = 2, gate rows 0..F-1 then up rows F..2F-1;
  * GELU: G = 1), b1[M,F] and b2[M,D] (GELU only, NULL = zero), W2[M,D,F],
  * w[T*k] fp32 indexed by flat slot, O[T*k,D] fp32 (rows >= offsets[M]
- * untouched).  The hidden activations (dtype) live in the workspace. */
+ * untouched).  The hidden activations (dtype) live in the workspace.
+ * With d->weight_layout == MOE_LAYOUT_TILED, W1 and W2 are the tiled
+ * copies (moe_tile_weights). */
 int moe_expert_ffn(moe_handle* h, const moe_desc* d, const void* x,
                    const int32_t* sorted_token, const int32_t* sorted_slot,
                    const int32_t* offsets, const float* w, const void* W1,
@@ -151,7 +195,8 @@ int moe_expert_ffn(moe_handle* h, const moe_desc* d, const void* x,
  * note, shared-expert equation; GLM-5 "All 5 steps"]:
  *   Ysh[t,:] = Wsh_dn (SiLU(Wsh_gate x_t) * (Wsh_up x_t))
  * Wsh_gu[2*F_shared, D] (gate rows then up rows), Wsh_dn[D, F_shared],
- * Ysh[T,D] fp32.  Requires F_shared > 0.  Uses workspace. */
+ * Ysh[T,D] fp32.  Requires F_shared > 0.  Uses workspace.  With
+ * d->weight_layout == MOE_LAYOUT_TILED both are the tiled copies. */
 int moe_shared_expert(moe_handle* h, const moe_desc* d, const void* x,
                       const void* Wsh_gu, const void* Wsh_dn, float* Ysh, void* ws,
                       size_t ws_bytes, void* stream);

@@ -21,19 +21,24 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0
 SCORER = {"softmax": 0, "sigmoid": 1}
 ACT = {"swiglu": 0, "gelu": 1}
 DTYPE = {"f32": 0, "bf16": 1}
+LAYOUT = {"rows": 0, "tiled": 1}
+WEIGHT = {"W1": 0, "W2": 1, "Wsh_gu": 2, "Wsh_dn": 3}
 _TORCH_OF = {0: torch.float32, 1: torch.bfloat16}
 
 EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_size", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_shared_expert", "moe_combine", "moe_forward",
            "moe_profile_start", "moe_profile_stop", "moe_profile_results",
-           "moe_status_string", "moe_last_error_detail")
+           "moe_status_string", "moe_last_error_detail", "moe_tiled_weight_size",
+           "moe_tile_weights")
 
 
 class moe_desc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("D", ctypes.c_int64), ("M", ctypes.c_int64),
                 ("F", ctypes.c_int64), ("F_shared", ctypes.c_int64), ("k", ctypes.c_int32),
                 ("scorer", ctypes.c_int32), ("act", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("renorm", ctypes.c_int32), ("alpha", ctypes.c_float), ("eps", ctypes.c_float)]
+                ("out_dtype", ctypes.c_int32), ("renorm", ctypes.c_int32),
+                ("alpha", ctypes.c_float), ("eps", ctypes.c_float),
+                ("weight_layout", ctypes.c_int32)]
 
 
 class moe_kernel_time(ctypes.Structure):
@@ -77,6 +82,8 @@ def load_library() -> ctypes.CDLL:
         "moe_profile_results": [vp, ctypes.POINTER(moe_kernel_time), i32,
                                 ctypes.POINTER(ctypes.c_int)],
         "moe_status_string": [i32],
+        "moe_tiled_weight_size": [dp, i32, ctypes.POINTER(sz)],
+        "moe_tile_weights": [vp, dp, i32, vp, vp, vp],
         "moe_last_error_detail": [],
     }
     for name, args in sig.items():
@@ -105,8 +112,8 @@ def _check(fn: str, rc: int):
 def make_desc(cfg=None, **kw) -> moe_desc:
     """Descriptor from a layer config object (T, D, M, F, F_shared, k,
     scorer, act, dtype, renorm, alpha, eps) with keyword overrides; enum
-    fields accept their names ("softmax", "swiglu", "bf16", ...).  out_dtype
-    defaults to dtype."""
+    fields accept their names ("softmax", "swiglu", "bf16", "tiled", ...).
+    out_dtype defaults to dtype, weight_layout to "rows"."""
     f = {}
     if cfg is not None:
         for n in ("T", "D", "M", "F", "F_shared", "k", "scorer", "act", "dtype", "renorm",
@@ -115,12 +122,13 @@ def make_desc(cfg=None, **kw) -> moe_desc:
     f.update(kw)
     sc, ac, dt = f["scorer"], f["act"], f["dtype"]
     od = f.get("out_dtype", dt)
+    wl = f.get("weight_layout", "rows")
     return moe_desc(T=int(f["T"]), D=int(f["D"]), M=int(f["M"]), F=int(f["F"]),
                     F_shared=int(f.get("F_shared", 0)), k=int(f["k"]),
                     scorer=SCORER.get(sc, sc), act=ACT.get(ac, ac), dtype=DTYPE.get(dt, dt),
                     out_dtype=DTYPE.get(od, od),
                     renorm=int(bool(f.get("renorm", 1))), alpha=float(f.get("alpha", 1.0)),
-                    eps=float(f.get("eps", 1e-20)))
+                    eps=float(f.get("eps", 1e-20)), weight_layout=LAYOUT.get(wl, wl))
 
 
 def _ptr(t, name, dtype=None, numel=None):
@@ -151,6 +159,13 @@ def _dt(d: moe_desc):
 
 def _odt(d: moe_desc):
     return _TORCH_OF[d.out_dtype]
+
+
+def _wnumel(d: moe_desc, which: str, rows_numel: int) -> int:
+    """Elements of weight matrix `which` in d's weight layout."""
+    if d.weight_layout == LAYOUT["tiled"]:
+        return moe_tiled_weight_size(d, which) // 2
+    return rows_numel
 
 
 # ---------------------------------------------------------------- entry points
@@ -202,8 +217,8 @@ def moe_expert_ffn(h, d, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b
         _ptr(sorted_token, "sorted_token", torch.int32, S),
         _ptr(sorted_slot, "sorted_slot", torch.int32, S),
         _ptr(offsets, "offsets", torch.int32, M + 1), _ptr(w, "w", torch.float32, S),
-        _ptr(W1, "W1", dt, M * G * F * D), _ptr(b1, "b1", dt, M * F),
-        _ptr(W2, "W2", dt, M * D * F), _ptr(b2, "b2", dt, M * D),
+        _ptr(W1, "W1", dt, _wnumel(d, "W1", M * G * F * D)), _ptr(b1, "b1", dt, M * F),
+        _ptr(W2, "W2", dt, _wnumel(d, "W2", M * D * F)), _ptr(b2, "b2", dt, M * D),
         _ptr(O, "O", torch.float32, S * D),
         _ptr(ws, "ws", torch.uint8), ws.numel() if ws is not None else 0, _stream(stream)))
 
@@ -212,8 +227,10 @@ def moe_shared_expert(h, d, x, Wsh_gu, Wsh_dn, Ysh, ws, stream=None):
     T, D, Fs = d.T, d.D, d.F_shared
     dt = _dt(d)
     _check("moe_shared_expert", load_library().moe_shared_expert(
-        h, ctypes.byref(d), _ptr(x, "x", dt, T * D), _ptr(Wsh_gu, "Wsh_gu", dt, 2 * Fs * D),
-        _ptr(Wsh_dn, "Wsh_dn", dt, D * Fs), _ptr(Ysh, "Ysh", torch.float32, T * D),
+        h, ctypes.byref(d), _ptr(x, "x", dt, T * D),
+        _ptr(Wsh_gu, "Wsh_gu", dt, _wnumel(d, "Wsh_gu", 2 * Fs * D)),
+        _ptr(Wsh_dn, "Wsh_dn", dt, _wnumel(d, "Wsh_dn", D * Fs)),
+        _ptr(Ysh, "Ysh", torch.float32, T * D),
         _ptr(ws, "ws", torch.uint8), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
@@ -233,9 +250,11 @@ def moe_forward(h, d, x, W_r, bias, W1, b1, W2, b2, Wsh_gu, Wsh_dn, y, ws, strea
     aux = None if aux_stream is None else _stream(aux_stream)
     _check("moe_forward", load_library().moe_forward(
         h, ctypes.byref(d), _ptr(x, "x", dt, T * D), _ptr(W_r, "W_r", torch.float32, M * D),
-        _ptr(bias, "bias", torch.float32, M), _ptr(W1, "W1", dt, M * G * F * D),
-        _ptr(b1, "b1", dt, M * F), _ptr(W2, "W2", dt, M * D * F), _ptr(b2, "b2", dt, M * D),
-        _ptr(Wsh_gu, "Wsh_gu", dt, 2 * Fs * D), _ptr(Wsh_dn, "Wsh_dn", dt, D * Fs),
+        _ptr(bias, "bias", torch.float32, M), _ptr(W1, "W1", dt, _wnumel(d, "W1", M * G * F * D)),
+        _ptr(b1, "b1", dt, M * F), _ptr(W2, "W2", dt, _wnumel(d, "W2", M * D * F)),
+        _ptr(b2, "b2", dt, M * D),
+        _ptr(Wsh_gu, "Wsh_gu", dt, _wnumel(d, "Wsh_gu", 2 * Fs * D) if Fs else None),
+        _ptr(Wsh_dn, "Wsh_dn", dt, _wnumel(d, "Wsh_dn", D * Fs) if Fs else None),
         _ptr(y, "y", _odt(d), T * D), _ptr(ws, "ws", torch.uint8),
         ws.numel() if ws is not None else 0, _stream(stream), aux))
 
@@ -255,3 +274,30 @@ def moe_profile_results(h) -> dict:
     n = ctypes.c_int()
     _check("moe_profile_results", load_library().moe_profile_results(h, arr, 16, ctypes.byref(n)))
     return {arr[i].label.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
+
+
+def moe_tiled_weight_size(d, which) -> int:
+    """Bytes of the tiled copy of weight matrix `which` ("W1", "W2", "Wsh_gu",
+    "Wsh_dn" or its MOE_WEIGHT_* number)."""
+    n = ctypes.c_size_t()
+    _check("moe_tiled_weight_size", load_library().moe_tiled_weight_size(
+        ctypes.byref(d), int(WEIGHT.get(which, which)), ctypes.byref(n)))
+    return n.value
+
+
+def moe_tile_weights(h, d, which, src, dst, stream=None):
+    """Write the tiled copy of row-major weight matrix `src` into `dst`."""
+    wh = int(WEIGHT.get(which, which))
+    rows = {0: d.M * (2 if d.act == 0 else 1) * d.F * d.D, 1: d.M * d.D * d.F,
+            2: 2 * d.F_shared * d.D, 3: d.D * d.F_shared}[wh]
+    _check("moe_tile_weights", load_library().moe_tile_weights(
+        h, ctypes.byref(d), wh, _ptr(src, "src", torch.bfloat16, rows),
+        _ptr(dst, "dst", torch.bfloat16, moe_tiled_weight_size(d, wh) // 2), _stream(stream)))
+
+
+def tile_weights(h, d, which, src, stream=None):
+    """A new bf16 tensor holding the tiled copy of `src`."""
+    dst = torch.empty(moe_tiled_weight_size(d, which) // 2, dtype=torch.bfloat16,
+                      device=src.device)
+    moe_tile_weights(h, d, which, src, dst, stream)
+    return dst

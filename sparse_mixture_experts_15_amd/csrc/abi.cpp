@@ -100,6 +100,10 @@ int validate(const moe_desc* d) {
     if (d->out_dtype != MOE_DTYPE_F32 && d->out_dtype != MOE_DTYPE_BF16)
         return fail(MOE_ERR_INVALID, "unknown out_dtype %d", d->out_dtype);
     if (d->renorm != 0 && d->renorm != 1) return fail(MOE_ERR_INVALID, "renorm must be 0 or 1");
+    if (d->weight_layout != MOE_LAYOUT_ROWS && d->weight_layout != MOE_LAYOUT_TILED)
+        return fail(MOE_ERR_INVALID, "unknown weight_layout %d", d->weight_layout);
+    if (d->weight_layout == MOE_LAYOUT_TILED && d->dtype != MOE_DTYPE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "the tiled weight layout is bf16 only");
     if (!(d->eps >= 0.f) || d->alpha != d->alpha)
         return fail(MOE_ERR_INVALID, "eps must be >= 0 and alpha a number");
     if (d->k > MOE_MAX_K) return fail(MOE_ERR_UNSUPPORTED, "k=%d > %d", d->k, MOE_MAX_K);
@@ -119,6 +123,30 @@ int validate(const moe_desc* d) {
         (d->T * d->D * 2 > lim || S * d->F * 2 > lim || G * d->F * d->D * 2 > lim ||
          d->T * d->F_shared * 2 > lim || 2 * d->F_shared * d->D * 2 > lim))
         return fail(MOE_ERR_UNSUPPORTED, "an operand exceeds 2 GiB");
+    if (d->weight_layout == MOE_LAYOUT_TILED &&
+        (tiled_elems(d->F, d->D, d->act == MOE_ACT_SWIGLU) * 2 > lim ||
+         tiled_elems(d->D, d->F, false) * 2 > lim ||
+         tiled_elems(d->F_shared, d->D, true) * 2 > lim ||
+         tiled_elems(d->D, d->F_shared, false) * 2 > lim))
+        return fail(MOE_ERR_UNSUPPORTED, "a tiled weight matrix exceeds 2 GiB");
+    return MOE_OK;
+}
+
+// Shape of weight matrix `which`: experts, rows, output columns, K, SwiGLU.
+struct WeightShape {
+    int64_t E, rows, n_out, K;
+    bool swiglu;
+};
+int weight_shape(const moe_desc* d, int which, WeightShape& ws) {
+    const bool sw = d->act == MOE_ACT_SWIGLU;
+    switch (which) {
+        case MOE_WEIGHT_W1: ws = {d->M, (sw ? 2 : 1) * d->F, d->F, d->D, sw}; return MOE_OK;
+        case MOE_WEIGHT_W2: ws = {d->M, d->D, d->D, d->F, false}; return MOE_OK;
+        case MOE_WEIGHT_SH_GU: ws = {1, 2 * d->F_shared, d->F_shared, d->D, true}; break;
+        case MOE_WEIGHT_SH_DN: ws = {1, d->D, d->D, d->F_shared, false}; break;
+        default: return fail(MOE_ERR_INVALID, "unknown weight matrix %d", which);
+    }
+    if (d->F_shared <= 0) return fail(MOE_ERR_INVALID, "no shared expert (F_shared = 0)");
     return MOE_OK;
 }
 
@@ -235,8 +263,10 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     GemmArgs up{};
     up.a = x;
     up.gather = sorted_token;
+    const bool tiled = d->weight_layout == MOE_LAYOUT_TILED;
     up.b = W1;
-    up.b_stride = (swiglu ? 2 : 1) * d->F * d->D;
+    up.b_stride = tiled ? tiled_elems(d->F, d->D, swiglu) : (swiglu ? 2 : 1) * d->F * d->D;
+    up.b_tiled = tiled;
     up.bias = swiglu ? nullptr : b1;
     up.c = H;
     up.tiles = tiles_up;
@@ -255,7 +285,8 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     GemmArgs dn{};
     dn.a = H;
     dn.b = W2;
-    dn.b_stride = d->D * d->F;
+    dn.b_stride = tiled ? tiled_elems(d->D, d->F, false) : d->D * d->F;
+    dn.b_tiled = tiled;
     dn.bias = swiglu ? nullptr : b2;
     dn.row_w = row_scale;
     dn.dense_rows = p.S;
@@ -278,7 +309,10 @@ int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, co
     const int64_t mt_dn = (d->T + p.bm_sh_dn - 1) / p.bm_sh_dn;
     GemmArgs up{};
     up.a = x;
+    const bool tiled = d->weight_layout == MOE_LAYOUT_TILED;
     up.b = Wgu;
+    up.b_stride = tiled ? tiled_elems(d->F_shared, d->D, true) : 0;
+    up.b_tiled = tiled;
     up.c = Hsh;
     up.dense_rows = d->T;
     up.a_rows = d->T;
@@ -291,6 +325,8 @@ int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, co
     GemmArgs dn{};
     dn.a = Hsh;
     dn.b = Wdn;
+    dn.b_stride = tiled ? tiled_elems(d->D, d->F_shared, false) : 0;
+    dn.b_tiled = tiled;
     dn.c = Ysh;
     dn.dense_rows = d->T;
     dn.a_rows = d->T;
@@ -450,6 +486,40 @@ int moe_shared_expert(moe_handle* h, const moe_desc* d, const void* x, const voi
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
     return do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, static_cast<hipStream_t>(stream));
+}
+
+int moe_tiled_weight_size(const moe_desc* d, int which, size_t* bytes) {
+    if (!bytes) return fail(MOE_ERR_INVALID, "bytes is NULL");
+    TRY(validate(d));
+    if (d->dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_UNSUPPORTED, "tiled weights are bf16 only");
+    WeightShape w;
+    TRY(weight_shape(d, which, w));
+    const int64_t per = tiled_elems(w.n_out, w.K, w.swiglu);
+    if (per * 2 > 0x7fffffffLL)
+        return fail(MOE_ERR_UNSUPPORTED, "a tiled weight matrix exceeds 2 GiB");
+    *bytes = (size_t)(w.E * per * 2);
+    return MOE_OK;
+}
+
+int moe_tile_weights(moe_handle* h, const moe_desc* d, int which, const void* src, void* dst,
+                     void* stream) {
+    CHECK_HANDLE(h);
+    size_t bytes = 0;
+    TRY(moe_tiled_weight_size(d, which, &bytes));
+    NEED(src, "src");
+    NEED(dst, "dst");
+    WeightShape w;
+    TRY(weight_shape(d, which, w));
+    const char* s0 = static_cast<const char*>(src);
+    const char* d0 = static_cast<const char*>(dst);
+    const size_t src_bytes = (size_t)(w.E * w.rows * w.K * 2);
+    if (d0 < s0 + src_bytes && s0 < d0 + bytes) return fail(MOE_ERR_INVALID, "src and dst overlap");
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+    const hipError_t e = launch_tile_weights(static_cast<hipStream_t>(stream), src, dst, w.E,
+                                             w.rows, w.n_out, w.K, w.swiglu);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "tile_weights launch: %s", hipGetErrorString(e));
+    return MOE_OK;
 }
 
 int moe_combine(moe_handle* h, const moe_desc* d, const float* O, const int32_t* slot_row,

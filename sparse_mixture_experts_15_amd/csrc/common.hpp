@@ -87,7 +87,22 @@ struct GemmArgs {
     int k_split;              // dense DOWN_F32 only: K chunks, each writing its own
                               // [rows, N] partial at c + chunk * rows * N (0 = 1)
     int group_m;              // m-tiles per group of the tile order (0 = 4)
+    int b_tiled;              // b holds tiled blocks (bf16): b_stride = one expert's blocks
 };
+
+// Weight tiles of the bf16 GEMM: 256 weight rows by K stages of 64.
+constexpr int kTileRows = 256;
+constexpr int kTileK = 64;
+// Elements of one expert's tiled copy of a weight matrix with n_out output
+// columns (SwiGLU: 128 per tile) and reduction length K.
+inline int64_t tiled_elems(int64_t n_out, int64_t K, bool swiglu) {
+    const int64_t per = swiglu ? kTileRows / 2 : kTileRows;
+    return ((n_out + per - 1) / per) * ((K + kTileK - 1) / kTileK) * (int64_t)kTileRows * kTileK;
+}
+// Writes the tiled copy of E weight matrices (each b_rows x K row-major,
+// n_out output columns; SwiGLU: gate rows then up rows at f_split).
+hipError_t launch_tile_weights(hipStream_t s, const void* src, void* dst, int64_t E,
+                               int64_t b_rows, int64_t n_out, int64_t K, bool swiglu);
 
 // m-tiles per group of the tile order for a grouped GEMM: about the m-tiles
 // one expert spans, so that the workgroups one XCD runs together share that

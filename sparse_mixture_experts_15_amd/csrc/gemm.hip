@@ -220,7 +220,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     const int64_t a_rows = g.gather ? g.a_rows : tl.rend;
     const i32x4 ra = make_rsrc(g.a, (uint32_t)(a_rows * K * 2));
     const bf16_t* Bp = static_cast<const bf16_t*>(g.b) + (int64_t)tl.e * g.b_stride;
-    const i32x4 rb = make_rsrc(Bp, (uint32_t)((int64_t)g.b_rows * K * 2));
+    const i32x4 rb = make_rsrc(Bp, (uint32_t)((g.b_tiled ? g.b_stride : (int64_t)g.b_rows * K) * 2));
+    // tiled weights: stage kt of this n-tile is one contiguous block
+    const uint32_t tile_base = (uint32_t)nt * (uint32_t)((K + BK - 1) / BK) * (BNB * BK * 2);
 
     // Load q of wave w (ins = w + 8 q) fills ROWS_PER_LOAD rows: B rows of
     // block ins for q < QB, else A rows of block ins - B_LOADS; lane l -> row
@@ -255,6 +257,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             // an invalid row stays >= kOOB (offsets are < 2^31); a K-tail chunk -> kOOB
             uint32_t off = rowoff[q] + (uint32_t)kc * 2u;
             off = kc < K ? off : kOOB;
+            if (q < QB && g.b_tiled)
+                off = tile_base + (uint32_t)kt * (BNB * BK * 2) + (uint32_t)ins * 1024u + lane * 16u;
             if (q < QB)
                 llvm_amdgcn_raw_buffer_load_lds(rb, (lds_u32_ptr)(st + BM * BK + ins * 512), 16,
                                                 (int)off, 0, 0, 0);
@@ -508,6 +512,7 @@ hipError_t launch_bf16(hipStream_t s, const GemmArgs& g, int64_t m_tiles) {
     const int opt = (EPI == EPI_SWIGLU) ? BNv / 2 : BNv;
     const int n_tiles = (g.N + opt - 1) / opt;
     if (g.k_split > (g.K + BK - 1) / BK) return hipErrorInvalidValue;   // each K chunk needs a stage
+    if (g.b_tiled && (KS != kTileK || BNv != kTileRows)) return hipErrorInvalidValue;
     const int64_t total = m_tiles * n_tiles * (g.k_split > 1 ? g.k_split : 1);
     hipLaunchKernelGGL((gemm_bf16<EPI, BMv, BNv, STv, KS>), dim3((unsigned)total), dim3(NT), 0, s, g,
                        (int)m_tiles, n_tiles);

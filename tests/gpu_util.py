@@ -184,3 +184,13 @@ def forward(L, t, aux=None, y=None):
 
 def new_layer(cfg, **kw):
     return MoELayer(B.make_desc(cfg, **kw))
+
+
+def tiled_weights(L, t):
+    """Copy of the input dict with W1, W2 and the shared weights replaced by
+    their tiled copies (moe_tile_weights); everything else shared."""
+    t = dict(t)
+    for name in ("W1", "W2", "Wsh_gu", "Wsh_dn"):
+        if t.get(name) is not None:
+            t[name] = B.tile_weights(L.handle, L.desc, name, t[name])
+    return t

@@ -35,9 +35,10 @@ def test_descriptor_layout_matches_header(tmp_path):
     prog = tmp_path / "layout.c"
     prog.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
-        'int main(void){printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(moe_desc),'
+        'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_desc),'
         ' offsetof(moe_desc,k), offsetof(moe_desc,renorm), offsetof(moe_desc,alpha),'
-        ' offsetof(moe_desc,eps), sizeof(moe_kernel_time)); return 0;}\n')
+        ' offsetof(moe_desc,eps), offsetof(moe_desc,weight_layout),'
+        ' sizeof(moe_kernel_time)); return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)],
                    check=True)
@@ -45,7 +46,7 @@ def test_descriptor_layout_matches_header(tmp_path):
                                        check=True).stdout.split()))
     d = B.moe_desc
     assert got == [ctypes.sizeof(d), d.k.offset, d.renorm.offset, d.alpha.offset,
-                   d.eps.offset, ctypes.sizeof(B.moe_kernel_time)]
+                   d.eps.offset, d.weight_layout.offset, ctypes.sizeof(B.moe_kernel_time)]
 
 
 def _ws(desc):
@@ -70,7 +71,7 @@ def test_workspace_size_covers_intermediates():
     ("dtype", 3, B.MOE_ERR_INVALID), ("renorm", 2, B.MOE_ERR_INVALID),
     ("D", 0, B.MOE_ERR_INVALID), ("F_shared", -8, B.MOE_ERR_INVALID),
     ("D", 12, B.MOE_ERR_UNSUPPORTED), ("F", 20, B.MOE_ERR_UNSUPPORTED),
-    ("F_shared", 4, B.MOE_ERR_UNSUPPORTED),
+    ("F_shared", 4, B.MOE_ERR_UNSUPPORTED), ("weight_layout", 2, B.MOE_ERR_INVALID),
 ])
 def test_bad_descriptor_rejected(field, value, status):
     cfg = workloads.shrink(workloads.GLAM_4K, T=16, D=64, F=32).replace(M=8)
@@ -117,3 +118,47 @@ def test_status_strings():
     assert [B.status_string(i) for i in range(5)] == [
         "MOE_OK", "MOE_ERR_INVALID", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP"]
     assert B.status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+def _tiled_bytes(n_out, K, swiglu, E):
+    """Closed form of the header's tiled layout size: ceil(N / C) tiles (C =
+    128 for a SwiGLU gate/up matrix, else 256) x ceil(K / 64) blocks of
+    256 x 64 bf16, per expert."""
+    per = 128 if swiglu else 256
+    return E * (-(-n_out // per)) * (-(-K // 64)) * 256 * 64 * 2
+
+
+@pytest.mark.parametrize("cfg", [
+    workloads.GLM45_PREFILL, workloads.GLAM_4K,
+    workloads.shrink(workloads.GLM45_PREFILL, T=8, D=200, F=200, F_shared=136),
+    workloads.shrink(workloads.GLAM_4K, T=8, D=136, F=264),
+])
+def test_tiled_weight_sizes(cfg):
+    d = B.make_desc(cfg)
+    sw = cfg.act == "swiglu"
+    assert B.moe_tiled_weight_size(d, "W1") == _tiled_bytes(cfg.F, cfg.D, sw, cfg.M)
+    assert B.moe_tiled_weight_size(d, "W2") == _tiled_bytes(cfg.D, cfg.F, False, cfg.M)
+    if cfg.F_shared:
+        assert B.moe_tiled_weight_size(d, "Wsh_gu") == _tiled_bytes(cfg.F_shared, cfg.D, True, 1)
+        assert B.moe_tiled_weight_size(d, "Wsh_dn") == _tiled_bytes(cfg.D, cfg.F_shared, False, 1)
+    if cfg.D % 256 == 0 and cfg.F % 256 == 0:   # no padding: the row-major size
+        assert B.moe_tiled_weight_size(d, "W1") == cfg.M * (2 if sw else 1) * cfg.F * cfg.D * 2
+    # the tiled layout is accepted for the whole layer's workspace query
+    assert B.moe_workspace_size(B.make_desc(cfg, weight_layout="tiled")) > 0
+
+
+def test_tiled_weight_errors():
+    lib = B.load_library()
+    n = ctypes.c_size_t(7)
+    d = B.make_desc(workloads.GLAM_4K)           # no shared expert
+    assert lib.moe_tiled_weight_size(ctypes.byref(d), 2, ctypes.byref(n)) == B.MOE_ERR_INVALID
+    assert lib.moe_tiled_weight_size(ctypes.byref(d), 9, ctypes.byref(n)) == B.MOE_ERR_INVALID
+    assert n.value == 7
+    d = B.make_desc(workloads.GLAM_TINY_FP32)    # fp32: no tiled layout
+    assert lib.moe_tiled_weight_size(ctypes.byref(d), 0, ctypes.byref(n)) == B.MOE_ERR_UNSUPPORTED
+    d = B.make_desc(workloads.GLAM_TINY_FP32, weight_layout="tiled")
+    assert lib.moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.MOE_ERR_UNSUPPORTED
+    d = B.make_desc(workloads.GLAM_4K)
+    vp = ctypes.c_void_p
+    assert lib.moe_tile_weights(None, ctypes.byref(d), 0, vp(16), vp(16), None) \
+        == B.MOE_ERR_INVALID

@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads
 from tests.gpu_util import (check_float, check_dispatch_props, check_route, forward,
-                            gpu_permute, new_layer, run_route, to_np)
+                            gpu_permute, new_layer, run_route, tiled_weights, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,17 +33,20 @@ def _sample_tokens(cfg, disp, n_random=24, n_expert=24, seed=0):
     return np.array(sorted(toks), dtype=np.int64)
 
 
-@pytest.mark.parametrize("name,out_dtype", [
-    ("tiny", None), ("decode", None), ("decode", "f32"), ("glm45", None), ("glm45", "f32"),
-    ("glam", None), ("glm5", None)])
-def test_full_size_forward(name, out_dtype):
+@pytest.mark.parametrize("name,out_dtype,layout", [
+    ("tiny", None, "rows"), ("decode", None, "rows"), ("decode", "f32", "rows"),
+    ("glm45", None, "rows"), ("glm45", "f32", "rows"), ("glam", None, "rows"),
+    ("glm5", None, "rows"), ("glam", None, "tiled"), ("decode", None, "tiled")])
+def test_full_size_forward(name, out_dtype, layout):
     cfg = workloads.get(name)
     out_dtype = out_dtype or cfg.dtype
-    print(f"full-size parity: {cfg.name} (y in {out_dtype})", flush=True)
+    print(f"full-size parity: {cfg.name} (y in {out_dtype}, {layout} weights)", flush=True)
     t = workloads.generate(cfg, seed=0, device="cuda")
-    L = new_layer(cfg, out_dtype=out_dtype)
+    L = new_layer(cfg, out_dtype=out_dtype, weight_layout=layout)
     aux = torch.cuda.Stream()
-    y = forward(L, t, aux=aux)
+    tw = tiled_weights(L, t) if layout == "tiled" else t
+    y = forward(L, tw, aux=aux)
+    del tw
     idx_g, w_g = run_route(L, L.desc, t)
     pg = gpu_permute(L, L.desc, idx_g)
     torch.cuda.synchronize()
