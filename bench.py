@@ -39,15 +39,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# HBM traffic per launch of a workload's dominant kernel: rocprofv3 FETCH_SIZE
-# and WRITE_SIZE passes over `bench.py --steps 3 --warmup 1 --no-cpu-baseline`,
+# HBM traffic per launch of a workload's dominant kernel (tiled weights):
+# rocprofv3 FETCH_SIZE and WRITE_SIZE passes over `bench.py --steps 3
+# --warmup 1 --no-cpu-baseline`,
 # each scaled by what the same counter reads for a plain 1 GiB copy (`bench.py
 # --calib-copy`); see the traffic summaries under profiles/.  An entry holds
 # only for the GEMM source it was measured on (hash of gemm.hip and
 # common.hpp); any change to them reports null until it is measured again.
 TRAFFIC = {
-    ("glam_t4096_d4096_m64_f16384", "ffn_up"): (9013800715, "0ed160efb8118e8f"),
-    ("glam_t4096_d4096_m64_f16384", "ffn_down"): (9076855848, "0ed160efb8118e8f"),
+    ("glam_t4096_d4096_m64_f16384", "ffn_up"): (9043530453, "d976610fefb6e3a0"),
+    ("glam_t4096_d4096_m64_f16384", "ffn_down"): (9070372575, "d976610fefb6e3a0"),
 }
 
 
