@@ -52,7 +52,8 @@ class _Cfg(ctypes.Structure):
                 ("k", ctypes.c_int32), ("scorer", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("alpha", ctypes.c_double),
-                ("eps", ctypes.c_double)]
+                ("eps", ctypes.c_double), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32)]
 
 
 _lib = None
@@ -86,12 +87,15 @@ def num_threads() -> int:
 
 def make_cfg(cfg) -> _Cfg:
     """Oracle descriptor from any object with the layer fields (T, D, M, F,
-    F_shared, k, scorer, act, dtype, renorm, alpha, eps)."""
+    F_shared, k, scorer, act, dtype, renorm, alpha, eps; n_group and
+    topk_group when present)."""
     return _Cfg(T=cfg.T, D=cfg.D, M=cfg.M, F=cfg.F, F_shared=cfg.F_shared, k=cfg.k,
                 scorer=SOFTMAX if cfg.scorer == "softmax" else SIGMOID,
                 act=SWIGLU if cfg.act == "swiglu" else GELU,
                 dtype=F32 if cfg.dtype == "f32" else BF16,
-                renorm=1 if cfg.renorm else 0, alpha=float(cfg.alpha), eps=float(cfg.eps))
+                renorm=1 if cfg.renorm else 0, alpha=float(cfg.alpha), eps=float(cfg.eps),
+                n_group=int(getattr(cfg, "n_group", 0)),
+                topk_group=int(getattr(cfg, "topk_group", 0)))
 
 
 def _ptr(a):

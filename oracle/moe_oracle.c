@@ -123,6 +123,43 @@ static void route_token(const moe_oracle_cfg* c, const void* x, const float* W_r
         for (int64_t e = 0; e < M; ++e)
             sel_out[e] = sel[e];
 
+    /* Expert groups [GLM45 "How it works": the router "optionally masks by
+     * expert group" before the top-k].  Experts form n_group contiguous
+     * groups; a group's score is the largest selection score among its
+     * experts; the topk_group best groups are kept (lower group index on an
+     * exact tie) and the other groups' experts leave the selection.  Marking
+     * them `taken` removes them from the top-k below. */
+    double group_gap = INFINITY;
+    if (c->n_group > 1) {
+        const int32_t ng = c->n_group, gs = (int32_t)(M / ng);
+        double* gscore = malloc(sizeof(double) * ng);
+        char* kept = calloc((size_t)ng, 1);
+        for (int32_t gi = 0; gi < ng; ++gi) {
+            gscore[gi] = sel[(int64_t)gi * gs];
+            for (int32_t u = 1; u < gs; ++u)
+                if (sel[(int64_t)gi * gs + u] > gscore[gi])
+                    gscore[gi] = sel[(int64_t)gi * gs + u];
+        }
+        double last_kept = INFINITY;
+        for (int32_t r = 0; r < c->topk_group; ++r) {
+            int32_t best = -1;
+            for (int32_t gi = 0; gi < ng; ++gi)
+                if (!kept[gi] && (best < 0 || gscore[gi] > gscore[best]))
+                    best = gi;
+            kept[best] = 1;
+            last_kept = gscore[best];
+        }
+        for (int32_t gi = 0; gi < ng; ++gi)
+            if (!kept[gi]) {
+                if (last_kept - gscore[gi] < group_gap)
+                    group_gap = last_kept - gscore[gi];
+                for (int32_t u = 0; u < gs; ++u)
+                    taken[(int64_t)gi * gs + u] = 1;
+            }
+        free(gscore);
+        free(kept);
+    }
+
     /* TopK: k times, take the not-yet-taken expert with the largest
      * selection score; scanning upward with a strict comparison keeps the
      * lower index on an exact tie. */
@@ -134,7 +171,8 @@ static void route_token(const moe_oracle_cfg* c, const void* x, const float* W_r
         taken[best] = 1;
         chosen[j] = (int32_t)best;
     }
-    /* boundary gap: k-th largest minus (k+1)-th largest selection score */
+    /* boundary gap: k-th largest minus (k+1)-th largest selection score
+     * among the candidates (and the group boundary's gap) */
     double next = -INFINITY;
     int have_next = 0;
     for (int64_t e = 0; e < M; ++e)
@@ -143,6 +181,8 @@ static void route_token(const moe_oracle_cfg* c, const void* x, const float* W_r
             have_next = 1;
         }
     *gap_out = have_next ? sel[chosen[k - 1]] - next : INFINITY;
+    if (group_gap < *gap_out)
+        *gap_out = group_gap;
 
     /* slots in ascending expert order (insertion sort of k values) */
     for (int32_t a = 1; a < k; ++a) {

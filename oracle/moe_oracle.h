@@ -32,12 +32,16 @@ typedef struct {
     int32_t renorm;  /* 1: renormalise the selected gate values */
     double alpha;    /* routed scaling factor */
     double eps;      /* renormalisation epsilon */
+    int32_t n_group;     /* expert groups (<= 1: none) */
+    int32_t topk_group;  /* groups kept per token */
 } moe_oracle_cfg;
 
 /* Router for tokens tokens[0..ntok): logits, scores, top-k, weights.
  * Outputs are indexed by position in the token list:
  *   idx[i*k+j] expert of slot j (ascending expert order), w[i*k+j] weight,
- *   gap[i] = (k-th largest selection score) - ((k+1)-th largest), +inf if k == M,
+ *   gap[i] = (k-th largest selection score) - ((k+1)-th largest), +inf if k == M;
+ *   with expert groups, the smaller of that (among the kept groups' experts)
+ *   and the topk_group-th minus the (topk_group+1)-th group score,
  *   logits[i*M+e] and the selection scores sel[i*M+e] (both nullable).
  *   bias is nullable (zero bias). */
 void oracle_route(const moe_oracle_cfg* c, const void* x, const float* W_r,

@@ -114,6 +114,67 @@ def test_topk_bruteforce(scorer, M, k):
             assert math.isinf(gap[t])
 
 
+def _sel_np(h, cfg):
+    lg = _logits_np(h, cfg)
+    if cfg.scorer == "softmax":
+        return lg
+    return special.expit(lg) + (h["bias"].astype(np.float64) if h["bias"] is not None else 0.0)
+
+
+@pytest.mark.parametrize("scorer,M,ng,tg,k", [("sigmoid", 12, 4, 2, 3), ("sigmoid", 12, 3, 1, 4),
+                                               ("softmax", 10, 5, 3, 2), ("sigmoid", 8, 4, 4, 3)])
+def test_group_limited_topk_bruteforce(scorer, M, ng, tg, k):
+    """Groups of M/ng consecutive experts, a group's score the largest
+    selection score in it, the tg best groups kept (numpy stable argsort),
+    then the brute-force top-k among the kept groups' experts."""
+    base = workloads.GLAM_4K if scorer == "softmax" else workloads.GLM45_PREFILL
+    cfg = base.replace(T=20, D=24, M=M, F=8, k=k, F_shared=0, n_group=ng, topk_group=tg)
+    h = _host(cfg, seed=5)
+    idx, _, gap = oracle.route(cfg, h["x"], h["W_r"], h["bias"])
+    sel = _sel_np(h, cfg)
+    gs = M // ng
+    for t in range(cfg.T):
+        gmax = sel[t].reshape(ng, gs).max(axis=1)
+        kept = np.argsort(-gmax, kind="stable")[:tg]
+        cand = [e for e in range(M) if e // gs in set(kept.tolist())]
+        sub = _brute_topk([sel[t][e] for e in cand], k)
+        assert tuple(idx[t]) == tuple(sorted(cand[i] for i in sub))
+        assert all(e // gs in set(kept.tolist()) for e in idx[t])
+        # the gap covers the group boundary too
+        if tg < ng:
+            srt = np.sort(gmax)[::-1]
+            assert gap[t] <= srt[tg - 1] - srt[tg] + 1e-12
+
+
+@pytest.mark.parametrize("ng,tg", [(1, 1), (0, 0), (4, 4)])
+def test_grouping_that_keeps_every_group_changes_nothing(ng, tg):
+    cfg = _small(workloads.GLM45_PREFILL).replace(M=16, n_group=ng, topk_group=tg)
+    h = _host(cfg, seed=6)
+    idx_g, w_g, _ = oracle.route(cfg, h["x"], h["W_r"], h["bias"])
+    idx_0, w_0, _ = oracle.route(cfg.replace(n_group=0, topk_group=0), h["x"], h["W_r"], h["bias"])
+    assert (idx_g == idx_0).all() and (w_g == w_0).all()
+
+
+def test_group_limited_planted_example():
+    """Group 0 holds the best single expert; groups 1 and 2 hold the next
+    best ones.  One kept group and k = 2 must take expert 0 and the best
+    other expert of group 0, not the overall second best."""
+    cfg = workloads.GLM45_PREFILL.replace(T=1, D=6, M=6, F=8, k=2, F_shared=0, n_group=3,
+                                          topk_group=1, renorm=True, alpha=1.0)
+    x = np.zeros((1, 6), np.uint16)
+    x[0, 0] = 0x3F80                               # bf16 1.0
+    W_r = np.zeros((6, 6), np.float32)
+    W_r[:, 0] = [3.0, -2.0, 2.5, 2.4, 2.3, 2.2]   # logits = first column
+    bias = np.zeros(6, np.float32)
+    idx, w, _ = oracle.route(cfg, x, W_r, bias)
+    assert tuple(idx[0]) == (0, 1)
+    # ungrouped, the two best experts are 0 and 2
+    idx2, _, _ = oracle.route(cfg.replace(n_group=0, topk_group=0), x, W_r, bias)
+    assert tuple(idx2[0]) == (0, 2)
+    s = special.expit([3.0, -2.0])
+    assert np.allclose(w[0], s / s.sum(), rtol=1e-15)
+
+
 @pytest.mark.parametrize("cfg", SMALL_CFGS, ids=SMALL_IDS)
 def test_exactly_k_distinct_ascending(cfg):
     h = _host(cfg)

@@ -42,6 +42,8 @@ class MoEConfig:
     ffn_bias_std: float = 0.0     # b1/b2 of GELU experts (0 = no biases)
     zipf_gamma: float = 0.0       # router row scale (pi(e)+1)^-gamma, 0 = off
     x_std: float = 1.0
+    n_group: int = 0              # expert groups for group-limited routing (0 = none)
+    topk_group: int = 0           # groups kept per token
 
     @property
     def G(self) -> int:
@@ -88,12 +90,18 @@ GLM5_ZIPF = MoEConfig(
 # Decode-shaped GLM-4.5 layer: 64 tokens (batch 64 x 1 position).
 GLM45_DECODE = GLM45_PREFILL.replace(name="glm45_decode_t64_d5120_m160_f1536", T=64)
 
-CONFIGS = [GLAM_TINY_FP32, GLAM_4K, GLM45_PREFILL, GLM5_ZIPF, GLM45_DECODE]
+# The GLM-4.5 prefill layer with group-limited routing (the router's optional
+# masking by expert group): 8 groups of 20 experts, the best 4 kept.  The
+# page gives no group counts; these exercise the variant at full size.
+GLM45_GROUPED = GLM45_PREFILL.replace(name="glm45_grouped_t8192_d5120_m160_f1536_g8k4",
+                                      n_group=8, topk_group=4)
+
+CONFIGS = [GLAM_TINY_FP32, GLAM_4K, GLM45_PREFILL, GLM5_ZIPF, GLM45_DECODE, GLM45_GROUPED]
 BY_NAME = {c.name: c for c in CONFIGS}
 # Short aliases used by the harness command line.
 ALIASES = {
     "tiny": GLAM_TINY_FP32, "glam": GLAM_4K, "glm45": GLM45_PREFILL,
-    "glm5": GLM5_ZIPF, "decode": GLM45_DECODE,
+    "glm5": GLM5_ZIPF, "decode": GLM45_DECODE, "glm45g": GLM45_GROUPED,
 }
 
 
