@@ -72,6 +72,7 @@ enum { MOE_WEIGHT_W1 = 0, MOE_WEIGHT_W2 = 1, MOE_WEIGHT_SH_GU = 2, MOE_WEIGHT_SH
 
 #define MOE_MAX_K 16
 #define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_GROUPS 64
 
 /* Layer descriptor (plain data).
  *   T        tokens (the flattened batch x positions, as the GLM-4.5 note's
@@ -87,7 +88,15 @@ enum { MOE_WEIGHT_W1 = 0, MOE_WEIGHT_W2 = 1, MOE_WEIGHT_SH_GU = 2, MOE_WEIGHT_SH
  *   eps      renormalisation epsilon (1e-20 in the GLM-4.5 note)
  *   weight_layout MOE_LAYOUT_ROWS (the row-major layouts below) or
  *            MOE_LAYOUT_TILED (W1, W2, Wsh_gu, Wsh_dn as moe_tile_weights
- *            writes them; bf16 only)                                     */
+ *            writes them; bf16 only)
+ *   n_group, topk_group  group-limited routing (the GLM-4.5 note's router
+ *            "optionally masks by expert group"): with n_group > 1 the M
+ *            experts form n_group groups of M/n_group consecutive experts,
+ *            a group's score is the largest selection score among its
+ *            experts, only the topk_group best groups (lower group index on
+ *            an exact tie) stay candidates for the top-k.  Requires
+ *            n_group | M, n_group <= 64 and k <= topk_group * M / n_group.
+ *            n_group <= 1: no grouping.                                  */
 typedef struct moe_desc {
     int64_t T, D, M, F, F_shared;
     int32_t k;
@@ -99,6 +108,8 @@ typedef struct moe_desc {
     float alpha;
     float eps;
     int32_t weight_layout;
+    int32_t n_group;
+    int32_t topk_group;
 } moe_desc;
 
 typedef struct moe_handle moe_handle;
@@ -152,7 +163,8 @@ int moe_tile_weights(moe_handle* h, const moe_desc* d, int which, const void* sr
  *   x[T,D] (dtype), W_r[M,D] fp32, bias[M] fp32 (SIGMOID only; NULL = zero;
  *   ignored for SOFTMAX) -> idx[T,k] int32, w[T,k] fp32.
  * A token's k experts are distinct and stored in ascending expert order;
- * an exactly equal selection score goes to the lower expert index.
+ * an exactly equal selection score goes to the lower expert index.  With
+ * d->n_group > 1 only the kept groups' experts compete (see moe_desc).
  * Uses workspace (the split router weights and partial logits). */
 int moe_route(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
               const float* bias, int32_t* idx, float* w, void* ws, size_t ws_bytes,

@@ -38,7 +38,8 @@ class moe_desc(ctypes.Structure):
                 ("scorer", ctypes.c_int32), ("act", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("renorm", ctypes.c_int32),
                 ("alpha", ctypes.c_float), ("eps", ctypes.c_float),
-                ("weight_layout", ctypes.c_int32)]
+                ("weight_layout", ctypes.c_int32), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32)]
 
 
 class moe_kernel_time(ctypes.Structure):
@@ -119,6 +120,8 @@ def make_desc(cfg=None, **kw) -> moe_desc:
         for n in ("T", "D", "M", "F", "F_shared", "k", "scorer", "act", "dtype", "renorm",
                   "alpha", "eps"):
             f[n] = getattr(cfg, n)
+        for n in ("n_group", "topk_group"):
+            f[n] = getattr(cfg, n, 0)
     f.update(kw)
     sc, ac, dt = f["scorer"], f["act"], f["dtype"]
     od = f.get("out_dtype", dt)
@@ -128,7 +131,8 @@ def make_desc(cfg=None, **kw) -> moe_desc:
                     scorer=SCORER.get(sc, sc), act=ACT.get(ac, ac), dtype=DTYPE.get(dt, dt),
                     out_dtype=DTYPE.get(od, od),
                     renorm=int(bool(f.get("renorm", 1))), alpha=float(f.get("alpha", 1.0)),
-                    eps=float(f.get("eps", 1e-20)), weight_layout=LAYOUT.get(wl, wl))
+                    eps=float(f.get("eps", 1e-20)), weight_layout=LAYOUT.get(wl, wl),
+                    n_group=int(f.get("n_group", 0)), topk_group=int(f.get("topk_group", 0)))
 
 
 def _ptr(t, name, dtype=None, numel=None):

@@ -100,6 +100,19 @@ int validate(const moe_desc* d) {
     if (d->out_dtype != MOE_DTYPE_F32 && d->out_dtype != MOE_DTYPE_BF16)
         return fail(MOE_ERR_INVALID, "unknown out_dtype %d", d->out_dtype);
     if (d->renorm != 0 && d->renorm != 1) return fail(MOE_ERR_INVALID, "renorm must be 0 or 1");
+    if (d->n_group < 0 || d->topk_group < 0)
+        return fail(MOE_ERR_INVALID, "n_group and topk_group must be >= 0");
+    if (d->n_group > 1) {
+        if (d->n_group > MOE_MAX_GROUPS)
+            return fail(MOE_ERR_UNSUPPORTED, "n_group=%d > %d", d->n_group, MOE_MAX_GROUPS);
+        if (d->M % d->n_group)
+            return fail(MOE_ERR_INVALID, "M=%lld is not a multiple of n_group=%d",
+                        (long long)d->M, d->n_group);
+        if (d->topk_group < 1 || d->topk_group > d->n_group ||
+            (int64_t)d->topk_group * (d->M / d->n_group) < d->k)
+            return fail(MOE_ERR_INVALID, "topk_group=%d must be in [1, n_group] and keep >= k "
+                        "experts", d->topk_group);
+    }
     if (d->weight_layout != MOE_LAYOUT_ROWS && d->weight_layout != MOE_LAYOUT_TILED)
         return fail(MOE_ERR_INVALID, "unknown weight_layout %d", d->weight_layout);
     if (d->weight_layout == MOE_LAYOUT_TILED && d->dtype != MOE_DTYPE_BF16)
@@ -224,7 +237,8 @@ int do_route(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, con
              const float* bias, int32_t* idx, float* w, void* ws, hipStream_t s) {
     return run(h, s, L_ROUTE, [&] {
         return launch_route(s, d->dtype, d->scorer, x, W_r, bias, idx, w, d->T, d->D, d->M, d->k,
-                            d->renorm, d->alpha, d->eps, at<char>(ws, p.route));
+                            d->renorm, d->alpha, d->eps, d->n_group > 1 ? d->n_group : 0,
+                            d->topk_group, at<char>(ws, p.route));
     });
 }
 

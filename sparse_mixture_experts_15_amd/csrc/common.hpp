@@ -115,7 +115,8 @@ int gemm_group_m(int64_t rows, int64_t groups, int bm);
 namespace moe {
 hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, const float* W_r,
                         const float* bias, int32_t* idx, float* w, int64_t T, int64_t D,
-                        int64_t M, int k, int renorm, float alpha, float eps, void* ws);
+                        int64_t M, int k, int renorm, float alpha, float eps, int n_group,
+                        int topk_group, void* ws);
 // Router workspace (bytes) and its K-split count.
 size_t route_workspace(int dtype, int64_t T, int64_t D, int64_t M);
 int route_ksplit(int64_t T, int64_t D, int64_t M);

@@ -56,9 +56,13 @@ __device__ __forceinline__ bool better(double av, int ai, double bv, int bi) {
 }
 
 // One wave: top-k of one token from its fp32 logits `lrow[0..M)`.
-// Writes k (expert, weight) pairs in ascending expert order.
+// Writes k (expert, weight) pairs in ascending expert order.  With
+// n_group > 1 the experts form n_group contiguous groups and only the
+// topk_group groups with the largest best selection score compete (the
+// GLM-4.5 note's optional masking by expert group).
 __device__ void topk_epilogue(const float* lrow, int M, int k, int scorer, const float* bias,
-                              int renorm, double alpha, double eps, int32_t* idx_t, float* w_t) {
+                              int renorm, double alpha, double eps, int n_group, int topk_group,
+                              int32_t* idx_t, float* w_t) {
     const int lane = threadIdx.x & 63;
     const int nj = (M + 63) >> 6;
     double sel[kMaxLanesJ];
@@ -94,6 +98,47 @@ __device__ void topk_epilogue(const float* lrow, int M, int k, int scorer, const
     }
 
     uint32_t taken = 0;
+    if (n_group > 1) {
+        // lane g holds group g's score: the largest selection score in it
+        const int gs = M / n_group;
+        double my_gs = -INFINITY;
+        for (int gi = 0; gi < n_group; ++gi) {
+            double v = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < kMaxLanesJ; ++j) {
+                const int e = lane + 64 * j;
+                if (j < nj && e < M && e / gs == gi) v = fmax(v, sel[j]);
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+            if (lane == gi) my_gs = v;
+        }
+        // keep the topk_group best groups (the lower group index on a tie)
+        uint64_t kept = 0;
+        bool mine = false;
+        for (int r = 0; r < topk_group; ++r) {
+            const bool cand = lane < n_group && !mine;
+            double bv = cand ? my_gs : -INFINITY;
+            int bi = cand ? lane : 0x7fffffff;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const double ov = __shfl_xor(bv, off);
+                const int oi = __shfl_xor(bi, off);
+                if (better(ov, oi, bv, bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            if (lane == bi) mine = true;
+            kept |= 1ull << bi;
+        }
+        // experts of the other groups leave the selection
+#pragma unroll
+        for (int j = 0; j < kMaxLanesJ; ++j) {
+            const int e = lane + 64 * j;
+            if (j < nj && e < M && !((kept >> (e / gs)) & 1ull)) taken |= 1u << j;
+        }
+    }
     int my_e = 0;
     for (int r = 0; r < k; ++r) {
         double bv = -INFINITY;
@@ -166,7 +211,8 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ P, i
                                                   const float* __restrict__ bias,
                                                   int32_t* __restrict__ idx, float* __restrict__ w,
                                                   int T, int M, int k, int scorer, int renorm,
-                                                  float alpha, float eps) {
+                                                  float alpha, float eps, int n_group,
+                                                  int topk_group) {
     extern __shared__ float s_logit[];   // [4][M]
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -187,8 +233,8 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ P, i
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    topk_epilogue(lrow, M, k, scorer, bias, renorm, (double)alpha, (double)eps,
-                  idx + (int64_t)t * k, w + (int64_t)t * k);
+    topk_epilogue(lrow, M, k, scorer, bias, renorm, (double)alpha, (double)eps, n_group,
+                  topk_group, idx + (int64_t)t * k, w + (int64_t)t * k);
 }
 
 // Generic router: one wave per token, fp64 dot products (fp32 or bf16 x).
@@ -196,7 +242,7 @@ template <typename XT>
 __global__ __launch_bounds__(256) void route_simple(
     const XT* __restrict__ x, const float* __restrict__ W_r, const float* __restrict__ bias,
     int32_t* __restrict__ idx, float* __restrict__ w, int T, int D, int M, int k, int scorer,
-    int renorm, float alpha, float eps) {
+    int renorm, float alpha, float eps, int n_group, int topk_group) {
     extern __shared__ float s_logit[];   // [4][M]
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -219,8 +265,8 @@ __global__ __launch_bounds__(256) void route_simple(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    topk_epilogue(lrow, M, k, scorer, bias, renorm, (double)alpha, (double)eps,
-                  idx + (int64_t)t * k, w + (int64_t)t * k);
+    topk_epilogue(lrow, M, k, scorer, bias, renorm, (double)alpha, (double)eps, n_group,
+                  topk_group, idx + (int64_t)t * k, w + (int64_t)t * k);
 }
 
 }  // namespace
@@ -245,7 +291,8 @@ size_t route_workspace(int dtype, int64_t T, int64_t D, int64_t M) {
 
 hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, const float* W_r,
                         const float* bias, int32_t* idx, float* w, int64_t T, int64_t D,
-                        int64_t M, int k, int renorm, float alpha, float eps, void* ws) {
+                        int64_t M, int k, int renorm, float alpha, float eps, int n_group,
+                        int topk_group, void* ws) {
     if (T == 0) return hipSuccess;
     const float* b = (scorer == 1) ? bias : nullptr;
     if (dtype == 1) {
@@ -271,14 +318,14 @@ hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, con
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(route_topk, dim3((unsigned)((T + 3) / 4)), dim3(256),
                            4 * (size_t)M * sizeof(float), s, P, nK, b, idx, w, (int)T, (int)M, k,
-                           scorer, renorm, alpha, eps);
+                           scorer, renorm, alpha, eps, n_group, topk_group);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((T + 3) / 4));
     const size_t lds = 4 * (size_t)M * sizeof(float);
     hipLaunchKernelGGL(route_simple<float>, grid, dim3(256), lds, s,
                        static_cast<const float*>(x), W_r, b, idx, w, (int)T, (int)D, (int)M, k,
-                       scorer, renorm, alpha, eps);
+                       scorer, renorm, alpha, eps, n_group, topk_group);
     return hipGetLastError();
 }
 

@@ -35,18 +35,20 @@ def test_descriptor_layout_matches_header(tmp_path):
     prog = tmp_path / "layout.c"
     prog.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
-        'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_desc),'
+        'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_kernel_time),'
+        ' sizeof(moe_desc),'
         ' offsetof(moe_desc,k), offsetof(moe_desc,renorm), offsetof(moe_desc,alpha),'
         ' offsetof(moe_desc,eps), offsetof(moe_desc,weight_layout),'
-        ' sizeof(moe_kernel_time)); return 0;}\n')
+        ' offsetof(moe_desc,topk_group)); return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)],
                    check=True)
     got = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True,
                                        check=True).stdout.split()))
     d = B.moe_desc
-    assert got == [ctypes.sizeof(d), d.k.offset, d.renorm.offset, d.alpha.offset,
-                   d.eps.offset, d.weight_layout.offset, ctypes.sizeof(B.moe_kernel_time)]
+    assert got == [ctypes.sizeof(B.moe_kernel_time), ctypes.sizeof(d), d.k.offset,
+                   d.renorm.offset, d.alpha.offset, d.eps.offset, d.weight_layout.offset,
+                   d.topk_group.offset]
 
 
 def _ws(desc):
@@ -162,3 +164,19 @@ def test_tiled_weight_errors():
     vp = ctypes.c_void_p
     assert lib.moe_tile_weights(None, ctypes.byref(d), 0, vp(16), vp(16), None) \
         == B.MOE_ERR_INVALID
+
+
+@pytest.mark.parametrize("ng,tg,status", [
+    (-1, 0, B.MOE_ERR_INVALID), (3, 1, B.MOE_ERR_INVALID),      # 8 experts: 3 groups do not divide
+    (4, 0, B.MOE_ERR_INVALID), (4, 5, B.MOE_ERR_INVALID),        # topk_group outside [1, n_group]
+    (8, 1, B.MOE_ERR_INVALID),                                   # 1 group of 1 expert < k = 2
+    (4, 1, B.MOE_OK), (1, 0, B.MOE_OK), (0, 0, B.MOE_OK), (8, 2, B.MOE_OK),
+])
+def test_group_routing_validation(ng, tg, status):
+    cfg = workloads.shrink(workloads.GLAM_4K, T=16, D=64, F=32).replace(M=8)
+    d = B.make_desc(cfg, n_group=ng, topk_group=tg)
+    n = ctypes.c_size_t()
+    assert B.load_library().moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == status
+    d = B.make_desc(workloads.GLM45_PREFILL, M=1024, n_group=128, topk_group=4)
+    assert B.load_library().moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) \
+        == B.MOE_ERR_UNSUPPORTED

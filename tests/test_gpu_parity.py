@@ -38,6 +38,11 @@ PARITY = {
     "glam_mid": S(workloads.GLAM_4K, T=512, D=512, F=1024).replace(M=8),
     # ~200 rows per expert under Zipf routing: one 256-row tile per expert
     "glm5_rows": S(workloads.GLM5_ZIPF, T=600, D=320, F=136, F_shared=136).replace(M=24),
+    # group-limited routing: 8 groups of 20 experts, the best 4 kept
+    "glm45_grouped": S(workloads.GLM45_PREFILL, T=333, D=264, F=200,
+                       F_shared=136).replace(n_group=8, topk_group=4),
+    # softmax scorer with 8 groups of 8 experts, the best 2 kept
+    "glam_grouped": S(workloads.GLAM_4K, T=700, D=264, F=200).replace(n_group=8, topk_group=2),
     # fp32 SwiGLU layer with a shared expert (fp32 path of every epilogue)
     "fp32_swiglu": S(workloads.GLM45_PREFILL, T=150, D=96, F=40, F_shared=48).replace(dtype="f32"),
 }
