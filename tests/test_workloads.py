@@ -8,10 +8,11 @@ import workloads
 
 def test_configs_shapes():
     c = workloads.CONFIGS
-    assert [x.T for x in c] == [64, 4096, 8192, 16384, 64, 8192]
-    assert [x.M for x in c] == [8, 64, 160, 256, 160, 160]
-    assert [x.k for x in c] == [2, 2, 8, 8, 8, 8]
-    assert [(x.n_group, x.topk_group) for x in c] == [(0, 0)] * 5 + [(8, 4)]
+    assert [x.T for x in c] == [64, 4096, 8192, 16384, 64, 8192, 4096]
+    assert [x.M for x in c] == [8, 64, 160, 256, 160, 160, 64]
+    assert [x.k for x in c] == [2, 2, 8, 8, 8, 8, 1]
+    assert [(x.n_group, x.topk_group) for x in c] == [(0, 0)] * 5 + [(8, 4), (0, 0)]
+    assert not workloads.SWITCH_TOP1.renorm
     assert workloads.GLM45_DECODE.D == workloads.GLM45_PREFILL.D
     assert workloads.get("glm45") is workloads.GLM45_PREFILL
 

@@ -96,12 +96,20 @@ GLM45_DECODE = GLM45_PREFILL.replace(name="glm45_decode_t64_d5120_m160_f1536", T
 GLM45_GROUPED = GLM45_PREFILL.replace(name="glm45_grouped_t8192_d5120_m160_f1536_g8k4",
                                       n_group=8, topk_group=4)
 
-CONFIGS = [GLAM_TINY_FP32, GLAM_4K, GLM45_PREFILL, GLM5_ZIPF, GLM45_DECODE, GLM45_GROUPED]
+# Switch-style top-1 routing (the GLaM note's related-work table: top-1
+# sparse FFN routing) through the same kernels, at the GLaM layer's shape.
+# The gate value is the router probability itself: with one expert, the
+# renormalised weight would always be 1.
+SWITCH_TOP1 = GLAM_4K.replace(name="switch_top1_t4096_d4096_m64_f16384", k=1, renorm=False)
+
+CONFIGS = [GLAM_TINY_FP32, GLAM_4K, GLM45_PREFILL, GLM5_ZIPF, GLM45_DECODE, GLM45_GROUPED,
+           SWITCH_TOP1]
 BY_NAME = {c.name: c for c in CONFIGS}
 # Short aliases used by the harness command line.
 ALIASES = {
     "tiny": GLAM_TINY_FP32, "glam": GLAM_4K, "glm45": GLM45_PREFILL,
     "glm5": GLM5_ZIPF, "decode": GLM45_DECODE, "glm45g": GLM45_GROUPED,
+    "switch": SWITCH_TOP1,
 }
 
 
