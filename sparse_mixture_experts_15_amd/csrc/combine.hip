@@ -1,9 +1,10 @@
 // Combine: y[t] = sum_j O[slot_row[t*k + j]] + Ysh[t]  (the GLaM study note's
 // MoE output sum over the selected experts; the GLM-4.5 note's output
 // equation adds the shared expert).  The sorted rows O (fp32) already carry
-// their gate weights.  One wave per token, fp32 sum in fixed slot order, one
-// rounding to the output dtype, 16-byte vector loads and stores.  It is a
-// gather, not a scatter: no atomics, so the result is deterministic.
+// their gate weights.  fp32 sum in fixed slot order, one rounding to the
+// output dtype, 16-byte vector loads and stores, one wave per token and
+// column chunk.  It is a gather, not a scatter: no atomics, so the result
+// is deterministic.
 #include "common.hpp"
 
 namespace moe {
@@ -42,35 +43,38 @@ template <typename TY>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ O,
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ Ysh,
-                                                      TY* __restrict__ y, int Tn, int k, int D) {
+                                                      TY* __restrict__ y, int Tn, int k, int D,
+                                                      int chunks) {
+    // one wave per (token, chunk of 64 x V columns): enough waves to keep
+    // HBM busy even for a decode-sized batch
     constexpr int V = Out<TY>::V;
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = (int)(wid / chunks);
     if (t >= Tn) return;
+    const int d0 = (int)(wid % chunks) * 64 * V + lane * V;
+    if (d0 >= D) return;
     int rows[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) rows[j] = (j < k) ? slot_row[(int64_t)t * k + j] : -1;
-#pragma unroll 2
-    for (int d0 = lane * V; d0 < D; d0 += 64 * V) {
-        float acc[V];
+    float acc[V];
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            if (rows[j] < 0) continue;
-            float v[V];
-            load_f32<V>(O + (int64_t)rows[j] * D + d0, v);
+    for (int j = 0; j < kMaxK; ++j) {
+        if (rows[j] < 0) continue;
+        float v[V];
+        load_f32<V>(O + (int64_t)rows[j] * D + d0, v);
 #pragma unroll
-            for (int i = 0; i < V; ++i) acc[i] += v[i];
-        }
-        if (Ysh) {
-            float v[V];
-            load_f32<V>(Ysh + (int64_t)t * D + d0, v);
-#pragma unroll
-            for (int i = 0; i < V; ++i) acc[i] += v[i];
-        }
-        Out<TY>::store(y + (int64_t)t * D + d0, acc);
+        for (int i = 0; i < V; ++i) acc[i] += v[i];
     }
+    if (Ysh) {
+        float v[V];
+        load_f32<V>(Ysh + (int64_t)t * D + d0, v);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] += v[i];
+    }
+    Out<TY>::store(y + (int64_t)t * D + d0, acc);
 }
 
 }  // namespace
@@ -78,13 +82,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 hipError_t launch_combine(hipStream_t s, int out_dtype, const float* O, const int32_t* slot_row,
                           const float* Ysh, void* y, int64_t T, int k, int64_t D) {
     if (T == 0) return hipSuccess;
-    dim3 grid((unsigned)((T + 3) / 4));
+    const int V = out_dtype == 1 ? Out<bf16_t>::V : Out<float>::V;
+    const int chunks = (int)((D + 64 * V - 1) / (64 * V));
+    dim3 grid((unsigned)((T * chunks + 3) / 4));
     if (out_dtype == 1)
         hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s, O, slot_row, Ysh,
-                           static_cast<bf16_t*>(y), (int)T, k, (int)D);
+                           static_cast<bf16_t*>(y), (int)T, k, (int)D, chunks);
     else
         hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, O, slot_row, Ysh,
-                           static_cast<float*>(y), (int)T, k, (int)D);
+                           static_cast<float*>(y), (int)T, k, (int)D, chunks);
     return hipGetLastError();
 }
 

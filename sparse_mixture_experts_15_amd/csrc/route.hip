@@ -203,38 +203,36 @@ __global__ __launch_bounds__(256) void router_split(const float* __restrict__ W_
     *reinterpret_cast<bf16x8*>(W3 + 2 * n + i) = lo;
 }
 
-// One wave per token: logit[e] = sum over K chunks z (in order) of the hi
-// plane's partial, plus the same sums of the mid and lo planes:
-// P[z][t][p*M + e] is x_t . plane_p[e] over chunk z.  Then the top-k
-// epilogue.
-__global__ __launch_bounds__(256) void route_topk(const float* __restrict__ P, int nK,
+// logit[t][e] = sum over K chunks z (in order) of the hi plane's partial,
+// plus the same sums of the mid and lo planes: P[z][t][p*M + e] is
+// x_t . plane_p[e] over chunk z.  One thread per (token, expert).
+__global__ __launch_bounds__(256) void route_reduce(const float* __restrict__ P, int nK, int T,
+                                                    int M, float* __restrict__ L) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)T * M) return;
+    const int64_t t = i / M, e = i % M, ld = 3 * (int64_t)M;
+    float h = 0.f, m = 0.f, l = 0.f;
+    for (int z = 0; z < nK; ++z) {
+        const float* row = P + ((int64_t)z * T + t) * ld;
+        h += row[e];
+        m += row[M + e];
+        l += row[2 * M + e];
+    }
+    L[i] = h + (m + l);
+}
+
+// One wave per token: the top-k epilogue on its logits L[t][0..M).
+__global__ __launch_bounds__(256) void route_topk(const float* __restrict__ L,
                                                   const float* __restrict__ bias,
                                                   int32_t* __restrict__ idx, float* __restrict__ w,
                                                   int T, int M, int k, int scorer, int renorm,
                                                   float alpha, float eps, int n_group,
                                                   int topk_group) {
-    extern __shared__ float s_logit[];   // [4][M]
-    const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;   // whole wave leaves; no block barrier follows
-    float* lrow = s_logit + wave * M;
-    const int64_t ld = 3 * (int64_t)M;
-    for (int e = lane; e < M; e += 64) {
-        float h = 0.f, m = 0.f, l = 0.f;
-        for (int z = 0; z < nK; ++z) {
-            const float* row = P + ((int64_t)z * T + t) * ld;
-            h += row[e];
-            m += row[M + e];
-            l += row[2 * M + e];
-        }
-        lrow[e] = h + (m + l);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    topk_epilogue(lrow, M, k, scorer, bias, renorm, (double)alpha, (double)eps, n_group,
-                  topk_group, idx + (int64_t)t * k, w + (int64_t)t * k);
+    topk_epilogue(L + (int64_t)t * M, M, k, scorer, bias, renorm, (double)alpha, (double)eps,
+                  n_group, topk_group, idx + (int64_t)t * k, w + (int64_t)t * k);
 }
 
 // Generic router: one wave per token, fp64 dot products (fp32 or bf16 x).
@@ -284,9 +282,13 @@ int route_ksplit(int64_t T, int64_t D, int64_t M) {
     return (int)nk;
 }
 
+// Workspace: the split router weights W3 [3][M][D] bf16, the partial logits
+// P [nK][T][3M] fp32 and the logits L [T][M] fp32, each 256-byte aligned.
+static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 size_t route_workspace(int dtype, int64_t T, int64_t D, int64_t M) {
     if (dtype != 1) return 0;
-    return (size_t)3 * M * D * 2 + 256 + (size_t)route_ksplit(T, D, M) * T * 3 * M * 4;
+    return align256((size_t)3 * M * D * 2) +
+           align256((size_t)route_ksplit(T, D, M) * T * 3 * M * 4) + (size_t)T * M * 4;
 }
 
 hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, const float* W_r,
@@ -298,8 +300,10 @@ hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, con
     if (dtype == 1) {
         const int nK = route_ksplit(T, D, M);
         bf16_t* W3 = static_cast<bf16_t*>(ws);
-        float* P = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                            (((size_t)3 * M * D * 2 + 255) & ~size_t(255)));
+        char* base = static_cast<char*>(ws);
+        float* P = reinterpret_cast<float*>(base + align256((size_t)3 * M * D * 2));
+        float* L = reinterpret_cast<float*>(base + align256((size_t)3 * M * D * 2) +
+                                            align256((size_t)nK * T * 3 * M * 4));
         const int64_t n = M * D;
         hipLaunchKernelGGL(router_split, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s,
                            W_r, W3, n);
@@ -316,9 +320,10 @@ hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, con
         g.k_split = nK;
         hipError_t e = launch_gemm(s, 1, 128, EPI_DOWN_F32, g, (T + 127) / 128);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(route_topk, dim3((unsigned)((T + 3) / 4)), dim3(256),
-                           4 * (size_t)M * sizeof(float), s, P, nK, b, idx, w, (int)T, (int)M, k,
-                           scorer, renorm, alpha, eps, n_group, topk_group);
+        hipLaunchKernelGGL(route_reduce, dim3((unsigned)((T * M + 255) / 256)), dim3(256), 0, s,
+                           P, nK, (int)T, (int)M, L);
+        hipLaunchKernelGGL(route_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, L, b, idx,
+                           w, (int)T, (int)M, k, scorer, renorm, alpha, eps, n_group, topk_group);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((T + 3) / 4));

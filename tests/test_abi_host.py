@@ -64,7 +64,9 @@ def test_workspace_size_covers_intermediates():
         need = S * cfg.F * esz + S * cfg.D * 4 + cfg.T * cfg.F_shared * esz
         if cfg.F_shared:
             need += cfg.T * cfg.D * 4
-        assert need <= n <= need + 64 * 2**20
+        # slack: the router's scratch (split weights, partial and final fp32
+        # logits) and alignment
+        assert need <= n <= need + 64 * 2**20 + 16 * cfg.T * cfg.M
 
 
 @pytest.mark.parametrize("field,value,status", [
