@@ -1,6 +1,7 @@
 // C ABI of the MoE layer: descriptor validation, workspace plan, stream
 // fork/join and kernel launches.  Every check runs before the first
 // launch, so an error leaves the outputs and the streams untouched.
+#include <cstdlib>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -286,6 +287,7 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     up.tiles = tiles_up;
     up.dense_rows = p.S;
     up.group_m = gemm_group_m(p.S, d->M, p.bm_up);
+    up.xcd_mode = gemm_xcd_mode(true, false);
     up.offsets = offsets;
     up.a_rows = d->T;
     up.b_rows = (int)((swiglu ? 2 : 1) * d->F);
@@ -307,6 +309,7 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     dn.c = O;
     dn.tiles = tiles_dn;
     dn.group_m = gemm_group_m(p.S, d->M, p.bm_dn);
+    dn.xcd_mode = gemm_xcd_mode(true, true);
     dn.offsets = offsets;
     dn.a_rows = p.S;
     dn.b_rows = (int)d->D;
@@ -334,6 +337,7 @@ int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, co
     up.K = (int)d->D;
     up.N = (int)d->F_shared;
     up.F_split = (int)d->F_shared;
+    up.xcd_mode = gemm_xcd_mode(false, false);
     TRY(run(h, s, L_SHARED_UP,
             [&] { return launch_gemm(s, d->dtype, p.bm_sh_up, EPI_SWIGLU, up, mt_up); }));
     GemmArgs dn{};
@@ -347,6 +351,7 @@ int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, co
     dn.b_rows = (int)d->D;
     dn.K = (int)d->F_shared;
     dn.N = (int)d->D;
+    dn.xcd_mode = gemm_xcd_mode(false, true);
     return run(h, s, L_SHARED_DOWN,
                [&] { return launch_gemm(s, d->dtype, p.bm_sh_dn, EPI_DOWN_F32, dn, mt_dn); });
 }
@@ -586,6 +591,11 @@ int moe_forward(moe_handle* h, const moe_desc* d, const void* x, const float* W_
     float* Ysh = d->F_shared > 0 ? at<float>(ws, p.Ysh) : nullptr;
 
     const bool fork = Ysh && aux && aux != s;
+    const char* fenv = getenv("MOE_FORK_AT");
+    const int fork_at = fenv ? atoi(fenv) : 0;
+    if (fork_at >= 1) TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
+    if (fork_at >= 2)
+        TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
     if (Ysh) {
         if (fork) {
             hipError_t e;
@@ -599,8 +609,9 @@ int moe_forward(moe_handle* h, const moe_desc* d, const void* x, const float* W_
             TRY(do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, s));
         }
     }
-    TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
-    TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
+    if (fork_at < 1) TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
+    if (fork_at < 2)
+        TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
     TRY(do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O, ws, s));
     if (fork) {
         const hipError_t e = hipStreamWaitEvent(s, h->ev_join, 0);

@@ -88,6 +88,8 @@ struct GemmArgs {
                               // [rows, N] partial at c + chunk * rows * N (0 = 1)
     int group_m;              // m-tiles per group of the tile order (0 = 4)
     int b_tiled;              // b holds tiled blocks (bf16): b_stride = one expert's blocks
+    int xcd_mode;             // workgroup order: 0 groups dealt to XCDs in turn, 1 plain,
+                              // 2 contiguous slices per XCD
 };
 
 // Weight tiles of the bf16 GEMM: 256 weight rows by K stages of 64.
@@ -108,6 +110,9 @@ hipError_t launch_tile_weights(hipStream_t s, const void* src, void* dst, int64_
 // one expert spans, so that the workgroups one XCD runs together share that
 // expert's weight tiles and rows in its L2.
 int gemm_group_m(int64_t rows, int64_t groups, int bm);
+// Workgroup order (GemmArgs::xcd_mode) of a grouped or dense up or down
+// projection.
+int gemm_xcd_mode(bool grouped, bool down);
 
 }  // namespace moe
 

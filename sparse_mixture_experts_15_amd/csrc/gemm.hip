@@ -147,24 +147,38 @@ __device__ __forceinline__ int swz(int row, int c) {
     return row * KS + ((c ^ swz_chunk<KS>(row)) << 3);
 }
 
-// Workgroup order.  Hardware hands consecutive workgroup ids to the eight
-// XCDs in turn; the ids are first regrouped so that consecutive logical
-// tiles land on one XCD, then tiles are ordered in groups of group_m m-tiles
-// with the n-tiles inside a group, so the ~32 workgroups one XCD runs at a
-// time cover a few m-tiles x several n-tiles and share both operands' K
-// slabs in that XCD's L2.  `m_tiles` is the number of valid m-tiles (the
-// grid may be larger; ids past m_tiles x n_tiles return false), so every
-// XCD gets real work.
+// Workgroup order.  Tiles are taken in groups of group_m m-tiles with all
+// n-tiles inside a group, so the ~32 workgroups one XCD runs at a time
+// cover a few m-tiles x several n-tiles and share both operands' K slabs in
+// that XCD's L2.  Hardware hands consecutive workgroup ids to the eight
+// XCDs in turn; mode 0 deals whole groups to the XCDs in turn as well (XCD
+// x runs groups x, x + 8, ...), which keeps each group on one XCD and
+// spreads the groups of a grouped GEMM, whose cost varies with the rows
+// its experts received, evenly over the XCDs.  Mode 2 gives each XCD one
+// contiguous eighth of the tiles, mode 1 keeps the hardware order.  Ids
+// past the valid tiles return false.  `m_tiles` is the number of valid
+// m-tiles; the grid holds grid_tiles() ids.
 __device__ __forceinline__ bool tile_coords(int m_tiles, int n_tiles, int group_m, int p, int& mt,
-                                            int& nt) {
+                                            int& nt, int mode = 0) {
     const int G = m_tiles * n_tiles;
-    if (p >= G) return false;
-    const int per = G / 8;
-    if (p < per * 8) p = (p & 7) * per + (p >> 3);
-    const int group = p / (group_m * n_tiles);
-    const int first = group * group_m;
+    const int gsz = group_m * n_tiles;
+    int first, in;
+    if (mode == 0) {
+        const int x = p & 7, i = p >> 3;
+        const int grp = x + 8 * (i / gsz);
+        first = grp * group_m;
+        in = i - (i / gsz) * gsz;
+        if (first >= m_tiles) return false;
+    } else {
+        if (p >= G) return false;
+        const int per = G / 8;
+        if (mode == 2 && p < per * 8) p = (p & 7) * per + (p >> 3);
+        const int group = p / gsz;
+        first = group * group_m;
+        in = p - group * gsz;
+    }
     const int gsize = min(m_tiles - first, group_m);
-    const int in = p - group * group_m * n_tiles;
+    if (in >= gsize * n_tiles) return false;
     mt = first + in % gsize;
     nt = in / gsize;
     return true;
@@ -201,11 +215,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     const int m_valid = g.tiles ? min(m_tiles, g.tiles[2 * m_tiles]) : m_tiles;
     // split-K (dense fp32 output only): chunk kc of g.k_split covers a K range
     const int nsplit = g.k_split > 1 ? g.k_split : 1;
-    const int per_split = m_valid * n_tiles;
-    const int kc_id = (int)blockIdx.x / max(per_split, 1);
-    int mt, nt;
-    if (kc_id >= nsplit || !tile_coords(m_valid, n_tiles, g.group_m > 0 ? g.group_m : 4,
-                                             (int)blockIdx.x - kc_id * per_split, mt, nt))
+    int kc_id = 0, p = (int)blockIdx.x, mt, nt;
+    if (nsplit > 1) {   // split-K: chunk-major ids, plain order inside a chunk
+        kc_id = p / max(m_valid * n_tiles, 1);
+        if (kc_id >= nsplit) return;
+        p -= kc_id * m_valid * n_tiles;
+    }
+    if (!tile_coords(m_valid, n_tiles, g.group_m > 0 ? g.group_m : 4, p, mt, nt,
+                     nsplit > 1 ? 1 : g.xcd_mode))
         return;
     Tile tl;
     if (!tile_of(g, mt, BM, tl)) return;
@@ -507,13 +524,24 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs g) {
     }
 }
 
+// Workgroups to launch for m_tiles x n_tiles tiles (m_tiles may bound the
+// valid count from above): mode 0 deals whole groups to the eight XCDs in
+// turn, so the grid is rounded up to eight groups.
+int64_t grid_tiles(const GemmArgs& g, int64_t m_tiles, int64_t n_tiles) {
+    if (g.k_split > 1) return m_tiles * n_tiles * g.k_split;
+    if (g.xcd_mode != 0) return m_tiles * n_tiles;
+    const int64_t gm = g.group_m > 0 ? g.group_m : 4;
+    const int64_t groups = (m_tiles + gm - 1) / gm;
+    return ((groups + 7) / 8) * 8 * gm * n_tiles;
+}
+
 template <int EPI, int BMv, int BNv, int STv, int KS = 64>
 hipError_t launch_bf16(hipStream_t s, const GemmArgs& g, int64_t m_tiles) {
     const int opt = (EPI == EPI_SWIGLU) ? BNv / 2 : BNv;
     const int n_tiles = (g.N + opt - 1) / opt;
     if (g.k_split > (g.K + BK - 1) / BK) return hipErrorInvalidValue;   // each K chunk needs a stage
     if (g.b_tiled && (KS != kTileK || BNv != kTileRows)) return hipErrorInvalidValue;
-    const int64_t total = m_tiles * n_tiles * (g.k_split > 1 ? g.k_split : 1);
+    const int64_t total = grid_tiles(g, m_tiles, n_tiles);
     hipLaunchKernelGGL((gemm_bf16<EPI, BMv, BNv, STv, KS>), dim3((unsigned)total), dim3(NT), 0, s, g,
                        (int)m_tiles, n_tiles);
     return hipGetLastError();
@@ -575,6 +603,24 @@ int gemm_group_m(int64_t rows, int64_t groups, int bm) {
     }
     const int64_t per = (rows / (groups > 0 ? groups : 1) + bm / 2) / bm;
     return per < 1 ? 1 : per > 4 ? 4 : (int)per;
+}
+
+// Workgroup order of a GEMM (tile_coords modes).  Grouped up projections
+// keep the hardware order: their tiles' cost follows the rows each expert
+// received, and dealing single tiles to the XCDs in turn balances them
+// best; measured faster than per-XCD groups by ~1% (GLM-4.5 prefill) to 9%
+// (GLM-5, Zipf-skewed).  The grouped down projections and the dense GEMMs
+// deal whole groups to the XCDs, which keeps a group's operand slabs in
+// one L2 (GLM-4.5 down projection 1.34 ms against 1.61 ms in hardware
+// order).
+int gemm_xcd_mode(bool grouped, bool down) {
+    const char* name = grouped ? (down ? "MOE_XCD_DN" : "MOE_XCD_UP")
+                               : (down ? "MOE_XCD_SH_DN" : "MOE_XCD_SH_UP");
+    if (const char* env = getenv(name)) {   // tuning override
+        const int v = atoi(env);
+        if (v >= 0 && v <= 2) return v;
+    }
+    return grouped && !down ? 1 : 0;
 }
 
 hipError_t launch_gemm(hipStream_t s, int dtype, int bm, int epi, const GemmArgs& g,
