@@ -246,6 +246,11 @@ int do_route(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, con
 int do_permute(moe_handle* h, const moe_desc* d, const Plan& p, const int32_t* idx,
                int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* sorted_slot,
                int32_t* slot_row, void* ws, hipStream_t s) {
+    if (d->T <= kSmallT)
+        return run(h, s, L_PERM_SCATTER, [&] {
+            return launch_perm_small(s, idx, d->T, d->k, d->M, counts, offsets, sorted_token,
+                                     sorted_slot, slot_row);
+        });
     int32_t* hist = at<int32_t>(ws, p.hist);
     TRY(run(h, s, L_PERM_COUNT, [&] { return launch_perm_count(s, idx, hist, d->T, d->k, d->M); }));
     TRY(run(h, s, L_PERM_SCAN, [&] {
@@ -271,8 +276,7 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     const int ntables = tiles_dn == tiles_up ? 1 : 2;
     float* row_scale = at<float>(ws, p.row_scale);
     TRY(run(h, s, L_TILE_TABLE, [&] {
-        const hipError_t e = launch_tile_table(s, offsets, d->M, tt, ntables);
-        return e != hipSuccess ? e : launch_row_scales(s, sorted_slot, w, p.S, row_scale);
+        return launch_tile_table(s, offsets, d->M, tt, ntables, sorted_slot, w, p.S, row_scale);
     }));
     const bool swiglu = d->act == MOE_ACT_SWIGLU;
     GemmArgs up{};

@@ -139,11 +139,16 @@ struct TileTables {
     int max_tiles[2];
     int32_t* tiles[2];
 };
-// row_scale[r] = w[sorted_slot[r]] for the S sorted rows.
-hipError_t launch_row_scales(hipStream_t s, const int32_t* sorted_slot, const float* w, int64_t S,
-                             float* row_scale);
+// The tile tables, plus row_scale[r] = w[sorted_slot[r]] (0 for an unused
+// row) for the S sorted rows, in one launch.
 hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M,
-                             const TileTables& tt, int count);
+                             const TileTables& tt, int count, const int32_t* sorted_slot,
+                             const float* w, int64_t S, float* row_scale);
+// Count, scan and scatter in one workgroup for T <= kSmallT tokens.
+constexpr int64_t kSmallT = 1024;
+hipError_t launch_perm_small(hipStream_t s, const int32_t* idx, int64_t T, int k, int64_t M,
+                             int32_t* counts, int32_t* offsets, int32_t* sorted_token,
+                             int32_t* sorted_slot, int32_t* slot_row);
 hipError_t launch_gemm(hipStream_t s, int dtype, int bm, int epi, const GemmArgs& g,
                        int64_t m_tiles);
 hipError_t launch_combine(hipStream_t s, int out_dtype, const float* O, const int32_t* slot_row,

@@ -238,8 +238,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     const i32x4 ra = make_rsrc(g.a, (uint32_t)(a_rows * K * 2));
     const bf16_t* Bp = static_cast<const bf16_t*>(g.b) + (int64_t)tl.e * g.b_stride;
     const i32x4 rb = make_rsrc(Bp, (uint32_t)((g.b_tiled ? g.b_stride : (int64_t)g.b_rows * K) * 2));
-    // tiled weights: stage kt of this n-tile is one contiguous block
-    const uint32_t tile_base = (uint32_t)nt * (uint32_t)((K + BK - 1) / BK) * (BNB * BK * 2);
+    // tiled weights: stage kt of a 256-row weight tile is one contiguous
+    // block of 256 LDS-image rows; a 128-row n-tile takes half of one
+    constexpr uint32_t TILE_STAGE = kTileRows * BK * 2;
+    const uint32_t tile_base =
+        (uint32_t)(nt * BNB / kTileRows) * (uint32_t)((K + BK - 1) / BK) * TILE_STAGE +
+        (uint32_t)(nt * BNB % kTileRows) * (BK * 2);
 
     // Load q of wave w (ins = w + 8 q) fills ROWS_PER_LOAD rows: B rows of
     // block ins for q < QB, else A rows of block ins - B_LOADS; lane l -> row
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             uint32_t off = rowoff[q] + (uint32_t)kc * 2u;
             off = kc < K ? off : kOOB;
             if (q < QB && g.b_tiled)
-                off = tile_base + (uint32_t)kt * (BNB * BK * 2) + (uint32_t)ins * 1024u + lane * 16u;
+                off = tile_base + (uint32_t)kt * TILE_STAGE + (uint32_t)ins * 1024u + lane * 16u;
             if (q < QB)
                 llvm_amdgcn_raw_buffer_load_lds(rb, (lds_u32_ptr)(st + BM * BK + ins * 512), 16,
                                                 (int)off, 0, 0, 0);
@@ -540,7 +544,7 @@ hipError_t launch_bf16(hipStream_t s, const GemmArgs& g, int64_t m_tiles) {
     const int opt = (EPI == EPI_SWIGLU) ? BNv / 2 : BNv;
     const int n_tiles = (g.N + opt - 1) / opt;
     if (g.k_split > (g.K + BK - 1) / BK) return hipErrorInvalidValue;   // each K chunk needs a stage
-    if (g.b_tiled && (KS != kTileK || BNv != kTileRows)) return hipErrorInvalidValue;
+    if (g.b_tiled && (KS != kTileK || kTileRows % BNv != 0)) return hipErrorInvalidValue;
     const int64_t total = grid_tiles(g, m_tiles, n_tiles);
     hipLaunchKernelGGL((gemm_bf16<EPI, BMv, BNv, STv, KS>), dim3((unsigned)total), dim3(NT), 0, s, g,
                        (int)m_tiles, n_tiles);
@@ -554,6 +558,7 @@ hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64
         // (256 x 256 with K = 32 stages, 4 or 5 deep, measured slower than 2 x 64)
         if (bm == 256) return launch_bf16<EPI, 256, 256, 2>(s, g, m_tiles);
         if (bm == 160) return launch_bf16<EPI, 160, 256, 3>(s, g, m_tiles);
+        if (bm == 64) return launch_bf16<EPI, 64, 128, 5>(s, g, m_tiles);
         return launch_bf16<EPI, 128, 256, 3>(s, g, m_tiles);
     }
     const int opt = (EPI == EPI_SWIGLU) ? FBN / 2 : FBN;
@@ -569,7 +574,11 @@ hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64
 // per weight byte per row) the tile should cover a whole group with the
 // deepest ring that fits: 160-row tiles (3 stages) take groups of up to 160
 // rows, enough for a mean of ~128 rows under uniform routing.  Far smaller
-// groups leave most of any tile empty, and 128-row tiles waste the least.
+// groups leave most of any tile empty, and 128-row tiles waste the least;
+// for groups of a few rows (decode) the up projection takes 64 x 128 tiles
+// with a 5-stage ring, twice the workgroups over the same weights, which
+// evens out the last round of workgroups (GLM-4.5 decode up projection
+// 0.29 -> 0.26 ms; the down projection, K = expert width, is slower so).
 // Groups of hundreds of rows are MFMA-bound: 256-row tiles halve the LDS
 // traffic per MFMA for the up projection; the down projection keeps 128-row
 // tiles there (its short K = expert width favours the 3-stage ring), unless
@@ -583,13 +592,14 @@ int gemm_block_m(int dtype, int64_t rows, int64_t groups, bool down, int64_t b_r
                                   : (down ? "MOE_GEMM_BM_SH_DN" : "MOE_GEMM_BM_SH_UP");
     if (const char* env = getenv(name)) {
         const int v = atoi(env);
-        if (v == 128 || v == 160 || v == 256) return v;
+        if (v == 64 || v == 128 || v == 160 || v == 256) return v;
     }
     if (groups <= 1) {
         const int64_t tiles256 = (rows / 256) * ((b_rows + 255) / 256);
         return tiles256 >= 4 * 256 ? 256 : 128;
     }
     const int64_t avg = rows / groups;
+    if (avg <= 16 && !down) return 64;
     if (avg <= 96) return 128;
     if (avg <= 136) return 160;
     if (avg <= 224 || !down) return 256;

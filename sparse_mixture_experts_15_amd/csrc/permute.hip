@@ -134,6 +134,91 @@ __global__ __launch_bounds__(kPermBlock) void perm_scatter(
     }
 }
 
+// The whole dispatch in one workgroup when T <= kSmallT (one token per
+// thread, decode-sized batches): the per-wave expert masks of the scatter
+// give both the counts (their popcounts) and the stable ranks, so count,
+// scan and scatter run back to back without a launch in between.  Same
+// results as the three kernels above.
+__global__ __launch_bounds__(kScanThreads) void perm_small(const int32_t* __restrict__ idx, int T,
+                                                          int k, int M, int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_token,
+                                                          int32_t* __restrict__ sorted_slot,
+                                                          int32_t* __restrict__ slot_row) {
+    constexpr int NW = kScanThreads / 64;
+    extern __shared__ unsigned long long s_mask[];   // [NW][M], then s_off[M]
+    int32_t* s_off = reinterpret_cast<int32_t*>(s_mask + NW * M);
+    __shared__ int32_t s_warp[NW];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    for (int i = tid; i < NW * M; i += kScanThreads) s_mask[i] = 0ull;
+    __syncthreads();
+    const int t = tid;
+    int e_of[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) e_of[j] = -1;
+    if (t < T) {
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j < k) {
+                const int e = idx[(int64_t)t * k + j];
+                if (e >= 0 && e < M) {
+                    e_of[j] = e;
+                    atomicOr(&s_mask[wv * M + e], 1ull << lane);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // counts and their exclusive scan over experts (one expert per thread)
+    int32_t c = 0;
+    if (tid < M)
+        for (int w2 = 0; w2 < NW; ++w2) c += __popcll(s_mask[w2 * M + tid]);
+    int32_t incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_warp[wv] = incl;
+    __syncthreads();
+    int32_t base = 0, total = 0;
+    for (int i = 0; i < NW; ++i) {
+        if (i < wv) base += s_warp[i];
+        total += s_warp[i];
+    }
+    incl += base;
+    if (tid < M) {
+        counts[tid] = c;
+        offsets[tid] = incl - c;
+        s_off[tid] = incl - c;
+    }
+    if (tid == M - 1) offsets[M] = incl;
+    __syncthreads();
+    const int64_t S = (int64_t)T * k;
+    for (int64_t r = total + tid; r < S; r += kScanThreads) {
+        sorted_token[r] = -1;
+        sorted_slot[r] = -1;
+    }
+    if (t >= T) return;
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j >= k) break;
+        const int64_t f = (int64_t)t * k + j;
+        const int e = e_of[j];
+        if (e < 0) {
+            slot_row[f] = -1;
+            continue;
+        }
+        int rank = __popcll(s_mask[wv * M + e] & below);
+        for (int w2 = 0; w2 < wv; ++w2) rank += __popcll(s_mask[w2 * M + e]);
+        const int32_t r = s_off[e] + rank;
+        sorted_slot[r] = (int32_t)f;
+        sorted_token[r] = t;
+        slot_row[f] = r;
+    }
+}
+
 // Per m-tile of `bm` rows: (expert, first row).  Tiles are laid out expert
 // after expert; entries past the last tile are (-1, 0), and the number of
 // valid tiles is stored after the table, at tiles[2 * max_tiles].  One
@@ -141,8 +226,22 @@ __global__ __launch_bounds__(kPermBlock) void perm_scatter(
 // Workgroup y builds table y (the up and down projections may use different
 // tile heights).
 __global__ __launch_bounds__(kScanThreads) void tile_table(const int32_t* __restrict__ offsets,
-                                                          int M, TileTables tt) {
+                                                          int M, TileTables tt,
+                                                          const int32_t* __restrict__ sorted_slot,
+                                                          const float* __restrict__ w, int64_t S,
+                                                          float* __restrict__ row_scale) {
     __shared__ int32_t s_warp[kScanThreads / 64];
+    if (blockIdx.x > 0) {
+        // blocks 1.. of row y = 0: the down projection's row scales,
+        // row_scale[r] = w[sorted_slot[r]] (gate weight of each sorted row)
+        if (blockIdx.y != 0) return;
+        const int64_t r = (int64_t)(blockIdx.x - 1) * kScanThreads + threadIdx.x;
+        if (r < S) {
+            const int32_t f = sorted_slot[r];
+            row_scale[r] = f >= 0 ? w[f] : 0.f;
+        }
+        return;
+    }
     const int bm = tt.bm[blockIdx.y], max_tiles = tt.max_tiles[blockIdx.y];
     int32_t* __restrict__ tiles = tt.tiles[blockIdx.y];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -176,15 +275,6 @@ __global__ __launch_bounds__(kScanThreads) void tile_table(const int32_t* __rest
     if (tid == 0) tiles[2 * max_tiles] = total;
 }
 
-// Gate weight of each sorted row, in sorted order (the down projection's
-// row scale).
-__global__ __launch_bounds__(256) void row_scales(const int32_t* __restrict__ sorted_slot,
-                                                 const float* __restrict__ w, int64_t S,
-                                                 float* __restrict__ row_scale) {
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (r < S) row_scale[r] = w[sorted_slot[r]];
-}
-
 }  // namespace
 
 hipError_t launch_perm_count(hipStream_t s, const int32_t* idx, int32_t* hist, int64_t T, int k,
@@ -213,17 +303,24 @@ hipError_t launch_perm_scatter(hipStream_t s, const int32_t* idx, const int32_t*
     return hipGetLastError();
 }
 
-hipError_t launch_row_scales(hipStream_t s, const int32_t* sorted_slot, const float* w, int64_t S,
-                             float* row_scale) {
-    if (S <= 0) return hipSuccess;
-    hipLaunchKernelGGL(row_scales, dim3((unsigned)((S + 255) / 256)), dim3(256), 0, s, sorted_slot,
-                       w, S, row_scale);
+hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M,
+                             const TileTables& tt, int count, const int32_t* sorted_slot,
+                             const float* w, int64_t S, float* row_scale) {
+    const unsigned rs_blocks = (unsigned)((S + kScanThreads - 1) / kScanThreads);
+    hipLaunchKernelGGL(tile_table, dim3(1 + rs_blocks, count), dim3(kScanThreads), 0, s, offsets,
+                       (int)M, tt, sorted_slot, w, S, row_scale);
     return hipGetLastError();
 }
 
-hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M,
-                             const TileTables& tt, int count) {
-    hipLaunchKernelGGL(tile_table, dim3(1, count), dim3(kScanThreads), 0, s, offsets, (int)M, tt);
+size_t perm_small_lds(int64_t M) {
+    return (size_t)(kScanThreads / 64) * M * sizeof(unsigned long long) + M * sizeof(int32_t);
+}
+
+hipError_t launch_perm_small(hipStream_t s, const int32_t* idx, int64_t T, int k, int64_t M,
+                             int32_t* counts, int32_t* offsets, int32_t* sorted_token,
+                             int32_t* sorted_slot, int32_t* slot_row) {
+    hipLaunchKernelGGL(perm_small, dim3(1), dim3(kScanThreads), perm_small_lds(M), s, idx, (int)T,
+                       k, (int)M, counts, offsets, sorted_token, sorted_slot, slot_row);
     return hipGetLastError();
 }
 

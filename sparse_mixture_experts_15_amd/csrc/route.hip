@@ -60,9 +60,10 @@ __device__ __forceinline__ bool better(double av, int ai, double bv, int bi) {
 // n_group > 1 the experts form n_group contiguous groups and only the
 // topk_group groups with the largest best selection score compete (the
 // GLM-4.5 note's optional masking by expert group).
-__device__ void topk_epilogue(const float* lrow, int M, int k, int scorer, const float* bias,
-                              int renorm, double alpha, double eps, int n_group, int topk_group,
-                              int32_t* idx_t, float* w_t) {
+__device__ __forceinline__ void topk_epilogue(const float* lrow, int M, int k, int scorer,
+                                              const float* bias, int renorm, double alpha,
+                                              double eps, int n_group, int topk_group,
+                                              int32_t* idx_t, float* w_t) {
     const int lane = threadIdx.x & 63;
     const int nj = (M + 63) >> 6;
     double sel[kMaxLanesJ];

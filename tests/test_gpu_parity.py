@@ -38,6 +38,9 @@ PARITY = {
     "glam_mid": S(workloads.GLAM_4K, T=512, D=512, F=1024).replace(M=8),
     # ~200 rows per expert under Zipf routing: one 256-row tile per expert
     "glm5_rows": S(workloads.GLM5_ZIPF, T=600, D=320, F=136, F_shared=136).replace(M=24),
+    # more than 1024 tokens: the three-kernel dispatch (smaller batches take
+    # the one-workgroup dispatch)
+    "glm45_t1500": S(workloads.GLM45_PREFILL, T=1500, D=64, F=48, F_shared=48),
     # group-limited routing: 8 groups of 20 experts, the best 4 kept
     "glm45_grouped": S(workloads.GLM45_PREFILL, T=333, D=264, F=200,
                        F_shared=136).replace(n_group=8, topk_group=4),
@@ -173,12 +176,22 @@ def test_forward_deterministic_and_stream_invariant(name):
 # Every bf16 tile height on every GEMM (the library picks one per shape; the
 # MOE_GEMM_BM_* overrides force the others), covering both activations, the
 # grouped and dense GEMMs and every epilogue.
-@pytest.mark.parametrize("bm", [128, 160, 256])
+@pytest.mark.parametrize("bm", [64, 128, 160, 256])
 @pytest.mark.parametrize("name", ["glam_tiles", "glm45_small", "glam_mid"])
 def test_tile_heights(name, bm, monkeypatch):
     for var in ("MOE_GEMM_BM_UP", "MOE_GEMM_BM_DN", "MOE_GEMM_BM_SH_UP", "MOE_GEMM_BM_SH_DN"):
         monkeypatch.setenv(var, str(bm))
     _stage_parity(PARITY[name])
+
+
+# The same on the tiled weight copies: 64-row tiles read half of each 256-row
+# weight block.
+@pytest.mark.parametrize("bm", [64, 128, 160, 256])
+@pytest.mark.parametrize("name", ["glam_tiles", "glm45_small"])
+def test_tile_heights_tiled(name, bm, monkeypatch):
+    for var in ("MOE_GEMM_BM_UP", "MOE_GEMM_BM_DN", "MOE_GEMM_BM_SH_UP", "MOE_GEMM_BM_SH_DN"):
+        monkeypatch.setenv(var, str(bm))
+    _stage_parity(PARITY[name], tiled=True)
 
 
 EDGE = {
@@ -211,8 +224,10 @@ def test_empty_batch_is_noop():
     assert (y.float() == 7.0).all()
 
 
-def test_dropped_slots_in_permute_and_combine():
-    cfg = S(workloads.GLM45_PREFILL, T=260, D=64, F=48, F_shared=0)
+# T = 260 takes the one-workgroup dispatch, T = 1500 the three-kernel one.
+@pytest.mark.parametrize("T", [260, 1500])
+def test_dropped_slots_in_permute_and_combine(T):
+    cfg = S(workloads.GLM45_PREFILL, T=T, D=64, F=48, F_shared=0)
     t = workloads.generate(cfg, seed=3, device="cuda")
     h = workloads.host_inputs(t)
     L = new_layer(cfg)
