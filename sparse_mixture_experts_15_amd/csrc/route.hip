@@ -60,19 +60,19 @@ __device__ __forceinline__ bool better(double av, int ai, double bv, int bi) {
 // n_group > 1 the experts form n_group contiguous groups and only the
 // topk_group groups with the largest best selection score compete (the
 // GLM-4.5 note's optional masking by expert group).
-__device__ __forceinline__ void topk_epilogue(const float* lrow, int M, int k, int scorer,
+template <int NJ>
+__device__ __forceinline__ void topk_epilogue_nj(const float* lrow, int M, int k, int scorer,
                                               const float* bias, int renorm, double alpha,
                                               double eps, int n_group, int topk_group,
                                               int32_t* idx_t, float* w_t) {
     const int lane = threadIdx.x & 63;
-    const int nj = (M + 63) >> 6;
-    double sel[kMaxLanesJ];
+    double sel[NJ];
     double mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kMaxLanesJ; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const int e = lane + 64 * j;
         sel[j] = -INFINITY;
-        if (j < nj && e < M) {
+        if (e < M) {
             const double l = (double)lrow[e];
             if (scorer == 0) {
                 sel[j] = l;   // softmax is increasing in the logit
@@ -90,9 +90,9 @@ __device__ __forceinline__ void topk_epilogue(const float* lrow, int M, int k, i
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
 #pragma unroll
-        for (int j = 0; j < kMaxLanesJ; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const int e = lane + 64 * j;
-            if (j < nj && e < M) Z += exp((double)lrow[e] - mx);
+            if (e < M) Z += exp((double)lrow[e] - mx);
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) Z += __shfl_xor(Z, off);
@@ -106,9 +106,9 @@ __device__ __forceinline__ void topk_epilogue(const float* lrow, int M, int k, i
         for (int gi = 0; gi < n_group; ++gi) {
             double v = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < kMaxLanesJ; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const int e = lane + 64 * j;
-                if (j < nj && e < M && e / gs == gi) v = fmax(v, sel[j]);
+                if (e < M && e / gs == gi) v = fmax(v, sel[j]);
             }
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
@@ -135,9 +135,9 @@ __device__ __forceinline__ void topk_epilogue(const float* lrow, int M, int k, i
         }
         // experts of the other groups leave the selection
 #pragma unroll
-        for (int j = 0; j < kMaxLanesJ; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const int e = lane + 64 * j;
-            if (j < nj && e < M && !((kept >> (e / gs)) & 1ull)) taken |= 1u << j;
+            if (e < M && !((kept >> (e / gs)) & 1ull)) taken |= 1u << j;
         }
     }
     int my_e = 0;
@@ -145,9 +145,9 @@ __device__ __forceinline__ void topk_epilogue(const float* lrow, int M, int k, i
         double bv = -INFINITY;
         int bi = 0x7fffffff;
 #pragma unroll
-        for (int j = 0; j < kMaxLanesJ; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const int e = lane + 64 * j;
-            if (j < nj && e < M && !((taken >> j) & 1u) && better(sel[j], e, bv, bi)) {
+            if (e < M && !((taken >> j) & 1u) && better(sel[j], e, bv, bi)) {
                 bv = sel[j];
                 bi = e;
             }
@@ -184,6 +184,24 @@ __device__ __forceinline__ void topk_epilogue(const float* lrow, int M, int k, i
         idx_t[rank] = my_e;
         w_t[rank] = (float)wv;
     }
+}
+
+// The top-k epilogue with NJ expert registers per lane (M <= 64 NJ): the
+// per-lane loops unroll over exactly the registers the layer needs.
+__device__ __forceinline__ void topk_epilogue(const float* lrow, int M, int k, int scorer,
+                                              const float* bias, int renorm, double alpha,
+                                              double eps, int n_group, int topk_group,
+                                              int32_t* idx_t, float* w_t) {
+    const int nj = (M + 63) >> 6;
+#define MOE_TOPK(NJ_) topk_epilogue_nj<NJ_>(lrow, M, k, scorer, bias, renorm, alpha, eps, \
+                                            n_group, topk_group, idx_t, w_t)
+    if (nj <= 1) MOE_TOPK(1);
+    else if (nj == 2) MOE_TOPK(2);
+    else if (nj == 3) MOE_TOPK(3);
+    else if (nj == 4) MOE_TOPK(4);
+    else if (nj <= 8) MOE_TOPK(8);
+    else MOE_TOPK(kMaxLanesJ);
+#undef MOE_TOPK
 }
 
 // ---- bf16 x: exact three-way split of W_r, MFMA partial logits, top-k ----
