@@ -33,7 +33,13 @@
  * - `stream` / `aux_stream` are hipStream_t values passed as void*; NULL is
  *   the null stream.  All work is enqueued asynchronously; no call copies
  *   between host and device or synchronises the host, so results are valid
- *   once the stream(s) complete, and every call may be captured in a graph.
+ *   once the stream(s) complete, and every call may be captured in a graph
+ *   (moe_forward with its aux-stream fork and join included).
+ * - Every buffer, the workspace included, must be ready on `stream` when the
+ *   call is enqueued: work that produced it, or that still uses memory the
+ *   allocator handed out again for it, must be ordered before `stream` (the
+ *   same stream, an event wait, or a synchronisation).  The library orders
+ *   `aux_stream` after `stream` itself.
  * - Validation happens before anything is enqueued: on any error nothing is
  *   launched and the outputs are untouched.  T == 0 is a valid no-op.
  * - Identical inputs on the same device give bitwise-identical outputs
