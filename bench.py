@@ -104,6 +104,22 @@ def kernel_work(cfg, counts):
     return w, U
 
 
+def merge_shared(cfg, w):
+    """When the library runs the shared expert as one more group of the
+    routed GEMM launches (no separate shared kernels in the split), credit
+    its work to those launches; x is read once by the merged up projection."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    w = dict(w)
+    for routed, shared in (("ffn_up", "shared_up"), ("ffn_down", "shared_down")):
+        if shared in w:
+            fr, br = w[routed]
+            fs, bs = w.pop(shared)
+            w[routed] = (fr + fs, br + bs)
+    fu, bu = w["ffn_up"]
+    w["ffn_up"] = (fu, bu - cfg.T * cfg.D * esz)
+    return w
+
+
 def layer_work(cfg, U):
     """Active FLOPs and algorithmic bytes of the whole layer: touched expert
     weights, shared weights, router, x and y (intermediates not credited)."""
@@ -213,6 +229,8 @@ def main():
         step()
     B.moe_profile_stop(L.handle)
     split = {k: v[1] / nprof for k, v in B.moe_profile_results(L.handle).items()}
+    if cfg.F_shared and "shared_up" not in split:
+        kw = merge_shared(cfg, kw)
     dominant = max(split, key=split.get)
     log("per-step kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in split.items()))
 

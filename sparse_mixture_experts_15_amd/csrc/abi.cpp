@@ -37,6 +37,11 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Device workspace layout shared by every entry point.
 struct Plan {
+    // merged: moe_forward runs the shared expert as one more group (index
+    // M, every token once) of the routed GEMMs; its rows follow the S routed
+    // rows, so Hsh and Ysh are the tails of H and O, and Sx = S + T.
+    bool merged = false;
+    int64_t Sx = 0;
     int64_t S = 0, nblk = 0, max_tiles_up = 0, max_tiles_dn = 0;
     int bm_up = 0, bm_dn = 0, bm_sh_up = 0, bm_sh_dn = 0;
     size_t esz = 0;
@@ -51,14 +56,23 @@ Plan make_plan(const moe_desc* d) {
     p.S = d->T * d->k;
     p.nblk = (d->T + kPermBlock - 1) / kPermBlock;
     const int64_t G = d->act == MOE_ACT_SWIGLU ? 2 : 1;   // up-projection weight rows per F
-    p.bm_up = gemm_block_m(d->dtype, p.S, d->M, false, G * d->F);
-    p.bm_dn = gemm_block_m(d->dtype, p.S, d->M, true, d->D);
+    // A shared expert of one routed expert's shape joins the routed GEMMs
+    // when the batch is decode-sized: alone its GEMMs have a handful of
+    // workgroups and only contend with the router on the second stream.
+    const char* menv = getenv("MOE_MERGE_SHARED");   // tuning override: 0 keeps them apart
+    p.merged = d->F_shared > 0 && d->F_shared == d->F && d->act == MOE_ACT_SWIGLU &&
+               d->dtype == MOE_DTYPE_BF16 && d->T <= kSmallT && d->M + 1 <= 1024 &&
+               !(menv && atoi(menv) == 0);
+    const int64_t groups = d->M + (p.merged ? 1 : 0);
+    p.Sx = p.S + (p.merged ? d->T : 0);
+    p.bm_up = gemm_block_m(d->dtype, p.Sx, groups, false, G * d->F);
+    p.bm_dn = gemm_block_m(d->dtype, p.Sx, groups, true, d->D);
     p.bm_sh_up = gemm_block_m(d->dtype, d->T, 1, false, 2 * d->F_shared);
     p.bm_sh_dn = gemm_block_m(d->dtype, d->T, 1, true, d->D);
-    // ceil(S / bm) tiles plus at most one partial tile per non-empty expert
-    const int64_t partial = d->M < p.S ? d->M : p.S;
-    p.max_tiles_up = (p.S + p.bm_up - 1) / p.bm_up + partial;
-    p.max_tiles_dn = (p.S + p.bm_dn - 1) / p.bm_dn + partial;
+    // ceil(Sx / bm) tiles plus at most one partial tile per non-empty group
+    const int64_t partial = groups < p.Sx ? groups : p.Sx;
+    p.max_tiles_up = (p.Sx + p.bm_up - 1) / p.bm_up + partial;
+    p.max_tiles_dn = (p.Sx + p.bm_dn - 1) / p.bm_dn + partial;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -68,18 +82,25 @@ Plan make_plan(const moe_desc* d) {
     p.idx = take(p.S * 4);
     p.w = take(p.S * 4);
     p.counts = take(d->M * 4);
-    p.offsets = take((d->M + 1) * 4);
-    p.sorted_token = take(p.S * 4);
+    p.offsets = take((d->M + 2) * 4);
+    p.sorted_token = take(p.Sx * 4);
     p.sorted_slot = take(p.S * 4);
     p.slot_row = take(p.S * 4);
     p.hist = take((size_t)p.nblk * d->M * 4);
-    p.row_scale = take(p.S * 4);
+    p.row_scale = take(p.Sx * 4);
     p.tiles_up = take(((size_t)p.max_tiles_up * 2 + 1) * 4);
     p.tiles_dn = p.bm_dn == p.bm_up ? p.tiles_up : take(((size_t)p.max_tiles_dn * 2 + 1) * 4);
-    p.H = take((size_t)p.S * d->F * p.esz);
-    p.O = take((size_t)p.S * d->D * 4);
-    p.Hsh = take((size_t)d->T * d->F_shared * p.esz);
-    p.Ysh = take(d->F_shared > 0 ? (size_t)d->T * d->D * 4 : 0);
+    if (p.merged) {
+        p.H = take((size_t)p.Sx * d->F * p.esz);
+        p.Hsh = p.H + (size_t)p.S * d->F * p.esz;
+        p.O = take((size_t)p.Sx * d->D * 4);
+        p.Ysh = p.O + (size_t)p.S * d->D * 4;
+    } else {
+        p.H = take((size_t)p.S * d->F * p.esz);
+        p.O = take((size_t)p.S * d->D * 4);
+        p.Hsh = take((size_t)d->T * d->F_shared * p.esz);
+        p.Ysh = take(d->F_shared > 0 ? (size_t)d->T * d->D * 4 : 0);
+    }
     p.route = take(route_workspace(d->dtype, d->T, d->D, d->M));
     p.total = off;
     return p;
@@ -263,10 +284,17 @@ int do_permute(moe_handle* h, const moe_desc* d, const Plan& p, const int32_t* i
     });
 }
 
+// The routed expert GEMMs.  With Wsh_gu / Wsh_dn non-null (a merged plan,
+// from moe_forward only, whose sorted_token and offsets live in the
+// workspace with room for the extra group) the shared expert runs as group
+// M of the same launches, its T rows after the S routed ones.
 int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x,
-                  const int32_t* sorted_token, const int32_t* sorted_slot, const int32_t* offsets,
+                  int32_t* sorted_token, const int32_t* sorted_slot, int32_t* offsets,
                   const float* w, const void* W1, const void* b1, const void* W2, const void* b2,
-                  float* O, void* ws, hipStream_t s) {
+                  float* O, void* ws, hipStream_t s, const void* Wsh_gu = nullptr,
+                  const void* Wsh_dn = nullptr) {
+    const bool merged = Wsh_gu != nullptr;
+    const int64_t rows = merged ? p.Sx : p.S;
     int32_t* tiles_up = at<int32_t>(ws, p.tiles_up);
     int32_t* tiles_dn = at<int32_t>(ws, p.tiles_dn);
     void* H = at<char>(ws, p.H);
@@ -276,7 +304,8 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     const int ntables = tiles_dn == tiles_up ? 1 : 2;
     float* row_scale = at<float>(ws, p.row_scale);
     TRY(run(h, s, L_TILE_TABLE, [&] {
-        return launch_tile_table(s, offsets, d->M, tt, ntables, sorted_slot, w, p.S, row_scale);
+        return launch_tile_table(s, offsets, d->M, tt, ntables, sorted_slot, w, p.S, row_scale,
+                                 merged ? d->T : 0, sorted_token);
     }));
     const bool swiglu = d->act == MOE_ACT_SWIGLU;
     GemmArgs up{};
@@ -289,8 +318,12 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     up.bias = swiglu ? nullptr : b1;
     up.c = H;
     up.tiles = tiles_up;
-    up.dense_rows = p.S;
-    up.group_m = gemm_group_m(p.S, d->M, p.bm_up);
+    up.dense_rows = rows;
+    up.group_m = gemm_group_m(rows, d->M, p.bm_up);
+    if (merged) {
+        up.b_extra = Wsh_gu;
+        up.extra_group = (int)d->M;
+    }
     up.xcd_mode = gemm_xcd_mode(true, false);
     up.offsets = offsets;
     up.a_rows = d->T;
@@ -309,13 +342,17 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     dn.b_tiled = tiled;
     dn.bias = swiglu ? nullptr : b2;
     dn.row_w = row_scale;
-    dn.dense_rows = p.S;
+    dn.dense_rows = rows;
     dn.c = O;
     dn.tiles = tiles_dn;
-    dn.group_m = gemm_group_m(p.S, d->M, p.bm_dn);
+    dn.group_m = gemm_group_m(rows, d->M, p.bm_dn);
+    if (merged) {
+        dn.b_extra = Wsh_dn;
+        dn.extra_group = (int)d->M;
+    }
     dn.xcd_mode = gemm_xcd_mode(true, true);
     dn.offsets = offsets;
-    dn.a_rows = p.S;
+    dn.a_rows = rows;
     dn.b_rows = (int)d->D;
     dn.K = (int)d->F;
     dn.N = (int)d->D;
@@ -490,7 +527,9 @@ int moe_expert_ffn(moe_handle* h, const moe_desc* d, const void* x, const int32_
     TRY(check_ws(p, ws, ws_bytes));
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
-    return do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O, ws,
+    // not merged: nothing is written through these two
+    return do_expert_ffn(h, d, p, x, const_cast<int32_t*>(sorted_token), sorted_slot,
+                         const_cast<int32_t*>(offsets), w, W1, b1, W2, b2, O, ws,
                          static_cast<hipStream_t>(stream));
 }
 
@@ -594,12 +633,15 @@ int moe_forward(moe_handle* h, const moe_desc* d, const void* x, const float* W_
     float* O = at<float>(ws, p.O);
     float* Ysh = d->F_shared > 0 ? at<float>(ws, p.Ysh) : nullptr;
 
-    const bool fork = Ysh && aux && aux != s;
-    const char* fenv = getenv("MOE_FORK_AT");
-    const int fork_at = fenv ? atoi(fenv) : 0;
-    if (fork_at >= 1) TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
-    if (fork_at >= 2)
+    if (p.merged) {
+        // the shared expert is group M of the routed GEMMs; Ysh is O's tail
+        TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
         TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
+        TRY(do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O,
+                          ws, s, Wsh_gu, Wsh_dn));
+        return do_combine(h, d, O, slot_row, Ysh, y, s);
+    }
+    const bool fork = Ysh && aux && aux != s;
     if (Ysh) {
         if (fork) {
             hipError_t e;
@@ -613,9 +655,8 @@ int moe_forward(moe_handle* h, const moe_desc* d, const void* x, const float* W_
             TRY(do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, s));
         }
     }
-    if (fork_at < 1) TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
-    if (fork_at < 2)
-        TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
+    TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
+    TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
     TRY(do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O, ws, s));
     if (fork) {
         const hipError_t e = hipStreamWaitEvent(s, h->ev_join, 0);

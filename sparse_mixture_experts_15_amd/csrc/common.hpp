@@ -90,6 +90,8 @@ struct GemmArgs {
     int b_tiled;              // b holds tiled blocks (bf16): b_stride = one expert's blocks
     int xcd_mode;             // workgroup order: 0 groups dealt to XCDs in turn, 1 plain,
                               // 2 contiguous slices per XCD
+    const void* b_extra;      // grouped: weights of group extra_group, in place of
+    int extra_group;          // b + extra_group * b_stride (NULL: none)
 };
 
 // Weight tiles of the bf16 GEMM: 256 weight rows by K stages of 64.
@@ -140,10 +142,13 @@ struct TileTables {
     int32_t* tiles[2];
 };
 // The tile tables, plus row_scale[r] = w[sorted_slot[r]] (0 for an unused
-// row) for the S sorted rows, in one launch.
-hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M,
-                             const TileTables& tt, int count, const int32_t* sorted_slot,
-                             const float* w, int64_t S, float* row_scale);
+// row) for the S sorted rows, in one launch.  With extra > 0 the tables get
+// one more group, index M, of `extra` rows starting at offsets[M] (= S):
+// the kernel writes offsets[M + 1] = offsets[M] + extra, and for those rows
+// row_scale = 1 and sorted_token[S + t] = t (every token once, in order).
+hipError_t launch_tile_table(hipStream_t s, int32_t* offsets, int64_t M, const TileTables& tt,
+                             int count, const int32_t* sorted_slot, const float* w, int64_t S,
+                             float* row_scale, int64_t extra, int32_t* sorted_token);
 // Count, scan and scatter in one workgroup for T <= kSmallT tokens.
 constexpr int64_t kSmallT = 1024;
 hipError_t launch_perm_small(hipStream_t s, const int32_t* idx, int64_t T, int k, int64_t M,

@@ -154,15 +154,18 @@ __device__ __forceinline__ int swz(int row, int c) {
 // XCDs in turn; mode 0 deals whole groups to the XCDs in turn as well (XCD
 // x runs groups x, x + 8, ...), which keeps each group on one XCD and
 // spreads the groups of a grouped GEMM, whose cost varies with the rows
-// its experts received, evenly over the XCDs.  Mode 2 gives each XCD one
-// contiguous eighth of the tiles, mode 1 keeps the hardware order.  Ids
-// past the valid tiles return false.  `m_tiles` is the number of valid
-// m-tiles; the grid holds grid_tiles() ids.
+// its experts received, evenly over the XCDs; with fewer than 64 groups
+// (fewer than 8 per XCD, e.g. a decode batch's few dozen experts) whole
+// groups cannot be spread evenly, and mode 0 falls back to the hardware
+// order.  Mode 2 gives each XCD one contiguous eighth of the tiles, mode 1
+// keeps the hardware order.  Ids past the valid tiles return false.
+// `m_tiles` is the number of valid m-tiles; the grid holds grid_tiles() ids.
 __device__ __forceinline__ bool tile_coords(int m_tiles, int n_tiles, int group_m, int p, int& mt,
                                             int& nt, int mode = 0) {
     const int G = m_tiles * n_tiles;
     const int gsz = group_m * n_tiles;
     int first, in;
+    if (mode == 0 && (m_tiles + group_m - 1) / group_m < 64) mode = 1;
     if (mode == 0) {
         const int x = p & 7, i = p >> 3;
         const int grp = x + 8 * (i / gsz);
@@ -236,7 +239,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     // buffer descriptors: A rows (whole activation matrix), B = this expert
     const int64_t a_rows = g.gather ? g.a_rows : tl.rend;
     const i32x4 ra = make_rsrc(g.a, (uint32_t)(a_rows * K * 2));
-    const bf16_t* Bp = static_cast<const bf16_t*>(g.b) + (int64_t)tl.e * g.b_stride;
+    const bf16_t* Bp = (g.b_extra && tl.e == g.extra_group)
+                           ? static_cast<const bf16_t*>(g.b_extra)
+                           : static_cast<const bf16_t*>(g.b) + (int64_t)tl.e * g.b_stride;
     const i32x4 rb = make_rsrc(Bp, (uint32_t)((g.b_tiled ? g.b_stride : (int64_t)g.b_rows * K) * 2));
     // tiled weights: stage kt of a 256-row weight tile is one contiguous
     // block of 256 LDS-image rows; a 128-row n-tile takes half of one
@@ -457,7 +462,9 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs g) {
     const int out_per_tile = (EPI == EPI_SWIGLU) ? FBN / 2 : FBN;
     const int n_base = blockIdx.x * out_per_tile;
     const float* A = static_cast<const float*>(g.a);
-    const float* B = static_cast<const float*>(g.b) + (int64_t)tl.e * g.b_stride;
+    const float* B = (g.b_extra && tl.e == g.extra_group)
+                         ? static_cast<const float*>(g.b_extra)
+                         : static_cast<const float*>(g.b) + (int64_t)tl.e * g.b_stride;
 
     float acc[4][4] = {};
     for (int k0 = 0; k0 < K; k0 += FBK) {

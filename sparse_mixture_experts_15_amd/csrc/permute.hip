@@ -225,30 +225,40 @@ __global__ __launch_bounds__(kScanThreads) void perm_small(const int32_t* __rest
 // thread per expert writes its own tiles after a scan of the tile counts.
 // Workgroup y builds table y (the up and down projections may use different
 // tile heights).
-__global__ __launch_bounds__(kScanThreads) void tile_table(const int32_t* __restrict__ offsets,
-                                                          int M, TileTables tt,
+__global__ __launch_bounds__(kScanThreads) void tile_table(int32_t* __restrict__ offsets, int M,
+                                                          TileTables tt,
                                                           const int32_t* __restrict__ sorted_slot,
                                                           const float* __restrict__ w, int64_t S,
-                                                          float* __restrict__ row_scale) {
+                                                          float* __restrict__ row_scale,
+                                                          int64_t extra,
+                                                          int32_t* __restrict__ sorted_token) {
     __shared__ int32_t s_warp[kScanThreads / 64];
     if (blockIdx.x > 0) {
         // blocks 1.. of row y = 0: the down projection's row scales,
-        // row_scale[r] = w[sorted_slot[r]] (gate weight of each sorted row)
+        // row_scale[r] = w[sorted_slot[r]] (gate weight of each sorted row),
+        // and the extra group's rows: every token once, scale 1
         if (blockIdx.y != 0) return;
         const int64_t r = (int64_t)(blockIdx.x - 1) * kScanThreads + threadIdx.x;
         if (r < S) {
             const int32_t f = sorted_slot[r];
             row_scale[r] = f >= 0 ? w[f] : 0.f;
+        } else if (r < S + extra) {
+            row_scale[r] = 1.f;
+            sorted_token[r] = (int32_t)(r - S);
         }
         return;
     }
+    // the extra group (index M) ends `extra` rows after the last expert's
+    const int Mg = extra > 0 ? M + 1 : M;
     const int bm = tt.bm[blockIdx.y], max_tiles = tt.max_tiles[blockIdx.y];
     int32_t* __restrict__ tiles = tt.tiles[blockIdx.y];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int32_t nt = 0, r0 = 0;
-    if (tid < M) {
+    if (tid < Mg) {
         r0 = offsets[tid];
-        nt = (offsets[tid + 1] - r0 + bm - 1) / bm;
+        const int32_t end = tid == M ? r0 + (int32_t)extra : offsets[tid + 1];
+        nt = (end - r0 + bm - 1) / bm;
+        if (tid == M && blockIdx.y == 0) offsets[M + 1] = end;
     }
     int32_t incl = nt;
 #pragma unroll
@@ -303,12 +313,13 @@ hipError_t launch_perm_scatter(hipStream_t s, const int32_t* idx, const int32_t*
     return hipGetLastError();
 }
 
-hipError_t launch_tile_table(hipStream_t s, const int32_t* offsets, int64_t M,
-                             const TileTables& tt, int count, const int32_t* sorted_slot,
-                             const float* w, int64_t S, float* row_scale) {
-    const unsigned rs_blocks = (unsigned)((S + kScanThreads - 1) / kScanThreads);
+hipError_t launch_tile_table(hipStream_t s, int32_t* offsets, int64_t M, const TileTables& tt,
+                             int count, const int32_t* sorted_slot, const float* w, int64_t S,
+                             float* row_scale, int64_t extra, int32_t* sorted_token) {
+    if (M + (extra > 0 ? 1 : 0) > kScanThreads) return hipErrorInvalidValue;
+    const unsigned rs_blocks = (unsigned)((S + extra + kScanThreads - 1) / kScanThreads);
     hipLaunchKernelGGL(tile_table, dim3(1 + rs_blocks, count), dim3(kScanThreads), 0, s, offsets,
-                       (int)M, tt, sorted_slot, w, S, row_scale);
+                       (int)M, tt, sorted_slot, w, S, row_scale, extra, sorted_token);
     return hipGetLastError();
 }
 

@@ -141,7 +141,7 @@ def test_stage_parity_fp32_output(name):
     _stage_parity(PARITY[name], out_dtype="f32")
 
 
-@pytest.mark.parametrize("name", ["glm45_small", "tiny_fp32", "glam_tiles"])
+@pytest.mark.parametrize("name", ["glm45_small", "tiny_fp32", "glam_tiles", "decode_small"])
 def test_forward_deterministic_and_stream_invariant(name):
     cfg = PARITY[name]
     t = workloads.generate(cfg, seed=1, device="cuda")
