@@ -47,8 +47,9 @@ def log(*a):
 # only for the GEMM source it was measured on (hash of gemm.hip and
 # common.hpp); any change to them reports null until it is measured again.
 TRAFFIC = {
-    ("glam_t4096_d4096_m64_f16384", "ffn_up"): (9043530453, "d976610fefb6e3a0"),
-    ("glam_t4096_d4096_m64_f16384", "ffn_down"): (9070372575, "d976610fefb6e3a0"),
+    ("glam_t4096_d4096_m64_f16384", "ffn_up"): (9411289894, "4ffd2786eeca6609"),
+    ("glam_t4096_d4096_m64_f16384", "ffn_down"): (8999882483, "4ffd2786eeca6609"),
+    ("glm45_decode_t64_d5120_m160_f1536", "ffn_up"): (1575522672, "4ffd2786eeca6609"),
 }
 
 
