@@ -1,4 +1,4 @@
-"""CPU oracle for the sparse MoE feed-forward layer forward pass.
+"""CPU oracle for the sparse MoE feed-forward layer: forward pass and gradient.
 
 TEST INFRASTRUCTURE ONLY.  The plain fp64 definition of the layer lives in
 ``moe_oracle.c`` (one token at a time, OpenMP across tokens); this module
@@ -73,9 +73,11 @@ def _load():
                                      vp, vp, vp]
         lib.oracle_forward.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp,
                                        vp, vp, vp]
+        lib.oracle_backward.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_num_threads.restype = ctypes.c_int
         for f in ("oracle_route", "oracle_dispatch", "oracle_expert", "oracle_shared",
-                  "oracle_layer", "oracle_forward"):
+                  "oracle_layer", "oracle_forward", "oracle_backward"):
             getattr(lib, f).restype = None
         _lib = lib
     return _lib
@@ -228,6 +230,39 @@ def forward(cfg, h, tokens=None):
                            _ptr(h["W2"]), _ptr(h.get("b2")), _ptr(h.get("Wsh_gu")),
                            _ptr(h.get("Wsh_dn")), n, _ptr(tok), _ptr(idx), _ptr(w), _ptr(y))
     return idx, w, y
+
+
+def backward(cfg, h, dy):
+    """Gradient of forward() over all T tokens for the output gradient
+    dy[T,D] (any float array, used in fp64).  Returns a dict of fp64 arrays:
+    dx[T,D], dW_r[M,D], dW1 / dW2 (and db1 / db2 when the layer has biases,
+    dWsh_gu / dWsh_dn when it has a shared expert) in their weights' shapes,
+    and the load statistics load_count[M] (int64 slots per expert) and
+    load_score[M] (sum over tokens of each expert's gate value)."""
+    c = make_cfg(cfg)
+    _check_storage(c, x=h["x"], W1=h["W1"], b1=h.get("b1"), W2=h["W2"], b2=h.get("b2"),
+                   Wsh_gu=h.get("Wsh_gu"), Wsh_dn=h.get("Wsh_dn"))
+    T, D, M, F, Fs = cfg.T, cfg.D, cfg.M, cfg.F, cfg.F_shared
+    G = 2 if cfg.act == "swiglu" else 1
+    dy = np.ascontiguousarray(dy, dtype=np.float64).reshape(T, D)
+    out = {"dx": np.zeros((T, D)), "dW_r": np.zeros((M, D)),
+           "dW1": np.zeros((M, G * F, D)), "dW2": np.zeros((M, D, F)),
+           "load_count": np.zeros(M, np.int64), "load_score": np.zeros(M)}
+    if h.get("b1") is not None:
+        out["db1"] = np.zeros((M, F))
+    if h.get("b2") is not None:
+        out["db2"] = np.zeros((M, D))
+    if Fs > 0:
+        out["dWsh_gu"] = np.zeros((2 * Fs, D))
+        out["dWsh_dn"] = np.zeros((D, Fs))
+    _load().oracle_backward(
+        ctypes.byref(c), _ptr(h["x"]), _ptr(_f32(h["W_r"])), _ptr(_f32(h.get("bias"))),
+        _ptr(h["W1"]), _ptr(h.get("b1")), _ptr(h["W2"]), _ptr(h.get("b2")),
+        _ptr(h.get("Wsh_gu")), _ptr(h.get("Wsh_dn")), _ptr(dy), _ptr(out["dx"]),
+        _ptr(out["dW_r"]), _ptr(out["dW1"]), _ptr(out.get("db1")), _ptr(out["dW2"]),
+        _ptr(out.get("db2")), _ptr(out.get("dWsh_gu")), _ptr(out.get("dWsh_dn")),
+        _ptr(out["load_count"]), _ptr(out["load_score"]))
+    return out
 
 
 # ---- parameter accounting ("Parameters" table, GLM-5 shared expert page) ----

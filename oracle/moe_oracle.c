@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the sparse MoE feed-forward layer forward pass.
+ * CPU oracle for the sparse MoE feed-forward layer: forward pass and its
+ * gradient.
  *
  * TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the harness's
  * CPU-baseline leg call this; the HIP library never does and shares no code
@@ -406,4 +407,241 @@ void oracle_forward(const moe_oracle_cfg* c, const void* x, const float* W_r,
         layer_token(c, x, idx + i * k, w + i * k, W1, b1, W2, b2, Wsh_gu, Wsh_dn,
                     tokens[i], y + i * D, NULL, NULL);
     }
+}
+
+/* ------------------------------------------------------------------ backward
+ *
+ * Gradient of the forward pass above for an output gradient dy[T,D], by the
+ * chain rule through each step of its definition, one token at a time.
+ * The selection (top-k, and the correction bias, which only enters the
+ * selection) is piecewise constant and passes no gradient; the weights w
+ * pass it to the gate values g (softmax probabilities or sigmoid scores)
+ * and on to the router logits.  The training objective that produces dy is
+ * the GLaM study note's causal LM loss ("training objective"); the pages give
+ * no other training term for the layer.
+ */
+
+static double silu_grad(double z)
+{
+    double s = sigmoid(z);
+    return s * (1.0 + z * (1.0 - s));
+}
+
+/* d/dz of z Phi(z) = Phi(z) + z phi(z). */
+static double gelu_erf_grad(double z)
+{
+    double Phi = 0.5 * (1.0 + erf(z / sqrt(2.0)));
+    double phi = exp(-0.5 * z * z) / sqrt(2.0 * 3.14159265358979323846);
+    return Phi + z * phi;
+}
+
+static void add_outer(double* G, int64_t g0, int64_t rows, int64_t cols, const double* a,
+                      const double* b)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t q = 0; q < cols; ++q)
+            G[g0 + r * cols + q] += a[r] * b[q];
+}
+
+/* SwiGLU of width Fw on xv with output gradient dout: accumulates the weight
+ * gradients (same layouts as Wgu / Wdn, at offsets gu0 / dn0) and dx; returns
+ * the forward output in out. */
+static void swiglu_backward(int32_t dtype, int64_t D, int64_t Fw, const void* Wgu, int64_t gu0,
+                            const void* Wdn, int64_t dn0, const double* xv, const double* dout,
+                            double* out, double* dWgu, double* dWdn, double* dx)
+{
+    double* a = malloc(sizeof(double) * Fw);
+    double* b = malloc(sizeof(double) * Fw);
+    double* h = malloc(sizeof(double) * Fw);
+    double* dh = malloc(sizeof(double) * Fw);
+    double* da = malloc(sizeof(double) * Fw);
+    double* db = malloc(sizeof(double) * Fw);
+    for (int64_t f = 0; f < Fw; ++f) {
+        a[f] = dot(Wgu, dtype, gu0 + f * D, D, xv);
+        b[f] = dot(Wgu, dtype, gu0 + (Fw + f) * D, D, xv);
+        h[f] = silu(a[f]) * b[f];
+    }
+    for (int64_t d = 0; d < D; ++d)
+        out[d] = dot(Wdn, dtype, dn0 + d * Fw, Fw, h);
+    /* dh = Wdn^T dout; dWdn += dout h^T */
+    for (int64_t f = 0; f < Fw; ++f) {
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            acc += elem(Wdn, dtype, dn0 + d * Fw + f) * dout[d];
+        dh[f] = acc;
+    }
+    if (dWdn)
+        add_outer(dWdn, dn0, D, Fw, dout, h);
+    for (int64_t f = 0; f < Fw; ++f) {
+        da[f] = dh[f] * b[f] * silu_grad(a[f]);
+        db[f] = dh[f] * silu(a[f]);
+    }
+    if (dWgu) {
+        add_outer(dWgu, gu0, Fw, D, da, xv);
+        add_outer(dWgu, gu0 + Fw * D, Fw, D, db, xv);
+    }
+    for (int64_t f = 0; f < Fw; ++f)
+        for (int64_t d = 0; d < D; ++d)
+            dx[d] += elem(Wgu, dtype, gu0 + f * D + d) * da[f] +
+                     elem(Wgu, dtype, gu0 + (Fw + f) * D + d) * db[f];
+    free(a); free(b); free(h); free(dh); free(da); free(db);
+}
+
+/* GELU FFN W2 gelu(W1 x + b1) + b2 with output gradient dout (a null bias is
+ * zero and gets no gradient). */
+static void gelu_backward(int32_t dtype, int64_t D, int64_t Fw, const void* W1, int64_t w10,
+                          const void* b1, int64_t b10, const void* W2, int64_t w20,
+                          const void* b2, int64_t b20, const double* xv, const double* dout,
+                          double* out, double* dW1, double* db1, double* dW2, double* db2,
+                          double* dx)
+{
+    double* z = malloc(sizeof(double) * Fw);
+    double* h = malloc(sizeof(double) * Fw);
+    double* dz = malloc(sizeof(double) * Fw);
+    for (int64_t f = 0; f < Fw; ++f) {
+        z[f] = dot(W1, dtype, w10 + f * D, D, xv) + (b1 ? elem(b1, dtype, b10 + f) : 0.0);
+        h[f] = gelu_erf(z[f]);
+    }
+    for (int64_t d = 0; d < D; ++d)
+        out[d] = dot(W2, dtype, w20 + d * Fw, Fw, h) + (b2 ? elem(b2, dtype, b20 + d) : 0.0);
+    for (int64_t f = 0; f < Fw; ++f) {
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            acc += elem(W2, dtype, w20 + d * Fw + f) * dout[d];
+        dz[f] = acc * gelu_erf_grad(z[f]);
+    }
+    add_outer(dW2, w20, D, Fw, dout, h);
+    if (b2)
+        for (int64_t d = 0; d < D; ++d)
+            db2[b20 + d] += dout[d];
+    add_outer(dW1, w10, Fw, D, dz, xv);
+    if (b1)
+        for (int64_t f = 0; f < Fw; ++f)
+            db1[b10 + f] += dz[f];
+    for (int64_t f = 0; f < Fw; ++f)
+        for (int64_t d = 0; d < D; ++d)
+            dx[d] += elem(W1, dtype, w10 + f * D + d) * dz[f];
+    free(z); free(h); free(dz);
+}
+
+void oracle_backward(const moe_oracle_cfg* c, const void* x, const float* W_r,
+                     const float* bias, const void* W1, const void* b1, const void* W2,
+                     const void* b2, const void* Wsh_gu, const void* Wsh_dn, const double* dy,
+                     double* dx, double* dW_r, double* dW1, double* db1, double* dW2,
+                     double* db2, double* dWsh_gu, double* dWsh_dn, int64_t* load_count,
+                     double* load_score)
+{
+    const int64_t T = c->T, D = c->D, M = c->M, F = c->F, Fs = c->F_shared;
+    const int32_t k = c->k;
+    const int64_t G = c->act == ORACLE_SWIGLU ? 2 : 1;
+    memset(dx, 0, sizeof(double) * T * D);
+    memset(dW_r, 0, sizeof(double) * M * D);
+    memset(dW1, 0, sizeof(double) * M * G * F * D);
+    memset(dW2, 0, sizeof(double) * M * D * F);
+    if (db1) memset(db1, 0, sizeof(double) * M * F);
+    if (db2) memset(db2, 0, sizeof(double) * M * D);
+    if (Fs > 0) {
+        memset(dWsh_gu, 0, sizeof(double) * 2 * Fs * D);
+        memset(dWsh_dn, 0, sizeof(double) * D * Fs);
+    }
+    memset(load_count, 0, sizeof(int64_t) * M);
+    memset(load_score, 0, sizeof(double) * M);
+
+    double* xv = malloc(sizeof(double) * D);
+    double* l = malloc(sizeof(double) * M);
+    double* g = malloc(sizeof(double) * M);
+    double* dg = malloc(sizeof(double) * M);
+    double* dl = malloc(sizeof(double) * M);
+    double* o = malloc(sizeof(double) * D);
+    double* dout = malloc(sizeof(double) * D);
+    int32_t* idx = malloc(sizeof(int32_t) * k);
+    double* w = malloc(sizeof(double) * k);
+    double* dw = malloc(sizeof(double) * k);
+
+    for (int64_t t = 0; t < T; ++t) {
+        double gap;
+        route_token(c, x, W_r, bias, t, idx, w, &gap, l, NULL);
+        load_row(c, x, t, xv);
+        const double* dyt = dy + t * D;
+        double* dxt = dx + t * D;
+        /* gate values g over all experts, as in the router */
+        if (c->scorer == ORACLE_SOFTMAX) {
+            double mx = l[0], Z = 0.0;
+            for (int64_t e = 1; e < M; ++e)
+                if (l[e] > mx) mx = l[e];
+            for (int64_t e = 0; e < M; ++e)
+                Z += exp(l[e] - mx);
+            for (int64_t e = 0; e < M; ++e)
+                g[e] = exp(l[e] - mx) / Z;
+        } else {
+            for (int64_t e = 0; e < M; ++e)
+                g[e] = sigmoid(l[e]);
+        }
+        for (int64_t e = 0; e < M; ++e)
+            load_score[e] += g[e];
+
+        /* routed experts: dw_j = dy . E_j(x); the expert sees w_j dy */
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t e = idx[j];
+            dw[j] = 0.0;
+            if (e < 0 || e >= M)
+                continue;
+            load_count[e] += 1;
+            for (int64_t d = 0; d < D; ++d)
+                dout[d] = w[j] * dyt[d];
+            if (c->act == ORACLE_SWIGLU)
+                swiglu_backward(c->dtype, D, F, W1, e * 2 * F * D, W2, e * D * F, xv, dout, o,
+                                dW1, dW2, dxt);
+            else
+                gelu_backward(c->dtype, D, F, W1, e * F * D, b1, e * F, W2, e * D * F, b2,
+                              e * D, xv, dout, o, dW1, db1, dW2, db2, dxt);
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                acc += dyt[d] * o[d];
+            dw[j] = acc;
+        }
+        /* shared expert, weight 1 */
+        if (Fs > 0)
+            swiglu_backward(c->dtype, D, Fs, Wsh_gu, 0, Wsh_dn, 0, xv, dyt, o, dWsh_gu,
+                            dWsh_dn, dxt);
+
+        /* weights -> gate values: w_j = alpha g_j / (sum_S g + eps), or alpha g_j */
+        for (int64_t e = 0; e < M; ++e)
+            dg[e] = 0.0;
+        if (c->renorm) {
+            double Gs = 0.0, s = 0.0;
+            for (int32_t j = 0; j < k; ++j)
+                if (idx[j] >= 0 && idx[j] < M)
+                    Gs += g[idx[j]];
+            const double den = Gs + c->eps;
+            for (int32_t j = 0; j < k; ++j)
+                if (idx[j] >= 0 && idx[j] < M)
+                    s += dw[j] * g[idx[j]];
+            for (int32_t j = 0; j < k; ++j)
+                if (idx[j] >= 0 && idx[j] < M)
+                    dg[idx[j]] = c->alpha * (dw[j] / den - s / (den * den));
+        } else {
+            for (int32_t j = 0; j < k; ++j)
+                if (idx[j] >= 0 && idx[j] < M)
+                    dg[idx[j]] = c->alpha * dw[j];
+        }
+        /* gate values -> logits */
+        if (c->scorer == ORACLE_SOFTMAX) {
+            double s = 0.0;
+            for (int64_t e = 0; e < M; ++e)
+                s += dg[e] * g[e];
+            for (int64_t e = 0; e < M; ++e)
+                dl[e] = g[e] * (dg[e] - s);
+        } else {
+            for (int64_t e = 0; e < M; ++e)
+                dl[e] = dg[e] * g[e] * (1.0 - g[e]);
+        }
+        /* logits l = W_r x: dW_r += dl x^T, dx += W_r^T dl */
+        add_outer(dW_r, 0, M, D, dl, xv);
+        for (int64_t e = 0; e < M; ++e)
+            for (int64_t d = 0; d < D; ++d)
+                dxt[d] += (double)W_r[e * D + d] * dl[e];
+    }
+    free(xv); free(l); free(g); free(dg); free(dl); free(o); free(dout); free(idx);
+    free(w); free(dw);
 }

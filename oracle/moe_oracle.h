@@ -85,6 +85,22 @@ void oracle_forward(const moe_oracle_cfg* c, const void* x, const float* W_r,
                     const void* Wsh_dn, int64_t ntok, const int64_t* tokens,
                     int32_t* idx, double* w, double* y);
 
+/* Gradient of oracle_forward over all T tokens for the output gradient
+ * dy[T,D] (fp64): dx[T,D]; dW_r[M,D]; dW1, db1, dW2, db2 and dWsh_gu, dWsh_dn
+ * in the layouts of the weights they belong to (db1 / db2 nullable: no
+ * biases; the shared ones only written when F_shared > 0).  The top-k
+ * selection and the correction bias pass no gradient (piecewise constant);
+ * the weights pass it through the renormalisation and the gate values to the
+ * logits.  Per-expert load statistics of the same pass: load_count[e] slots
+ * routed to e, load_score[e] the sum over tokens of e's gate value (softmax
+ * probability or sigmoid score).  Single-threaded, for small shapes. */
+void oracle_backward(const moe_oracle_cfg* c, const void* x, const float* W_r,
+                     const float* bias, const void* W1, const void* b1, const void* W2,
+                     const void* b2, const void* Wsh_gu, const void* Wsh_dn, const double* dy,
+                     double* dx, double* dW_r, double* dW1, double* db1, double* dW2,
+                     double* db2, double* dWsh_gu, double* dWsh_dn, int64_t* load_count,
+                     double* load_score);
+
 /* Number of OpenMP threads the oracle will use. */
 int oracle_num_threads(void);
 

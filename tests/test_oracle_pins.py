@@ -453,3 +453,119 @@ def test_gelu_is_the_erf_form():
         y = oracle.expert(cfg, h["x"], 0, 0, h["W1"], None, h["W2"], None)
         zf = float(np.float32(z))            # the weight is stored in fp32
         assert y[0] == pytest.approx(zf * special.ndtr(zf), abs=1e-15)
+
+
+# ------------------------------------------------------------- the gradient
+#
+# The backward is pinned to the forward definition by central finite
+# differences of L = sum(dy * y): inputs are multiples of 2^-8 and the step
+# is 2^-12, so x +- h is exact in fp32 storage, the forward runs in fp64 and
+# the difference quotient's truncation error (~h^2) is ~1e-7.  Entries whose
+# perturbation changes the top-k selection are skipped (the selection is
+# piecewise constant and passes no gradient).
+
+_FD_H = 2.0 ** -12
+
+
+def _q(rng, shape, std):
+    """fp32 normal draws rounded to multiples of 2^-8 (exact in fp32)."""
+    return (np.round(rng.normal(0.0, std, shape) * 256.0) / 256.0).astype(np.float32)
+
+
+def _fd_case(scorer, act, M, k, T=4, D=6, F=4, Fs=0, renorm=True, alpha=1.0, biases=False,
+             n_group=0, topk_group=0, seed=0):
+    cfg = workloads.MoEConfig(name="fd", T=T, D=D, M=M, F=F, k=k, scorer=scorer, act=act,
+                              F_shared=Fs, dtype="f32", renorm=renorm, alpha=alpha,
+                              n_group=n_group, topk_group=topk_group)
+    rng = np.random.default_rng(seed)
+    G = 2 if act == "swiglu" else 1
+    h = {"x": _q(rng, (T, D), 1.0), "W_r": _q(rng, (M, D), 1.0),
+         "bias": _q(rng, (M,), 0.3) if scorer == "sigmoid" else None,
+         "W1": _q(rng, (M, G * F, D), 0.5), "W2": _q(rng, (M, D, F), 0.5),
+         "b1": _q(rng, (M, F), 0.3) if biases else None,
+         "b2": _q(rng, (M, D), 0.3) if biases else None,
+         "Wsh_gu": _q(rng, (2 * Fs, D), 0.5) if Fs else None,
+         "Wsh_dn": _q(rng, (D, Fs), 0.5) if Fs else None}
+    dy = rng.normal(0.0, 1.0, (T, D))
+    return cfg, h, dy
+
+
+def _loss(cfg, h, dy):
+    idx, _, y = oracle.forward(cfg, h)
+    return float((dy * y).sum()), idx
+
+
+FD_CASES = {
+    "swiglu_sigmoid_shared": dict(scorer="sigmoid", act="swiglu", M=5, k=2, Fs=3, alpha=2.5),
+    "gelu_softmax_biases": dict(scorer="softmax", act="gelu", M=4, k=2, biases=True),
+    "swiglu_sigmoid_norenorm": dict(scorer="sigmoid", act="swiglu", M=4, k=1, renorm=False,
+                                    alpha=1.5),
+    "gelu_softmax_norenorm_k3": dict(scorer="softmax", act="gelu", M=5, k=3, renorm=False),
+    "swiglu_sigmoid_groups": dict(scorer="sigmoid", act="swiglu", M=6, k=2, n_group=3,
+                                  topk_group=2, Fs=2),
+}
+
+
+@pytest.mark.parametrize("name", list(FD_CASES))
+def test_backward_matches_finite_differences(name):
+    cfg, h, dy = _fd_case(**FD_CASES[name])
+    g = oracle.backward(cfg, h, dy)
+    _, idx0 = _loss(cfg, h, dy)
+    names = [("x", "dx"), ("W_r", "dW_r"), ("W1", "dW1"), ("W2", "dW2"), ("b1", "db1"),
+             ("b2", "db2"), ("Wsh_gu", "dWsh_gu"), ("Wsh_dn", "dWsh_dn")]
+    checked = skipped = 0
+    for pname, gname in names:
+        if h.get(pname) is None:
+            assert gname not in g
+            continue
+        a = h[pname]
+        flat = a.reshape(-1)
+        for i in range(flat.size):
+            v = flat[i]
+            flat[i] = v + np.float32(_FD_H)
+            lp, ip = _loss(cfg, h, dy)
+            flat[i] = v - np.float32(_FD_H)
+            lm, im = _loss(cfg, h, dy)
+            flat[i] = v
+            if not (np.array_equal(ip, idx0) and np.array_equal(im, idx0)):
+                skipped += 1
+                continue
+            fd = (lp - lm) / (2 * _FD_H)
+            an = g[gname].reshape(-1)[i]
+            assert abs(fd - an) <= 2e-5 * (1.0 + abs(fd)), (pname, i, fd, an)
+            checked += 1
+    assert checked > 20 * skipped
+
+
+def test_backward_load_statistics():
+    cfg, h, dy = _fd_case(scorer="sigmoid", act="swiglu", M=6, k=2, T=9, Fs=2)
+    g = oracle.backward(cfg, h, dy)
+    idx, _, _, logits = oracle.route(cfg, h["x"], h["W_r"], h["bias"], want_logits=True)
+    assert (g["load_count"] == np.bincount(idx.reshape(-1), minlength=cfg.M)).all()
+    assert g["load_count"].sum() == cfg.T * cfg.k
+    assert np.allclose(g["load_score"], special.expit(logits).sum(axis=0), rtol=1e-13)
+    cfg, h, dy = _fd_case(scorer="softmax", act="gelu", M=5, k=2, T=7)
+    g = oracle.backward(cfg, h, dy)
+    _, _, _, logits = oracle.route(cfg, h["x"], h["W_r"], None, want_logits=True)
+    assert np.allclose(g["load_score"], special.softmax(logits, axis=1).sum(axis=0), rtol=1e-13)
+    assert np.isclose(g["load_score"].sum(), cfg.T, rtol=1e-13)
+
+
+def test_backward_alpha_zero_is_shared_swiglu_only():
+    """alpha = 0 zeroes every routed weight: the routed experts and the
+    router receive no gradient, and dx is a plain SwiGLU's input gradient
+    (numpy matmuls)."""
+    cfg, h, dy = _fd_case(scorer="sigmoid", act="swiglu", M=5, k=2, Fs=3, alpha=0.0, T=5)
+    g = oracle.backward(cfg, h, dy)
+    for key in ("dW1", "dW2", "dW_r"):
+        assert not g[key].any(), key
+    x = h["x"].astype(np.float64)
+    Wg, Wu = h["Wsh_gu"][:3].astype(np.float64), h["Wsh_gu"][3:].astype(np.float64)
+    Wd = h["Wsh_dn"].astype(np.float64)
+    a, b = x @ Wg.T, x @ Wu.T
+    sg = special.expit(a)
+    dh = dy @ Wd
+    da = dh * b * sg * (1 + a * (1 - sg))
+    db = dh * a * sg
+    assert np.allclose(g["dx"], da @ Wg + db @ Wu, rtol=1e-12, atol=1e-12)
+    assert np.allclose(g["dWsh_dn"], dy.T @ (a * sg * b), rtol=1e-12, atol=1e-12)
