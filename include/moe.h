@@ -237,13 +237,41 @@ int moe_forward(moe_handle* h, const moe_desc* d, const void* x, const float* W_
                 const void* b2, const void* Wsh_gu, const void* Wsh_dn, void* y,
                 void* ws, size_t ws_bytes, void* stream, void* aux_stream);
 
+/* Layer backward (training).  Gradient of moe_forward for the output
+ * gradient dy[T,D] (bf16): the chain rule through each step of the forward
+ * definition (GLaM study note, "Sparse MoE Layer": routed sum of gate-
+ * weighted expert FFNs, trained under the causal LM objective; GLM-4.5 note,
+ * "How it works": sigmoid scores, selection-only correction bias,
+ * renormalisation with eps, alpha, shared expert).  The top-k selection and
+ * the correction bias are piecewise constant and get no gradient; the
+ * weights pass it through the renormalisation and the gate values (softmax
+ * probabilities or sigmoid scores) to the router logits.  The routing is
+ * recomputed from x.
+ *
+ * bf16 layers with row-major weights only (MOE_ERR_UNSUPPORTED otherwise).
+ * Outputs, all fp32 and written whole: dx[T,D]; dW_r[M,D]; dW1, dW2, dWsh_gu,
+ * dWsh_dn in their weights' layouts (shared ones only when F_shared > 0);
+ * db1[M,F] and db2[M,D] for GELU experts when non-NULL (ignored for SwiGLU);
+ * load_count[M] (int32 slots routed to each expert) and load_score[M] (sum
+ * over tokens of each expert's gate value), the per-expert load statistics
+ * of this batch.  Workspace: moe_backward_workspace_size() bytes.  T == 0
+ * writes zero gradients.  Deterministic (no atomics). */
+int moe_backward_workspace_size(const moe_desc* d, size_t* bytes);
+int moe_backward(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
+                 const float* bias, const void* W1, const void* b1, const void* W2,
+                 const void* b2, const void* Wsh_gu, const void* Wsh_dn, const void* dy,
+                 float* dx, float* dW_r, float* dW1, float* db1, float* dW2, float* db2,
+                 float* dWsh_gu, float* dWsh_dn, int32_t* load_count, float* load_score,
+                 void* ws, size_t ws_bytes, void* stream);
+
 /* Per-kernel timing for measurement harnesses.  While enabled, every kernel
  * the handle launches whose label contains `filter` (NULL or "" = all) is
  * bracketed by a pair of HIP timing events on the stream it runs on, up to
  * `capacity` launches.  moe_profile_stop() waits for those events and folds
  * them into per-label totals readable with moe_profile_results().  Labels:
  * route, perm_count, perm_scan, perm_scatter, tile_table, ffn_up, ffn_down,
- * shared_up, shared_down, combine. */
+ * shared_up, shared_down, combine, and for the backward b_up, b_dh, b_dx,
+ * b_wgrad, b_transpose, b_other. */
 typedef struct moe_kernel_time {
     char label[32];
     int64_t launches;

@@ -29,7 +29,7 @@ EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_size", "moe_route", "moe_
            "moe_expert_ffn", "moe_shared_expert", "moe_combine", "moe_forward",
            "moe_profile_start", "moe_profile_stop", "moe_profile_results",
            "moe_status_string", "moe_last_error_detail", "moe_tiled_weight_size",
-           "moe_tile_weights")
+           "moe_tile_weights", "moe_backward_workspace_size", "moe_backward")
 
 
 class moe_desc(ctypes.Structure):
@@ -86,6 +86,8 @@ def load_library() -> ctypes.CDLL:
         "moe_tiled_weight_size": [dp, i32, ctypes.POINTER(sz)],
         "moe_tile_weights": [vp, dp, i32, vp, vp, vp],
         "moe_last_error_detail": [],
+        "moe_backward_workspace_size": [dp, ctypes.POINTER(sz)],
+        "moe_backward": [vp, dp] + [vp] * 21 + [sz, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -261,6 +263,53 @@ def moe_forward(h, d, x, W_r, bias, W1, b1, W2, b2, Wsh_gu, Wsh_dn, y, ws, strea
         _ptr(Wsh_dn, "Wsh_dn", dt, _wnumel(d, "Wsh_dn", D * Fs) if Fs else None),
         _ptr(y, "y", _odt(d), T * D), _ptr(ws, "ws", torch.uint8),
         ws.numel() if ws is not None else 0, _stream(stream), aux))
+
+
+def moe_backward_workspace_size(d: moe_desc) -> int:
+    n = ctypes.c_size_t()
+    _check("moe_backward_workspace_size",
+           load_library().moe_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def moe_backward(h, d, x, W_r, bias, W1, b1, W2, b2, Wsh_gu, Wsh_dn, dy, grads, ws,
+                 stream=None):
+    """Layer backward.  `grads` is a dict of preallocated fp32 tensors dx,
+    dW_r, dW1, dW2 (db1, db2 for biased GELU experts; dWsh_gu, dWsh_dn with a
+    shared expert), int32 load_count and fp32 load_score."""
+    T, D, M, F, Fs = d.T, d.D, d.M, d.F, d.F_shared
+    G = 2 if d.act == 0 else 1
+    dt = _dt(d)
+    f32 = torch.float32
+    gr = grads.get
+    _check("moe_backward", load_library().moe_backward(
+        h, ctypes.byref(d), _ptr(x, "x", dt, T * D), _ptr(W_r, "W_r", f32, M * D),
+        _ptr(bias, "bias", f32, M), _ptr(W1, "W1", dt, M * G * F * D),
+        _ptr(b1, "b1", dt, M * F), _ptr(W2, "W2", dt, M * D * F), _ptr(b2, "b2", dt, M * D),
+        _ptr(Wsh_gu, "Wsh_gu", dt, 2 * Fs * D if Fs else None),
+        _ptr(Wsh_dn, "Wsh_dn", dt, D * Fs if Fs else None), _ptr(dy, "dy", dt, T * D),
+        _ptr(gr("dx"), "dx", f32, T * D), _ptr(gr("dW_r"), "dW_r", f32, M * D),
+        _ptr(gr("dW1"), "dW1", f32, M * G * F * D), _ptr(gr("db1"), "db1", f32, M * F),
+        _ptr(gr("dW2"), "dW2", f32, M * D * F), _ptr(gr("db2"), "db2", f32, M * D),
+        _ptr(gr("dWsh_gu"), "dWsh_gu", f32, 2 * Fs * D if Fs else None),
+        _ptr(gr("dWsh_dn"), "dWsh_dn", f32, D * Fs if Fs else None),
+        _ptr(gr("load_count"), "load_count", torch.int32, M),
+        _ptr(gr("load_score"), "load_score", f32, M), _ptr(ws, "ws", torch.uint8),
+        ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def backward_grads(d: moe_desc, device="cuda", biases=False) -> dict:
+    """Empty fp32 gradient tensors for moe_backward in the weights' shapes."""
+    T, D, M, F, Fs = d.T, d.D, d.M, d.F, d.F_shared
+    G = 2 if d.act == 0 else 1
+    e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=device)
+    g = {"dx": e(T, D), "dW_r": e(M, D), "dW1": e(M, G * F, D), "dW2": e(M, D, F),
+         "load_count": torch.empty(M, dtype=torch.int32, device=device), "load_score": e(M)}
+    if biases:
+        g["db1"], g["db2"] = e(M, F), e(M, D)
+    if Fs:
+        g["dWsh_gu"], g["dWsh_dn"] = e(2 * Fs, D), e(D, Fs)
+    return g
 
 
 def moe_profile_start(h, capacity: int, filter: str | None = None):

@@ -20,7 +20,8 @@ LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmoe.so")
 
 ARCH = "gfx950"
-SOURCES = ["abi.cpp", "route.hip", "permute.hip", "gemm.hip", "combine.hip", "tile.hip"]
+SOURCES = ["abi.cpp", "route.hip", "permute.hip", "gemm.hip", "combine.hip", "tile.hip",
+           "backward.hip"]
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1,6 +1,7 @@
 // C ABI of the MoE layer: descriptor validation, workspace plan, stream
 // fork/join and kernel launches.  Every check runs before the first
 // launch, so an error leaves the outputs and the streams untouched.
+#include <algorithm>
 #include <cstdlib>
 #include <hip/hip_runtime.h>
 
@@ -29,9 +30,10 @@ int fail(int code, const char* fmt, ...) {
     return code;
 }
 
-const char* kLabels[L_COUNT] = {"route",     "perm_count", "perm_scan",  "perm_scatter",
+const char* kLabels[L_COUNT] = {"route",      "perm_count", "perm_scan",  "perm_scatter",
                                 "tile_table", "ffn_up",     "ffn_down",   "shared_up",
-                                "shared_down", "combine"};
+                                "shared_down", "combine",   "b_up",       "b_dh",
+                                "b_dx",       "b_wgrad",    "b_transpose", "b_other"};
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -50,7 +52,7 @@ struct Plan {
            total = 0;
 };
 
-Plan make_plan(const moe_desc* d) {
+Plan make_plan(const moe_desc* d, bool allow_merge = true) {
     Plan p;
     p.esz = d->dtype == MOE_DTYPE_BF16 ? 2 : 4;
     p.S = d->T * d->k;
@@ -60,9 +62,9 @@ Plan make_plan(const moe_desc* d) {
     // when the batch is decode-sized: alone its GEMMs have a handful of
     // workgroups and only contend with the router on the second stream.
     const char* menv = getenv("MOE_MERGE_SHARED");   // tuning override: 0 keeps them apart
-    p.merged = d->F_shared > 0 && d->F_shared == d->F && d->act == MOE_ACT_SWIGLU &&
-               d->dtype == MOE_DTYPE_BF16 && d->T <= kSmallT && d->M + 1 <= 1024 &&
-               !(menv && atoi(menv) == 0);
+    p.merged = allow_merge && d->F_shared > 0 && d->F_shared == d->F &&
+               d->act == MOE_ACT_SWIGLU && d->dtype == MOE_DTYPE_BF16 && d->T <= kSmallT &&
+               d->M + 1 <= 1024 && !(menv && atoi(menv) == 0);
     const int64_t groups = d->M + (p.merged ? 1 : 0);
     p.Sx = p.S + (p.merged ? d->T : 0);
     p.bm_up = gemm_block_m(d->dtype, p.Sx, groups, false, G * d->F);
@@ -404,6 +406,348 @@ int do_combine(moe_handle* h, const moe_desc* d, const float* O, const int32_t* 
     });
 }
 
+// ------------------------------------------------------------- backward
+
+// Backward workspace: the forward's (unmerged) layout, with H, O, Hsh and
+// Ysh reused as H, the expert rows' input gradients dXs [S, D] fp32, Hsh and
+// the shared expert's dXsh [T, D] fp32, followed by the backward's own
+// regions.  Spad = S + 64 M, rounded up to 64, bounds the per-expert padded
+// positions.
+struct BwdPlan {
+    Plan f;
+    int64_t S = 0, G = 1, Spad = 0, Tp = 0;
+    int part_ld = 0, bm_w2 = 0, bm_w1 = 0, bm_sh2 = 0, bm_sh1 = 0, bm_r = 0;
+    size_t Z = 0, dZ = 0, part = 0, Zsh = 0, dZsh = 0, W1T = 0, W2T = 0, WshguT = 0,
+           WshdnT = 0, poff = 0, pad_row = 0, pad_tok = 0, dOT = 0, HT = 0, dZT = 0, XT = 0,
+           xT = 0, dyT = 0, HshT = 0, dZshT = 0, dl = 0, gate = 0, dlT3 = 0, C3 = 0, total = 0;
+};
+
+BwdPlan make_bwd_plan(const moe_desc* d) {
+    BwdPlan b;
+    b.f = make_plan(d, false);
+    const int64_t T = d->T, D = d->D, M = d->M, F = d->F, Fs = d->F_shared;
+    b.S = T * d->k;
+    b.G = d->act == MOE_ACT_SWIGLU ? 2 : 1;
+    b.Spad = ((b.S + 64 * M + 63) / 64) * 64;
+    b.Tp = ((T + 63) / 64) * 64;
+    b.part_ld = gemm_part_cols(b.f.bm_up, F);
+    b.bm_w2 = gemm_block_m(MOE_DTYPE_BF16, D, 1, false, F);
+    b.bm_w1 = gemm_block_m(MOE_DTYPE_BF16, b.G * F, 1, false, D);
+    b.bm_sh2 = gemm_block_m(MOE_DTYPE_BF16, D, 1, false, Fs);
+    b.bm_sh1 = gemm_block_m(MOE_DTYPE_BF16, 2 * Fs, 1, false, D);
+    b.bm_r = gemm_block_m(MOE_DTYPE_BF16, 3 * M, 1, false, D);
+    size_t off = b.f.total;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    const size_t GF = b.G * F;
+    b.Z = take(b.S * GF * 2);
+    b.dZ = take(b.S * GF * 2);
+    b.part = take(b.S * b.part_ld * 4);
+    b.Zsh = take(T * 2 * Fs * 2);
+    b.dZsh = take(T * 2 * Fs * 2);
+    b.W1T = take(M * D * GF * 2);
+    b.W2T = take(M * F * D * 2);
+    b.WshguT = take(D * 2 * Fs * 2);
+    b.WshdnT = take(Fs * D * 2);
+    b.poff = take((M + 1) * 4);
+    b.pad_row = take(b.Spad * 4);
+    b.pad_tok = take(b.Spad * 4);
+    b.dOT = take(D * b.Spad * 2);
+    b.HT = take(F * b.Spad * 2);
+    b.dZT = take(GF * b.Spad * 2);
+    b.XT = take(D * b.Spad * 2);
+    b.xT = take(D * b.Tp * 2);
+    b.dyT = take(Fs > 0 ? D * b.Tp * 2 : 0);
+    b.HshT = take(Fs * b.Tp * 2);
+    b.dZshT = take(2 * Fs * b.Tp * 2);
+    b.dl = take(T * M * 4);
+    b.gate = take(T * M * 4);
+    b.dlT3 = take(3 * M * b.Tp * 2);
+    b.C3 = take(3 * M * D * 4);
+    b.total = off;
+    return b;
+}
+
+int validate_bwd(const moe_desc* d) {
+    TRY(validate(d));
+    if (d->dtype != MOE_DTYPE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "the backward runs on bf16 layers only");
+    if (d->weight_layout != MOE_LAYOUT_ROWS)
+        return fail(MOE_ERR_UNSUPPORTED, "the backward reads row-major weights only");
+    const int64_t S = d->T * d->k, Spad = ((S + 64 * d->M + 63) / 64) * 64;
+    const int64_t G = d->act == MOE_ACT_SWIGLU ? 2 : 1;
+    const int64_t biggest = std::max({d->D * Spad, G * d->F * Spad, d->D * G * d->F});
+    if (biggest * 2 > ((int64_t)1 << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "a backward operand exceeds 2 GiB");
+    return MOE_OK;
+}
+
+GemmArgs dense_args(const void* a, const void* b, void* c, int64_t rows, int64_t b_rows,
+                    int64_t K, int64_t N) {
+    GemmArgs g{};
+    g.a = a;
+    g.b = b;
+    g.c = c;
+    g.dense_rows = rows;
+    g.a_rows = rows;
+    g.b_rows = (int)b_rows;
+    g.K = (int)K;
+    g.N = (int)N;
+    g.xcd_mode = gemm_xcd_mode(false, false);
+    return g;
+}
+
+int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* x,
+                const float* W_r, const float* bias, const void* W1, const void* b1,
+                const void* W2, const void* b2, const void* Wsh_gu, const void* Wsh_dn,
+                const void* dy,
+                float* dx, float* dW_r, float* dW1, float* db1, float* dW2, float* db2,
+                float* dWsh_gu, float* dWsh_dn, int32_t* load_count, float* load_score, void* ws,
+                hipStream_t s) {
+    const Plan& p = b.f;
+    const int64_t T = d->T, D = d->D, M = d->M, F = d->F, Fs = d->F_shared, S = b.S;
+    const int64_t GF = b.G * F;
+    const bool swiglu = d->act == MOE_ACT_SWIGLU;
+    int32_t* idx = at<int32_t>(ws, p.idx);
+    float* w = at<float>(ws, p.w);
+    int32_t* counts = at<int32_t>(ws, p.counts);
+    int32_t* offsets = at<int32_t>(ws, p.offsets);
+    int32_t* sorted_token = at<int32_t>(ws, p.sorted_token);
+    int32_t* sorted_slot = at<int32_t>(ws, p.sorted_slot);
+    int32_t* slot_row = at<int32_t>(ws, p.slot_row);
+    float* row_scale = at<float>(ws, p.row_scale);
+    int32_t* tiles_up = at<int32_t>(ws, p.tiles_up);
+    int32_t* tiles_dn = at<int32_t>(ws, p.tiles_dn);
+    void* H = at<char>(ws, p.H);
+    float* dXs = at<float>(ws, p.O);
+    void* Hsh = at<char>(ws, p.Hsh);
+    float* dXsh = Fs > 0 ? at<float>(ws, p.Ysh) : nullptr;
+    const float* L = reinterpret_cast<const float*>(at<char>(ws, p.route) +
+                                                    route_logits_offset(1, T, D, M));
+    void* Z = at<char>(ws, b.Z);
+    void* dZ = at<char>(ws, b.dZ);
+    float* part = at<float>(ws, b.part);
+    void* W1T = at<char>(ws, b.W1T);
+    void* W2T = at<char>(ws, b.W2T);
+    int32_t* poff = at<int32_t>(ws, b.poff);
+    int32_t* pad_row = at<int32_t>(ws, b.pad_row);
+    int32_t* pad_tok = at<int32_t>(ws, b.pad_tok);
+    void* dOT = at<char>(ws, b.dOT);
+    void* HT = at<char>(ws, b.HT);
+    void* dZT = at<char>(ws, b.dZT);
+    void* XT = at<char>(ws, b.XT);
+    void* xT = at<char>(ws, b.xT);
+    float* dl = at<float>(ws, b.dl);
+    float* gate = at<float>(ws, b.gate);
+    void* dlT3 = at<char>(ws, b.dlT3);
+    float* C3 = at<float>(ws, b.C3);
+
+    // forward recompute of the routing (the bf16 router leaves its logits)
+    TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
+    TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
+    TileTables tt{{p.bm_up, p.bm_dn},
+                  {(int)p.max_tiles_up, (int)p.max_tiles_dn},
+                  {tiles_up, tiles_dn}};
+    const int ntables = tiles_dn == tiles_up ? 1 : 2;
+    TRY(run(h, s, L_TILE_TABLE, [&] {
+        return launch_tile_table(s, offsets, M, tt, ntables, sorted_slot, w, S, row_scale, 0,
+                                 sorted_token);
+    }));
+    // weights transposed for the input-gradient GEMMs: W2T[e] = W2[e]^T [F, D],
+    // W1T[e] = W1[e]^T [D, G F]
+    TRY(run(h, s, L_B_TRANSPOSE, [&] {
+        hipError_t e = launch_transpose(s, W2, F, D, D * F, nullptr, nullptr, nullptr, F, D, W2T,
+                                        D, F * D, (int)M);
+        if (e != hipSuccess) return e;
+        return launch_transpose(s, W1, D, GF, GF * D, nullptr, nullptr, nullptr, D, GF, W1T, GF,
+                                D * GF, (int)M);
+    }));
+
+    // 1. up projection again, keeping the pre-activations Z (bf16)
+    GemmArgs up{};
+    up.a = x;
+    up.gather = sorted_token;
+    up.b = W1;
+    up.b_stride = GF * D;
+    up.bias = swiglu ? nullptr : b1;
+    up.c = H;
+    up.c2 = Z;
+    up.tiles = tiles_up;
+    up.offsets = offsets;
+    up.dense_rows = S;
+    up.a_rows = T;
+    up.b_rows = (int)GF;
+    up.K = (int)D;
+    up.N = (int)F;
+    up.F_split = (int)F;
+    up.group_m = gemm_group_m(S, M, p.bm_up);
+    up.xcd_mode = gemm_xcd_mode(true, false);
+    TRY(run(h, s, L_B_UP, [&] {
+        return launch_gemm(s, 1, p.bm_up, swiglu ? EPI_SWIGLU_SAVE : EPI_GELU_SAVE, up,
+                           p.max_tiles_up);
+    }));
+    // 2. dH_raw = dy W2[e] per sorted row -> dZ (activation derivative, row
+    //    weight) and the per-tile dots H . dH_raw for the router
+    GemmArgs dh = up;
+    dh.a = dy;
+    dh.b = W2T;
+    dh.b_stride = F * D;
+    dh.bias = nullptr;
+    dh.c = dZ;
+    dh.c2 = Z;
+    dh.aux = H;
+    dh.row_w = row_scale;
+    dh.part = part;
+    dh.part_ld = b.part_ld;
+    dh.b_rows = (int)F;
+    dh.F_split = 0;
+    TRY(run(h, s, L_B_DH, [&] {
+        return launch_gemm(s, 1, p.bm_up, swiglu ? EPI_DH_SWIGLU : EPI_DH_GELU, dh,
+                           p.max_tiles_up);
+    }));
+    // 3. expert rows' input gradients dXs = dZ W1[e] (fp32, sorted order)
+    GemmArgs dxg{};
+    dxg.a = dZ;
+    dxg.b = W1T;
+    dxg.b_stride = D * GF;
+    dxg.c = dXs;
+    dxg.tiles = tiles_dn;
+    dxg.offsets = offsets;
+    dxg.dense_rows = S;
+    dxg.a_rows = S;
+    dxg.b_rows = (int)D;
+    dxg.K = (int)GF;
+    dxg.N = (int)D;
+    dxg.group_m = gemm_group_m(S, M, p.bm_dn);
+    dxg.xcd_mode = gemm_xcd_mode(true, true);
+    TRY(run(h, s, L_B_DX, [&] {
+        return launch_gemm(s, 1, p.bm_dn, EPI_DOWN_F32, dxg, p.max_tiles_dn);
+    }));
+
+    // 4. the shared expert, the same three steps as one dense group
+    if (Fs > 0) {
+        void* Zsh = at<char>(ws, b.Zsh);
+        void* dZsh = at<char>(ws, b.dZsh);
+        void* WshguT = at<char>(ws, b.WshguT);
+        void* WshdnT = at<char>(ws, b.WshdnT);
+        TRY(run(h, s, L_B_TRANSPOSE, [&] {
+            hipError_t e = launch_transpose(s, Wsh_dn, Fs, D, 0, nullptr, nullptr, nullptr, Fs, D,
+                                            WshdnT, D, 0, 1);
+            if (e != hipSuccess) return e;
+            return launch_transpose(s, Wsh_gu, D, 2 * Fs, 0, nullptr, nullptr, nullptr, D, 2 * Fs,
+                                    WshguT, 2 * Fs, 0, 1);
+        }));
+        const int64_t mt_up = (T + p.bm_sh_up - 1) / p.bm_sh_up;
+        const int64_t mt_dn = (T + p.bm_sh_dn - 1) / p.bm_sh_dn;
+        GemmArgs su = dense_args(x, Wsh_gu, Hsh, T, 2 * Fs, D, Fs);
+        su.c2 = Zsh;
+        su.F_split = (int)Fs;
+        TRY(run(h, s, L_B_UP, [&] {
+            return launch_gemm(s, 1, p.bm_sh_up, EPI_SWIGLU_SAVE, su, mt_up);
+        }));
+        GemmArgs sd = dense_args(dy, WshdnT, dZsh, T, Fs, D, Fs);
+        sd.c2 = Zsh;
+        TRY(run(h, s, L_B_DH, [&] {
+            return launch_gemm(s, 1, p.bm_sh_up, EPI_DH_SWIGLU, sd, mt_up);
+        }));
+        GemmArgs sx = dense_args(dZsh, WshguT, dXsh, T, D, 2 * Fs, D);
+        TRY(run(h, s, L_B_DX, [&] { return launch_gemm(s, 1, p.bm_sh_dn, EPI_DOWN_F32, sx, mt_dn); }));
+    }
+
+    // 5. router: weights -> gate values -> logits; then dx
+    TRY(run(h, s, L_B_OTHER, [&] {
+        hipError_t e = launch_router_backward(s, L, idx, w, slot_row, part, b.part_ld,
+                                              swiglu ? nullptr : b2, dy, D, T, M, d->k, d->scorer,
+                                              d->renorm, d->alpha, d->eps, dl, gate);
+        if (e != hipSuccess) return e;
+        e = launch_bwd_combine(s, dXs, slot_row, dXsh, dl, idx, W_r, T, d->k, M, D,
+                               d->scorer == MOE_SCORER_SIGMOID, dx);
+        if (e != hipSuccess) return e;
+        return launch_load_stats(s, gate, T, M, counts, load_count, load_score);
+    }));
+
+    // 6. weight gradients: per-expert padded, transposed operands, one
+    //    K-grouped GEMM each (K = the expert's padded rows)
+    TRY(run(h, s, L_B_TRANSPOSE, [&] {
+        hipError_t e = launch_pad_layout(s, offsets, M, sorted_token, b.Spad, poff, pad_row, pad_tok);
+        if (e != hipSuccess) return e;
+        // dO = w dy per sorted row (gathered through sorted_token)
+        e = launch_transpose(s, dy, D, S, 0, pad_row, sorted_token, row_scale, D, b.Spad, dOT,
+                             b.Spad, 0, 1);
+        if (e != hipSuccess) return e;
+        e = launch_transpose(s, H, F, S, 0, pad_row, nullptr, nullptr, F, b.Spad, HT, b.Spad, 0, 1);
+        if (e != hipSuccess) return e;
+        e = launch_transpose(s, dZ, GF, S, 0, pad_row, nullptr, nullptr, GF, b.Spad, dZT, b.Spad, 0,
+                             1);
+        if (e != hipSuccess) return e;
+        e = launch_transpose(s, x, D, S, 0, pad_row, sorted_token, nullptr, D, b.Spad, XT, b.Spad,
+                             0, 1);
+        if (e != hipSuccess) return e;
+        return launch_transpose(s, x, D, T, 0, nullptr, nullptr, nullptr, D, b.Tp, xT, b.Tp, 0, 1);
+    }));
+    GemmArgs w2 = dense_args(dOT, HT, dW2, D, F, b.Spad, F);
+    w2.koff = poff;
+    w2.kgroups = (int)M;
+    w2.c_group_stride = D * F;
+    GemmArgs w1 = dense_args(dZT, XT, dW1, GF, D, b.Spad, D);
+    w1.koff = poff;
+    w1.kgroups = (int)M;
+    w1.c_group_stride = GF * D;
+    TRY(run(h, s, L_B_WGRAD, [&] {
+        hipError_t e = launch_gemm(s, 1, b.bm_w2, EPI_DOWN_F32, w2, (D + b.bm_w2 - 1) / b.bm_w2);
+        if (e != hipSuccess) return e;
+        return launch_gemm(s, 1, b.bm_w1, EPI_DOWN_F32, w1, (GF + b.bm_w1 - 1) / b.bm_w1);
+    }));
+    if (Fs > 0) {
+        void* dyT = at<char>(ws, b.dyT);
+        void* HshT = at<char>(ws, b.HshT);
+        void* dZshT = at<char>(ws, b.dZshT);
+        void* dZsh = at<char>(ws, b.dZsh);
+        TRY(run(h, s, L_B_TRANSPOSE, [&] {
+            hipError_t e = launch_transpose(s, dy, D, T, 0, nullptr, nullptr, nullptr, D, b.Tp, dyT,
+                                            b.Tp, 0, 1);
+            if (e != hipSuccess) return e;
+            e = launch_transpose(s, Hsh, Fs, T, 0, nullptr, nullptr, nullptr, Fs, b.Tp, HshT, b.Tp,
+                                 0, 1);
+            if (e != hipSuccess) return e;
+            return launch_transpose(s, dZsh, 2 * Fs, T, 0, nullptr, nullptr, nullptr, 2 * Fs, b.Tp,
+                                    dZshT, b.Tp, 0, 1);
+        }));
+        GemmArgs s2 = dense_args(dyT, HshT, dWsh_dn, D, Fs, b.Tp, Fs);
+        GemmArgs s1 = dense_args(dZshT, xT, dWsh_gu, 2 * Fs, D, b.Tp, D);
+        TRY(run(h, s, L_B_WGRAD, [&] {
+            hipError_t e = launch_gemm(s, 1, b.bm_sh2, EPI_DOWN_F32, s2, (D + b.bm_sh2 - 1) / b.bm_sh2);
+            if (e != hipSuccess) return e;
+            return launch_gemm(s, 1, b.bm_sh1, EPI_DOWN_F32, s1,
+                               (2 * Fs + b.bm_sh1 - 1) / b.bm_sh1);
+        }));
+    }
+    // router weight gradient: dl split exactly into three bf16 planes, so the
+    // MFMA products with bf16 x are exact; the planes' results are summed
+    GemmArgs rw = dense_args(dlT3, xT, C3, 3 * M, D, b.Tp, D);
+    TRY(run(h, s, L_B_WGRAD, [&] {
+        hipError_t e = launch_split_transpose_dl(s, dl, T, M, b.Tp, dlT3);
+        if (e != hipSuccess) return e;
+        e = launch_gemm(s, 1, b.bm_r, EPI_DOWN_F32, rw, (3 * M + b.bm_r - 1) / b.bm_r);
+        if (e != hipSuccess) return e;
+        return launch_sum3(s, C3, C3 + M * D, C3 + 2 * M * D, M * D, dW_r);
+    }));
+    // bias gradients (GELU experts): db1 = column sums of dz, db2 of w dy
+    if (!swiglu && (db1 || db2)) {
+        TRY(run(h, s, L_B_OTHER, [&] {
+            hipError_t e = hipSuccess;
+            if (db1) e = launch_seg_colsum(s, dZ, F, offsets, nullptr, nullptr, M, F, db1);
+            if (e != hipSuccess) return e;
+            if (db2) e = launch_seg_colsum(s, dy, D, offsets, sorted_token, row_scale, M, D, db2);
+            return e;
+        }));
+    }
+    return MOE_OK;
+}
+
 #define CHECK_HANDLE(h)                                                      \
     do {                                                                     \
         if (!(h)) return fail(MOE_ERR_INVALID, "handle is NULL");            \
@@ -663,6 +1007,68 @@ int moe_forward(moe_handle* h, const moe_desc* d, const void* x, const float* W_
         if (e != hipSuccess) return fail(MOE_ERR_HIP, "stream join: %s", hipGetErrorString(e));
     }
     return do_combine(h, d, O, slot_row, Ysh, y, s);
+}
+
+int moe_backward_workspace_size(const moe_desc* d, size_t* bytes) {
+    if (!bytes) return fail(MOE_ERR_INVALID, "bytes is NULL");
+    TRY(validate_bwd(d));
+    *bytes = make_bwd_plan(d).total;
+    return MOE_OK;
+}
+
+int moe_backward(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
+                 const float* bias, const void* W1, const void* b1, const void* W2,
+                 const void* b2, const void* Wsh_gu, const void* Wsh_dn, const void* dy,
+                 float* dx, float* dW_r, float* dW1, float* db1, float* dW2, float* db2,
+                 float* dWsh_gu, float* dWsh_dn, int32_t* load_count, float* load_score,
+                 void* ws, size_t ws_bytes, void* stream) {
+    CHECK_HANDLE(h);
+    TRY(validate_bwd(d));
+    NEED(dW_r, "dW_r");
+    NEED(dW1, "dW1");
+    NEED(dW2, "dW2");
+    NEED(load_count, "load_count");
+    NEED(load_score, "load_score");
+    if (d->F_shared > 0) {
+        NEED(dWsh_gu, "dWsh_gu");
+        NEED(dWsh_dn, "dWsh_dn");
+    }
+    if (d->T > 0) {   // with no tokens only the (zeroed) gradients are touched
+        NEED(x, "x");
+        NEED(W_r, "W_r");
+        NEED(W1, "W1");
+        NEED(W2, "W2");
+        NEED(dy, "dy");
+        NEED(dx, "dx");
+        if (d->F_shared > 0) {
+            NEED(Wsh_gu, "Wsh_gu");
+            NEED(Wsh_dn, "Wsh_dn");
+        }
+    }
+    if (d->act == MOE_ACT_SWIGLU) db1 = db2 = nullptr;   // no biases
+    const BwdPlan b = make_bwd_plan(d);
+    if (ws_bytes < b.total)
+        return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, b.total);
+    if (!ws) return fail(MOE_ERR_INVALID, "workspace pointer is NULL");
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (d->T == 0) {   // no tokens: every gradient and statistic is zero
+        const int64_t G = d->act == MOE_ACT_SWIGLU ? 2 : 1;
+        hipError_t e = hipSuccess;
+        const std::pair<float*, int64_t> zs[] = {
+            {dW_r, d->M * d->D}, {dW1, d->M * G * d->F * d->D}, {dW2, d->M * d->D * d->F},
+            {db1, d->M * d->F}, {db2, d->M * d->D}, {load_score, d->M},
+            {reinterpret_cast<float*>(load_count), d->M},
+            {d->F_shared > 0 ? dWsh_gu : nullptr, 2 * d->F_shared * d->D},
+            {d->F_shared > 0 ? dWsh_dn : nullptr, d->D * d->F_shared}};
+        for (const auto& z : zs)
+            if (e == hipSuccess) e = launch_fill_zero(s, z.first, z.second);
+        if (e != hipSuccess) return fail(MOE_ERR_HIP, "zero fill: %s", hipGetErrorString(e));
+        return MOE_OK;
+    }
+    return do_backward(h, d, b, x, W_r, bias, W1, b1, W2, b2, Wsh_gu, Wsh_dn, dy, dx, dW_r, dW1, db1,
+                       dW2, db2, dWsh_gu, dWsh_dn, load_count, load_score, ws, s);
 }
 
 int moe_profile_start(moe_handle* h, int capacity, const char* filter) {

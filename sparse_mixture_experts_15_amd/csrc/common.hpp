@@ -51,10 +51,32 @@ __device__ __forceinline__ float gelu_erf_f32(float z) {
     return z * (z >= 0.f ? 1.0f - lower : lower);
 }
 
+// Derivatives for the backward.  silu'(z) = s (1 + z (1 - s)), s = sigmoid(z).
+__device__ __forceinline__ float silu_grad_f32(float z) {
+    const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+    return s * (1.0f + z * (1.0f - s));
+}
+// gelu'(z) = Phi(z) + z phi(z); Phi from the same erfc approximation as
+// gelu_erf_f32, phi(z) = exp(-z^2 / 2) / sqrt(2 pi).
+__device__ __forceinline__ float gelu_grad_f32(float z) {
+    const float a = fabsf(z) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, a, 1.0f));
+    float p = fmaf(1.061405429f, t, -1.453152027f);
+    p = fmaf(p, t, 1.421413741f);
+    p = fmaf(p, t, -0.284496736f);
+    p = fmaf(p, t, 0.254829592f);
+    const float e = __expf(-a * a);
+    const float lower = 0.5f * t * p * e;   // Phi(-|z|)
+    const float Phi = z >= 0.f ? 1.0f - lower : lower;
+    return Phi + z * e * 0.3989422804014327f;   // exp(-z^2/2) = exp(-a^2)
+}
+
 // Kernel labels (indices into the profiling table).
 enum Label : int {
     L_ROUTE = 0, L_PERM_COUNT, L_PERM_SCAN, L_PERM_SCATTER, L_TILE_TABLE,
-    L_FFN_UP, L_FFN_DOWN, L_SHARED_UP, L_SHARED_DOWN, L_COMBINE, L_COUNT
+    L_FFN_UP, L_FFN_DOWN, L_SHARED_UP, L_SHARED_DOWN, L_COMBINE,
+    // backward
+    L_B_UP, L_B_DH, L_B_DX, L_B_WGRAD, L_B_TRANSPOSE, L_B_OTHER, L_COUNT
 };
 
 // Epilogues of the expert GEMMs.
@@ -62,8 +84,18 @@ enum Epi : int {
     EPI_SWIGLU = 0,      // out[r, n] = silu(gate) * up            -> dtype
     EPI_GELU = 1,        // out[r, n] = gelu(acc + b1[e, n])       -> dtype
     EPI_DOWN_SCALED = 2, // out[r, n] = w[slot(r)] * (acc + b2[e, n]) -> fp32
-    EPI_DOWN_F32 = 3     // out[r, n] = acc                         -> fp32
+    EPI_DOWN_F32 = 3,    // out[r, n] = acc                         -> fp32
+    // backward (bf16 only):
+    EPI_SWIGLU_SAVE = 4, // EPI_SWIGLU, and c2[r, n] = gate, c2[r, N + n] = up   (bf16)
+    EPI_GELU_SAVE = 5,   // EPI_GELU, and c2[r, n] = acc + b1[e, n]             (bf16)
+    EPI_DH_SWIGLU = 6,   // acc = dH_raw[r, n]; with dH = w * acc, gate / up from c2:
+                         // out[r, n] = dH up silu'(gate), out[r, N + n] = dH silu(gate)
+    EPI_DH_GELU = 7      // out[r, n] = w * acc * gelu'(z), z = c2[r, n]
+    // EPI_DH_*: part[r][n-tile x waves] = sum over the wave's columns of
+    // aux[r, n] * acc (aux = H), when part is non-null; w = row_w[r] or 1.
 };
+
+constexpr bool epi_pairs(int epi) { return epi == EPI_SWIGLU || epi == EPI_SWIGLU_SAVE; }
 
 // One expert GEMM launch: C[rows, N] = epi(A[rows, K] . B[e]^T), where
 // A rows come from `a` (through `gather` when non-null) and B[e] is the
@@ -92,6 +124,18 @@ struct GemmArgs {
                               // 2 contiguous slices per XCD
     const void* b_extra;      // grouped: weights of group extra_group, in place of
     int extra_group;          // b + extra_group * b_stride (NULL: none)
+    // backward epilogues
+    void* c2;                 // EPI_*_SAVE: pre-activations out; EPI_DH_*: in (bf16)
+    const void* aux;          // EPI_DH_*: H (bf16, [rows, N]) for the weight-gradient dots
+    float* part;              // EPI_DH_*: [rows][part_ld] partial dots (nullable)
+    int part_ld;
+    // K-grouped mode (koff non-null): group q multiplies A and B over the K
+    // range [koff[q], koff[q+1]) (multiples of 64) and writes its own
+    // [a_rows, N] output at c + q * c_group_stride; kgroups groups, dense
+    // tiles over the A rows (dense_rows) and the N B rows.
+    const int32_t* koff;
+    int kgroups;
+    int64_t c_group_stride;
 };
 
 // Weight tiles of the bf16 GEMM: 256 weight rows by K stages of 64.
@@ -112,6 +156,9 @@ hipError_t launch_tile_weights(hipStream_t s, const void* src, void* dst, int64_
 // one expert spans, so that the workgroups one XCD runs together share that
 // expert's weight tiles and rows in its L2.
 int gemm_group_m(int64_t rows, int64_t groups, int bm);
+// Columns of the EPI_DH_* partial-dot buffer (part_ld) for a GEMM of N
+// output columns on the tile height bm.
+int gemm_part_cols(int bm, int64_t N);
 // Workgroup order (GemmArgs::xcd_mode) of a grouped or dense up or down
 // projection.
 int gemm_xcd_mode(bool grouped, bool down);
@@ -124,8 +171,10 @@ hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, con
                         const float* bias, int32_t* idx, float* w, int64_t T, int64_t D,
                         int64_t M, int k, int renorm, float alpha, float eps, int n_group,
                         int topk_group, void* ws);
-// Router workspace (bytes) and its K-split count.
+// Router workspace (bytes) and its K-split count; the bf16 router leaves
+// the fp32 logits L[T][M] at route_logits_offset() bytes into it.
 size_t route_workspace(int dtype, int64_t T, int64_t D, int64_t M);
+size_t route_logits_offset(int dtype, int64_t T, int64_t D, int64_t M);
 int route_ksplit(int64_t T, int64_t D, int64_t M);
 hipError_t launch_perm_count(hipStream_t s, const int32_t* idx, int32_t* hist, int64_t T, int k,
                              int64_t M);
@@ -158,6 +207,34 @@ hipError_t launch_gemm(hipStream_t s, int dtype, int bm, int epi, const GemmArgs
                        int64_t m_tiles);
 hipError_t launch_combine(hipStream_t s, int out_dtype, const float* O, const int32_t* slot_row,
                           const float* Ysh, void* y, int64_t T, int k, int64_t D);
+
+// Backward (backward.hip).
+hipError_t launch_transpose(hipStream_t s, const void* src, int64_t ld_src, int64_t src_rows,
+                            int64_t src_bstride, const int32_t* idx1, const int32_t* idx2,
+                            const float* scale, int64_t C, int64_t P, void* out, int64_t ld_out,
+                            int64_t out_bstride, int batches);
+hipError_t launch_pad_layout(hipStream_t s, const int32_t* offsets, int64_t M,
+                             const int32_t* sorted_token, int64_t P, int32_t* poff,
+                             int32_t* pad_row, int32_t* pad_tok);
+hipError_t launch_router_backward(hipStream_t s, const float* L, const int32_t* idx,
+                                  const float* w, const int32_t* slot_row, const float* part,
+                                  int part_ld, const void* b2, const void* dy, int64_t D,
+                                  int64_t T, int64_t M, int k, int scorer, int renorm,
+                                  float alpha, float eps, float* dl, float* gate);
+hipError_t launch_bwd_combine(hipStream_t s, const float* dXs, const int32_t* slot_row,
+                              const float* dXsh, const float* dl, const int32_t* idx,
+                              const float* W_r, int64_t T, int k, int64_t M, int64_t D,
+                              int sparse_dl, float* dx);
+hipError_t launch_split_transpose_dl(hipStream_t s, const float* dl, int64_t T, int64_t M,
+                                     int64_t Tp, void* out);
+hipError_t launch_sum3(hipStream_t s, const float* a, const float* b, const float* c, int64_t n,
+                       float* out);
+hipError_t launch_seg_colsum(hipStream_t s, const void* src, int64_t ld, const int32_t* offsets,
+                             const int32_t* gather, const float* row_scale, int64_t M, int64_t C,
+                             float* out);
+hipError_t launch_load_stats(hipStream_t s, const float* gate, int64_t T, int64_t M,
+                             const int32_t* counts, int32_t* count_out, float* score);
+hipError_t launch_fill_zero(hipStream_t s, float* p, int64_t n);
 
 // Rows per m-tile of a GEMM for a dtype, given its total rows, the number of
 // groups (experts) sharing them, whether it is a down projection and the

@@ -62,7 +62,7 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& g, int mt, int bm, Tile&
 template <int EPI>
 __device__ __forceinline__ void brow_map(int b, int n_base, int F_split, int& out_col,
                                          int& b_row) {
-    if (EPI == EPI_SWIGLU) {
+    if (epi_pairs(EPI)) {
         const int wb = b >> 6, within = b & 63;
         out_col = n_base + 32 * wb + (within & 31);
         b_row = out_col + ((within >> 5) ? F_split : 0);
@@ -187,6 +187,59 @@ __device__ __forceinline__ bool tile_coords(int m_tiles, int n_tiles, int group_
     return true;
 }
 
+// Backward epilogue of the down projection's input gradient (EPI_DH_*): the
+// accumulator is dH_raw = dy . W2[e] for sorted row r and output column n
+// (an expert-width column).  With the row's gate weight w (row_w, or 1 for
+// the shared expert) dH = w dH_raw passes through the activation's
+// derivative at the saved pre-activations (c2) into the bf16 gradient of
+// the up projection's output (c: SwiGLU [rows, 2N] gate then up, GELU
+// [rows, N]).  The weight gradient's dot dw = H . dH_raw over the columns
+// is summed per row over the wave's columns (lanes of a row meet by
+// shuffles) and stored per (row, n-tile, wave) in part, without atomics.
+template <int EPI, int TM, int TN, int WROWS, int WN>
+__device__ __forceinline__ void dh_epilogue(const GemmArgs& g, const Tile& tl,
+                                            const floatx4 (&acc)[TM][TN], int wlive, int wm,
+                                            int wn, int n_base, int nt, int lane) {
+    const int N = g.N;
+    const int lr = lane & 15, lc = 4 * (lane >> 4);
+    const bf16_t* zp = static_cast<const bf16_t*>(g.c2);
+    const bf16_t* hp = static_cast<const bf16_t*>(g.aux);
+    bf16_t* out = static_cast<bf16_t*>(g.c);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        if (i >= wlive) continue;   // wave-uniform
+        const int64_t r = tl.r0 + wm * WROWS + 16 * i + lr;
+        const bool rv = r < tl.rend;
+        float pw = 0.f;
+        if (rv) {
+            const float wr = g.row_w ? g.row_w[r] : 1.f;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int n = n_base + 64 * wn + 16 * j + lc;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (n + q >= N) continue;
+                    const float a = acc[i][j][q];
+                    if (hp) pw += bf16_to_f32(hp[r * N + n + q]) * a;
+                    const float dh = wr * a;
+                    if (EPI == EPI_DH_SWIGLU) {
+                        const float gt = bf16_to_f32(zp[r * 2 * N + n + q]);
+                        const float up = bf16_to_f32(zp[r * 2 * N + N + n + q]);
+                        out[r * 2 * N + n + q] = f32_to_bf16(dh * up * silu_grad_f32(gt));
+                        out[r * 2 * N + N + n + q] = f32_to_bf16(dh * silu_f32(gt));
+                    } else {
+                        const float z = bf16_to_f32(zp[r * N + n + q]);
+                        out[r * N + n + q] = f32_to_bf16(dh * gelu_grad_f32(z));
+                    }
+                }
+            }
+        }
+        pw += __shfl_xor(pw, 16);
+        pw += __shfl_xor(pw, 32);
+        if (rv && g.part && lane < 16) g.part[r * g.part_ld + nt * WN + wn] = pw;
+    }
+}
+
 // One tile configuration: BM A rows x BNB B rows per workgroup, STAGES LDS
 // stages of K = KS (64 or 32); the eight waves form WM x WN with 64 B rows
 // per wave.
@@ -218,14 +271,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     const int m_valid = g.tiles ? min(m_tiles, g.tiles[2 * m_tiles]) : m_tiles;
     // split-K (dense fp32 output only): chunk kc of g.k_split covers a K range
     const int nsplit = g.k_split > 1 ? g.k_split : 1;
-    int kc_id = 0, p = (int)blockIdx.x, mt, nt;
-    if (nsplit > 1) {   // split-K: chunk-major ids, plain order inside a chunk
+    int kc_id = 0, kg = 0, p = (int)blockIdx.x, mt, nt;
+    if (g.koff) {       // K-grouped: group-major ids, plain order inside a group
+        kg = p / max(m_valid * n_tiles, 1);
+        if (kg >= g.kgroups) return;
+        p -= kg * m_valid * n_tiles;
+    } else if (nsplit > 1) {   // split-K: chunk-major ids, plain order inside a chunk
         kc_id = p / max(m_valid * n_tiles, 1);
         if (kc_id >= nsplit) return;
         p -= kc_id * m_valid * n_tiles;
     }
     if (!tile_coords(m_valid, n_tiles, g.group_m > 0 ? g.group_m : 4, p, mt, nt,
-                     nsplit > 1 ? 1 : g.xcd_mode))
+                     (nsplit > 1 || g.koff) ? 1 : g.xcd_mode))
         return;
     Tile tl;
     if (!tile_of(g, mt, BM, tl)) return;
@@ -233,7 +290,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
     const int K = g.K, N = g.N;
-    const int out_per_tile = (EPI == EPI_SWIGLU) ? BNB / 2 : BNB;
+    const int out_per_tile = epi_pairs(EPI) ? BNB / 2 : BNB;
     const int n_base = nt * out_per_tile;
 
     // buffer descriptors: A rows (whole activation matrix), B = this expert
@@ -309,8 +366,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     // STAGES-deep ring: stages kt+1 .. kt+STAGES-1 load while stage kt is
     // multiplied.  With split-K this workgroup runs stages [k_first, k_last).
     const int nk_all = (K + BK - 1) / BK;
-    const int k_first = (int)((int64_t)nk_all * kc_id / nsplit);
-    const int k_last = (int)((int64_t)nk_all * (kc_id + 1) / nsplit);
+    const int k_first = g.koff ? g.koff[kg] / BK : (int)((int64_t)nk_all * kc_id / nsplit);
+    const int k_last = g.koff ? g.koff[kg + 1] / BK : (int)((int64_t)nk_all * (kc_id + 1) / nsplit);
     const int nk = k_last - k_first;
 #pragma unroll
     for (int s0 = 0; s0 < STAGES - 1; ++s0)
@@ -387,11 +444,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     // four lanes of a row write 32 / 64 contiguous bytes, and a row's
     // fragments fill whole cache lines in L2.
     const int lr = lane & 15, lc = 4 * (lane >> 4);
+    if constexpr (EPI == EPI_DH_SWIGLU || EPI == EPI_DH_GELU) {
+        dh_epilogue<EPI, TM, TN, WROWS, WN>(g, tl, acc, wlive, wm, wn, n_base, nt, lane);
+        return;
+    } else {
     const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
-    constexpr bool OUT_BF16 = (EPI == EPI_SWIGLU || EPI == EPI_GELU);
-    constexpr bool HAS_BIAS = (EPI == EPI_GELU || EPI == EPI_DOWN_SCALED);
-    constexpr int OUT_FR = (EPI == EPI_SWIGLU) ? TN / 2 : TN;   // output fragments per row
-    constexpr int OUT_W = (EPI == EPI_SWIGLU) ? 32 : 64;        // output columns per wave
+    constexpr bool SAVE = (EPI == EPI_SWIGLU_SAVE || EPI == EPI_GELU_SAVE);
+    constexpr bool OUT_BF16 = (EPI == EPI_SWIGLU || EPI == EPI_GELU || SAVE);
+    constexpr bool HAS_BIAS = (EPI == EPI_GELU || EPI == EPI_GELU_SAVE || EPI == EPI_DOWN_SCALED);
+    constexpr int OUT_FR = epi_pairs(EPI) ? TN / 2 : TN;   // output fragments per row
+    constexpr int OUT_W = epi_pairs(EPI) ? 32 : 64;        // output columns per wave
     const bool vec = (N % 4) == 0;                              // aligned 4-column groups
     float bv[OUT_FR][4];
 #pragma unroll
@@ -414,10 +476,27 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             const int n = n_base + OUT_W * wn + 16 * j + lc;
             if (n >= N) continue;
             float v[4];
+            if constexpr (SAVE) {
+                // pre-activations for the backward: gate and up (SwiGLU, row
+                // stride 2N) or z = acc + b1 (GELU, row stride N), bf16
+                bf16_t* zp = static_cast<bf16_t*>(g.c2);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (n + q >= N) continue;
+                    if (EPI == EPI_SWIGLU_SAVE) {
+                        zp[r * 2 * N + n + q] = f32_to_bf16(acc[i][j][q]);
+                        zp[r * 2 * N + N + n + q] = f32_to_bf16(acc[i][j + 2][q]);
+                    } else {
+                        zp[r * N + n + q] = f32_to_bf16(acc[i][j][q] + bv[j][q]);
+                    }
+                }
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                if (EPI == EPI_SWIGLU) v[q] = silu_f32(acc[i][j][q]) * acc[i][j + 2][q];
-                else if (EPI == EPI_GELU) v[q] = gelu_erf_f32(acc[i][j][q] + bv[j][q]);
+                if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE)
+                    v[q] = silu_f32(acc[i][j][q]) * acc[i][j + 2][q];
+                else if (EPI == EPI_GELU || EPI == EPI_GELU_SAVE)
+                    v[q] = gelu_erf_f32(acc[i][j][q] + bv[j][q]);
                 else if (EPI == EPI_DOWN_SCALED) v[q] = wr * (acc[i][j][q] + bv[j][q]);
                 else v[q] = acc[i][j][q];
             }
@@ -434,7 +513,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
                         if (n + q < N) dst[q] = f32_to_bf16(v[q]);
                 }
             } else {
-                float* dst = static_cast<float*>(g.c) + (int64_t)kc_id * g.dense_rows * N + r * N + n;
+                float* dst = static_cast<float*>(g.c) +
+                             (g.koff ? (int64_t)kg * g.c_group_stride
+                                     : (int64_t)kc_id * g.dense_rows * N) +
+                             r * N + n;
                 if (vec && n + 4 <= N) {
                     *reinterpret_cast<floatx4*>(dst) = floatx4{v[0], v[1], v[2], v[3]};
                 } else {
@@ -444,6 +526,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
                 }
             }
         }
+    }
     }
 }
 
@@ -539,6 +622,7 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs g) {
 // valid count from above): mode 0 deals whole groups to the eight XCDs in
 // turn, so the grid is rounded up to eight groups.
 int64_t grid_tiles(const GemmArgs& g, int64_t m_tiles, int64_t n_tiles) {
+    if (g.koff) return m_tiles * n_tiles * g.kgroups;
     if (g.k_split > 1) return m_tiles * n_tiles * g.k_split;
     if (g.xcd_mode != 0) return m_tiles * n_tiles;
     const int64_t gm = g.group_m > 0 ? g.group_m : 4;
@@ -548,7 +632,7 @@ int64_t grid_tiles(const GemmArgs& g, int64_t m_tiles, int64_t n_tiles) {
 
 template <int EPI, int BMv, int BNv, int STv, int KS = 64>
 hipError_t launch_bf16(hipStream_t s, const GemmArgs& g, int64_t m_tiles) {
-    const int opt = (EPI == EPI_SWIGLU) ? BNv / 2 : BNv;
+    const int opt = epi_pairs(EPI) ? BNv / 2 : BNv;
     const int n_tiles = (g.N + opt - 1) / opt;
     if (g.k_split > (g.K + BK - 1) / BK) return hipErrorInvalidValue;   // each K chunk needs a stage
     if (g.b_tiled && (KS != kTileK || kTileRows % BNv != 0)) return hipErrorInvalidValue;
@@ -568,10 +652,14 @@ hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64
         if (bm == 64) return launch_bf16<EPI, 64, 128, 5>(s, g, m_tiles);
         return launch_bf16<EPI, 128, 256, 3>(s, g, m_tiles);
     }
-    const int opt = (EPI == EPI_SWIGLU) ? FBN / 2 : FBN;
-    dim3 grid((unsigned)((g.N + opt - 1) / opt), (unsigned)m_tiles);
-    hipLaunchKernelGGL(gemm_f32<EPI>, grid, dim3(256), 0, s, g);
-    return hipGetLastError();
+    if constexpr (EPI > EPI_DOWN_F32) {
+        return hipErrorInvalidValue;   // the backward epilogues are bf16 only
+    } else {
+        const int opt = (EPI == EPI_SWIGLU) ? FBN / 2 : FBN;
+        dim3 grid((unsigned)((g.N + opt - 1) / opt), (unsigned)m_tiles);
+        hipLaunchKernelGGL(gemm_f32<EPI>, grid, dim3(256), 0, s, g);
+        return hipGetLastError();
+    }
 }
 
 }  // namespace
@@ -646,8 +734,17 @@ hipError_t launch_gemm(hipStream_t s, int dtype, int bm, int epi, const GemmArgs
         case EPI_SWIGLU: return launch_one<EPI_SWIGLU>(s, dtype, bm, g, m_tiles);
         case EPI_GELU: return launch_one<EPI_GELU>(s, dtype, bm, g, m_tiles);
         case EPI_DOWN_SCALED: return launch_one<EPI_DOWN_SCALED>(s, dtype, bm, g, m_tiles);
+        case EPI_SWIGLU_SAVE: return launch_one<EPI_SWIGLU_SAVE>(s, dtype, bm, g, m_tiles);
+        case EPI_GELU_SAVE: return launch_one<EPI_GELU_SAVE>(s, dtype, bm, g, m_tiles);
+        case EPI_DH_SWIGLU: return launch_one<EPI_DH_SWIGLU>(s, dtype, bm, g, m_tiles);
+        case EPI_DH_GELU: return launch_one<EPI_DH_GELU>(s, dtype, bm, g, m_tiles);
         default: return launch_one<EPI_DOWN_F32>(s, dtype, bm, g, m_tiles);
     }
+}
+
+int gemm_part_cols(int bm, int64_t N) {
+    const int bnb = bm == 64 ? 128 : 256;   // the B rows of that tile height's config
+    return (int)((N + bnb - 1) / bnb) * (bnb / 64);
 }
 
 }  // namespace moe

@@ -310,6 +310,11 @@ size_t route_workspace(int dtype, int64_t T, int64_t D, int64_t M) {
            align256((size_t)route_ksplit(T, D, M) * T * 3 * M * 4) + (size_t)T * M * 4;
 }
 
+size_t route_logits_offset(int dtype, int64_t T, int64_t D, int64_t M) {
+    if (dtype != 1) return 0;
+    return align256((size_t)3 * M * D * 2) + align256((size_t)route_ksplit(T, D, M) * T * 3 * M * 4);
+}
+
 hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, const float* W_r,
                         const float* bias, int32_t* idx, float* w, int64_t T, int64_t D,
                         int64_t M, int k, int renorm, float alpha, float eps, int n_group,

@@ -182,3 +182,19 @@ def test_group_routing_validation(ng, tg, status):
     d = B.make_desc(workloads.GLM45_PREFILL, M=1024, n_group=128, topk_group=4)
     assert B.load_library().moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) \
         == B.MOE_ERR_UNSUPPORTED
+
+
+def test_backward_workspace_and_unsupported_layers():
+    lib = B.load_library()
+    cfg = workloads.shrink(workloads.GLM45_PREFILL, T=200, D=128, F=96, F_shared=96)
+    d = B.make_desc(cfg)
+    n = B.moe_backward_workspace_size(d)
+    S, Spad = cfg.T * cfg.k, ((cfg.T * cfg.k + 64 * cfg.M + 63) // 64) * 64
+    # at least the padded transposed operands of the weight gradients
+    assert n >= 2 * Spad * (cfg.D + cfg.F + 2 * cfg.F + cfg.D)
+    out = ctypes.c_size_t(5)
+    for kw in ({"dtype": "f32"}, {"weight_layout": "tiled"}):
+        d2 = B.make_desc(cfg, **kw)
+        rc = lib.moe_backward_workspace_size(ctypes.byref(d2), ctypes.byref(out))
+        assert rc == B.MOE_ERR_UNSUPPORTED, B.last_error_detail()
+        assert out.value == 5
