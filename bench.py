@@ -159,6 +159,87 @@ def cpu_baseline(cfg, t, target_s: float):
                       f"forward in fp64, {dt:.1f} s"}
 
 
+def backward_work(cfg, U):
+    """Algorithmic FLOPs and bytes per launch label of the backward: the
+    gradients with respect to inputs and weights of every GEMM of the forward
+    (2x its active FLOPs); the recomputed up projection and router are not
+    credited.  Bytes: the touched experts' weights read for the input
+    gradients and the weight gradients written (fp32)."""
+    esz = 2
+    T, D, M, F, k, Fs, G = cfg.T, cfg.D, cfg.M, cfg.F, cfg.k, cfg.F_shared, cfg.G
+    S = T * k
+    w = {
+        "b_dh": (2.0 * S * D * F + 2.0 * T * D * Fs, U * D * F * esz + Fs * D * esz),
+        "b_dx": (2.0 * S * G * F * D + 2.0 * T * 2 * Fs * D,
+                 U * G * F * D * esz + 2 * Fs * D * esz + (S + T) * D * 4),
+        "b_wgrad": (2.0 * S * D * F + 2.0 * S * G * F * D + 6.0 * T * Fs * D + 2.0 * T * D * M,
+                    (U * (G + 1) * F * D + 3 * Fs * D + M * D) * 4),
+    }
+    flops = sum(v[0] for v in w.values())
+    return w, flops
+
+
+def bench_backward(args):
+    """One JSON line for the layer backward at the workload: steps of
+    moe_backward over HBM-resident inputs and dy."""
+    import torch
+
+    import workloads
+    from sparse_mixture_experts_15_amd import binding as B
+    from sparse_mixture_experts_15_amd.layer import MoELayer
+
+    cfg = workloads.get(args.config)
+    t = workloads.generate(cfg, seed=args.seed, device="cuda")
+    L = MoELayer(B.make_desc(cfg, weight_layout="rows"))
+    d = L.desc
+    ws = torch.empty(B.moe_backward_workspace_size(d), dtype=torch.uint8, device="cuda")
+    g = B.backward_grads(d, biases=t.get("b1") is not None)
+    gen = torch.Generator(device="cuda").manual_seed(args.seed + 1)
+    dy = torch.randn(cfg.T, cfg.D, generator=gen, device="cuda").to(torch.bfloat16)
+
+    def step():
+        B.moe_backward(L.handle, d, t["x"], t["W_r"], t["bias"], t["W1"], t.get("b1"), t["W2"],
+                       t.get("b2"), t.get("Wsh_gu"), t.get("Wsh_dn"), dy, g, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    counts = g["load_count"].cpu().tolist()
+    U = sum(1 for c in counts if c > 0)
+    kw, flops = backward_work(cfg, U)
+    nprof = min(args.steps, 5)
+    B.moe_profile_start(L.handle, 64 * nprof, None)
+    for _ in range(nprof):
+        step()
+    B.moe_profile_stop(L.handle)
+    split = {k: v[1] / nprof for k, v in B.moe_profile_results(L.handle).items()}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    dom = max((k for k in split if k in kw), key=split.get)
+    fl, by = kw[dom]
+    out = {
+        "metric": "MoE layer backward tokens/s + TFLOP/s of the input and weight gradients",
+        "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "pass": "backward", "touched_experts": U,
+                   "weights": "rows"},
+        "gradient_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "kernel_ms_per_step": {k: round(v, 4) for k, v in split.items()},
+        "roofline": {"bound": "mfma", "kernel": dom, "kernel_ms": round(split[dom], 4),
+                     "achieved": round(fl / (split[dom] * 1e-3) / 1e12, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(fl / (split[dom] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "alg_flops": fl, "alg_bytes": by},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +254,8 @@ def main():
                     help="expert/shared weight layout (tiled: copied once before timing)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the layer backward (moe_backward) instead of the forward")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -182,6 +265,9 @@ def main():
 
     if args.calib_copy:
         calib_copy()
+        return
+    if args.backward:
+        bench_backward(args)
         return
 
     import torch
