@@ -417,8 +417,7 @@ struct BwdPlan {
     Plan f;
     int64_t S = 0, G = 1, Spad = 0, Tp = 0;
     int part_ld = 0, bm_w2 = 0, bm_w1 = 0, bm_sh2 = 0, bm_sh1 = 0, bm_r = 0;
-    size_t Z = 0, dZ = 0, part = 0, Zsh = 0, dZsh = 0, W1T = 0, W2T = 0, WshguT = 0,
-           WshdnT = 0, poff = 0, pad_row = 0, pad_tok = 0, dOT = 0, HT = 0, dZT = 0, XT = 0,
+    size_t Z = 0, dZ = 0, part = 0, Zsh = 0, dZsh = 0, poff = 0, pad_row = 0, pad_tok = 0, dOT = 0, HT = 0, dZT = 0, XT = 0,
            xT = 0, dyT = 0, HshT = 0, dZshT = 0, dl = 0, gate = 0, dlT3 = 0, C3 = 0, total = 0;
 };
 
@@ -448,10 +447,6 @@ BwdPlan make_bwd_plan(const moe_desc* d) {
     b.part = take(b.S * b.part_ld * 4);
     b.Zsh = take(T * 2 * Fs * 2);
     b.dZsh = take(T * 2 * Fs * 2);
-    b.W1T = take(M * D * GF * 2);
-    b.W2T = take(M * F * D * 2);
-    b.WshguT = take(D * 2 * Fs * 2);
-    b.WshdnT = take(Fs * D * 2);
     b.poff = take((M + 1) * 4);
     b.pad_row = take(b.Spad * 4);
     b.pad_tok = take(b.Spad * 4);
@@ -466,7 +461,7 @@ BwdPlan make_bwd_plan(const moe_desc* d) {
     b.dl = take(T * M * 4);
     b.gate = take(T * M * 4);
     b.dlT3 = take(3 * M * b.Tp * 2);
-    b.C3 = take(3 * M * D * 4);
+    b.C3 = take(std::max(3 * M * D, ((T + 255) / 256) * M) * 4);
     b.total = off;
     return b;
 }
@@ -530,8 +525,6 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
     void* Z = at<char>(ws, b.Z);
     void* dZ = at<char>(ws, b.dZ);
     float* part = at<float>(ws, b.part);
-    void* W1T = at<char>(ws, b.W1T);
-    void* W2T = at<char>(ws, b.W2T);
     int32_t* poff = at<int32_t>(ws, b.poff);
     int32_t* pad_row = at<int32_t>(ws, b.pad_row);
     int32_t* pad_tok = at<int32_t>(ws, b.pad_tok);
@@ -556,16 +549,6 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
         return launch_tile_table(s, offsets, M, tt, ntables, sorted_slot, w, S, row_scale, 0,
                                  sorted_token);
     }));
-    // weights transposed for the input-gradient GEMMs: W2T[e] = W2[e]^T [F, D],
-    // W1T[e] = W1[e]^T [D, G F]
-    TRY(run(h, s, L_B_TRANSPOSE, [&] {
-        hipError_t e = launch_transpose(s, W2, F, D, D * F, nullptr, nullptr, nullptr, F, D, W2T,
-                                        D, F * D, (int)M);
-        if (e != hipSuccess) return e;
-        return launch_transpose(s, W1, D, GF, GF * D, nullptr, nullptr, nullptr, D, GF, W1T, GF,
-                                D * GF, (int)M);
-    }));
-
     // 1. up projection again, keeping the pre-activations Z (bf16)
     GemmArgs up{};
     up.a = x;
@@ -593,8 +576,9 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
     //    weight) and the per-tile dots H . dH_raw for the router
     GemmArgs dh = up;
     dh.a = dy;
-    dh.b = W2T;
-    dh.b_stride = F * D;
+    dh.b = W2;             // read in place as [K = D, N = F]
+    dh.b_kn = 1;
+    dh.b_stride = D * F;
     dh.bias = nullptr;
     dh.c = dZ;
     dh.c2 = Z;
@@ -611,8 +595,9 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
     // 3. expert rows' input gradients dXs = dZ W1[e] (fp32, sorted order)
     GemmArgs dxg{};
     dxg.a = dZ;
-    dxg.b = W1T;
-    dxg.b_stride = D * GF;
+    dxg.b = W1;            // read in place as [K = G F, N = D]
+    dxg.b_kn = 1;
+    dxg.b_stride = GF * D;
     dxg.c = dXs;
     dxg.tiles = tiles_dn;
     dxg.offsets = offsets;
@@ -631,15 +616,6 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
     if (Fs > 0) {
         void* Zsh = at<char>(ws, b.Zsh);
         void* dZsh = at<char>(ws, b.dZsh);
-        void* WshguT = at<char>(ws, b.WshguT);
-        void* WshdnT = at<char>(ws, b.WshdnT);
-        TRY(run(h, s, L_B_TRANSPOSE, [&] {
-            hipError_t e = launch_transpose(s, Wsh_dn, Fs, D, 0, nullptr, nullptr, nullptr, Fs, D,
-                                            WshdnT, D, 0, 1);
-            if (e != hipSuccess) return e;
-            return launch_transpose(s, Wsh_gu, D, 2 * Fs, 0, nullptr, nullptr, nullptr, D, 2 * Fs,
-                                    WshguT, 2 * Fs, 0, 1);
-        }));
         const int64_t mt_up = (T + p.bm_sh_up - 1) / p.bm_sh_up;
         const int64_t mt_dn = (T + p.bm_sh_dn - 1) / p.bm_sh_dn;
         GemmArgs su = dense_args(x, Wsh_gu, Hsh, T, 2 * Fs, D, Fs);
@@ -648,12 +624,16 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
         TRY(run(h, s, L_B_UP, [&] {
             return launch_gemm(s, 1, p.bm_sh_up, EPI_SWIGLU_SAVE, su, mt_up);
         }));
-        GemmArgs sd = dense_args(dy, WshdnT, dZsh, T, Fs, D, Fs);
+        GemmArgs sd = dense_args(dy, Wsh_dn, dZsh, T, Fs, D, Fs);
+        sd.b_kn = 1;
+        sd.b_stride = D * Fs;
         sd.c2 = Zsh;
         TRY(run(h, s, L_B_DH, [&] {
             return launch_gemm(s, 1, p.bm_sh_up, EPI_DH_SWIGLU, sd, mt_up);
         }));
-        GemmArgs sx = dense_args(dZsh, WshguT, dXsh, T, D, 2 * Fs, D);
+        GemmArgs sx = dense_args(dZsh, Wsh_gu, dXsh, T, D, 2 * Fs, D);
+        sx.b_kn = 1;
+        sx.b_stride = 2 * Fs * D;
         TRY(run(h, s, L_B_DX, [&] { return launch_gemm(s, 1, p.bm_sh_dn, EPI_DOWN_F32, sx, mt_dn); }));
     }
 
@@ -666,7 +646,8 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
         e = launch_bwd_combine(s, dXs, slot_row, dXsh, dl, idx, W_r, T, d->k, M, D,
                                d->scorer == MOE_SCORER_SIGMOID, dx);
         if (e != hipSuccess) return e;
-        return launch_load_stats(s, gate, T, M, counts, load_count, load_score);
+        // the split-plane router product's buffer C3 serves as scratch here
+        return launch_load_stats(s, gate, T, M, counts, C3, load_count, load_score);
     }));
 
     // 6. weight gradients: per-expert padded, transposed operands, one

@@ -12,8 +12,8 @@
 //  - pad layout: each expert's sorted rows padded to a multiple of 64 so
 //    the weight-gradient GEMMs contract over whole K stages per expert;
 //  - transpose: row-major [rows, C] -> [C, positions], optionally gathered,
-//    scaled and zero-padded (the weight-gradient operands, and the weights
-//    transposed for the input-gradient GEMMs);
+//    scaled and zero-padded (the weight-gradient operands; the input-
+//    gradient GEMMs read the weights in place, as [K, N] B operands);
 //  - router backward: per token, the weights' gradient dw_j = dy . E_j(x)
 //    (summed from the GEMM epilogue's per-tile dots) through the
 //    renormalisation and the gate values to the logits;
@@ -27,7 +27,7 @@
 namespace moe {
 namespace {
 
-constexpr int kT = 64;   // transpose tile (positions x columns)
+constexpr int kT = 64;   // transpose tile (positions x columns); 128 measured no faster
 
 // out[b][c * ld_out + p] = scale(r1) * src[b][r2 * ld_src + c] for p < P,
 // c < C, where r1 = idx1 ? idx1[p] : p, r2 = idx2 ? idx2[r1] : r1; a position
@@ -40,13 +40,15 @@ __global__ __launch_bounds__(256) void transpose_bf16(
     const float* __restrict__ scale, int64_t C, int64_t P, bf16_t* __restrict__ out,
     int64_t ld_out, int64_t out_bstride) {
     __shared__ bf16_t s[kT][kT + 8];
+    constexpr int CH = kT / 8;            // 16-byte chunks per tile row
+    constexpr int RPI = 256 / CH;         // tile rows per pass of the 256 threads
     const int tid = threadIdx.x;
     const int64_t pb = (int64_t)blockIdx.x * kT, cb = (int64_t)blockIdx.y * kT;
     src += (int64_t)blockIdx.z * src_bstride;
     out += (int64_t)blockIdx.z * out_bstride;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int pl = tid / 8 + 32 * it, c8 = (tid % 8) * 8;
+    for (int it = 0; it < kT / RPI; ++it) {
+        const int pl = tid / CH + RPI * it, c8 = (tid % CH) * 8;
         const int64_t p = pb + pl, c = cb + c8;
         u32x4 v = {0u, 0u, 0u, 0u};
         if (p < P && c < C) {
@@ -73,8 +75,8 @@ __global__ __launch_bounds__(256) void transpose_bf16(
     }
     __syncthreads();
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int cl = tid / 8 + 32 * it, p8 = (tid % 8) * 8;
+    for (int it = 0; it < kT / RPI; ++it) {
+        const int cl = tid / CH + RPI * it, p8 = (tid % CH) * 8;
         const int64_t c = cb + cl, p = pb + p8;
         if (c >= C || p >= P) continue;
         u32x4 v;
@@ -313,16 +315,33 @@ __global__ __launch_bounds__(256) void seg_colsum(const bf16_t* __restrict__ src
     out[i] = acc;
 }
 
-// Load statistics: score[e] = sum over tokens of gate[t][e] (in token
-// order); count[e] copied from the dispatch counts.
-__global__ __launch_bounds__(256) void load_stats(const float* __restrict__ gate, int T, int M,
-                                                  const int32_t* __restrict__ counts,
+// Load statistics, deterministically in two passes: partial[c][e] = sum of
+// gate[t][e] over token chunk c of 256 (four 64-token runs added in order),
+// then score[e] = sum over chunks in order; count[e] copied from the
+// dispatch counts.
+__global__ __launch_bounds__(256) void load_partial(const float* __restrict__ gate, int T, int M,
+                                                    float* __restrict__ partial) {
+    __shared__ float s_p[4][64];
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int e = blockIdx.y * 64 + tx;
+    const int t0 = blockIdx.x * 256 + ty * 64;
+    float acc = 0.f;
+    if (e < M)
+        for (int i = 0; i < 64 && t0 + i < T; ++i) acc += gate[(int64_t)(t0 + i) * M + e];
+    s_p[ty][tx] = acc;
+    __syncthreads();
+    if (ty == 0 && e < M)
+        partial[(int64_t)blockIdx.x * M + e] = ((s_p[0][tx] + s_p[1][tx]) + s_p[2][tx]) + s_p[3][tx];
+}
+
+__global__ __launch_bounds__(256) void load_stats(const float* __restrict__ partial, int chunks,
+                                                  int M, const int32_t* __restrict__ counts,
                                                   int32_t* __restrict__ count_out,
                                                   float* __restrict__ score) {
     const int e = blockIdx.x * 256 + threadIdx.x;
     if (e >= M) return;
     float acc = 0.f;
-    for (int t = 0; t < T; ++t) acc += gate[(int64_t)t * M + e];
+    for (int c = 0; c < chunks; ++c) acc += partial[(int64_t)c * M + e];
     score[e] = acc;
     count_out[e] = counts[e];
 }
@@ -413,9 +432,13 @@ hipError_t launch_seg_colsum(hipStream_t s, const void* src, int64_t ld, const i
 }
 
 hipError_t launch_load_stats(hipStream_t s, const float* gate, int64_t T, int64_t M,
-                             const int32_t* counts, int32_t* count_out, float* score) {
-    hipLaunchKernelGGL(load_stats, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, gate, (int)T,
-                       (int)M, counts, count_out, score);
+                             const int32_t* counts, float* partial, int32_t* count_out,
+                             float* score) {
+    const int chunks = (int)((T + 255) / 256);
+    hipLaunchKernelGGL(load_partial, dim3((unsigned)chunks, (unsigned)((M + 63) / 64)), dim3(256),
+                       0, s, gate, (int)T, (int)M, partial);
+    hipLaunchKernelGGL(load_stats, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, partial,
+                       chunks, (int)M, counts, count_out, score);
     return hipGetLastError();
 }
 

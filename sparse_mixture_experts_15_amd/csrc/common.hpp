@@ -120,6 +120,7 @@ struct GemmArgs {
                               // [rows, N] partial at c + chunk * rows * N (0 = 1)
     int group_m;              // m-tiles per group of the tile order (0 = 4)
     int b_tiled;              // b holds tiled blocks (bf16): b_stride = one expert's blocks
+    int b_kn;                 // b[e] is [K, N] row-major (b_stride = K * N); bf16, K = 64 stages
     int xcd_mode;             // workgroup order: 0 groups dealt to XCDs in turn, 1 plain,
                               // 2 contiguous slices per XCD
     const void* b_extra;      // grouped: weights of group extra_group, in place of
@@ -232,8 +233,10 @@ hipError_t launch_sum3(hipStream_t s, const float* a, const float* b, const floa
 hipError_t launch_seg_colsum(hipStream_t s, const void* src, int64_t ld, const int32_t* offsets,
                              const int32_t* gather, const float* row_scale, int64_t M, int64_t C,
                              float* out);
+// partial: ceil(T / 256) x M floats of scratch
 hipError_t launch_load_stats(hipStream_t s, const float* gate, int64_t T, int64_t M,
-                             const int32_t* counts, int32_t* count_out, float* score);
+                             const int32_t* counts, float* partial, int32_t* count_out,
+                             float* score);
 hipError_t launch_fill_zero(hipStream_t s, float* p, int64_t n);
 
 // Rows per m-tile of a GEMM for a dtype, given its total rows, the number of

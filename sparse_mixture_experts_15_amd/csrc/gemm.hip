@@ -243,8 +243,44 @@ __device__ __forceinline__ void dh_epilogue(const GemmArgs& g, const Tile& tl,
 // One tile configuration: BM A rows x BNB B rows per workgroup, STAGES LDS
 // stages of K = KS (64 or 32); the eight waves form WM x WN with 64 B rows
 // per wave.
-template <int EPI, int BM, int BNB, int STAGES, int KS>
+// KN-layout B operand (BKN): B[e] is stored [K][N] row-major (the layout
+// the backward finds the weights in: W2[e] = [D][F] against dy, W1[e] =
+// [G F][D] against dZ), so no transposed copy is made.  A stage's B tile is
+// 64 K-rows of BNB columns in LDS, 16-byte chunk c of row k stored at chunk
+// c ^ kn_swz(k); the MFMA B fragments (8 consecutive k of one column per
+// lane) come from pairs of ds_read_b64_tr_b16.  That instruction works on
+// groups of 16 lanes: lane i of a group receives element i % 4 of the
+// 8-byte pieces addressed by lanes 4 j + i / 4 (j = 0..3) of its group, so
+// lane 4 j + q addressing columns n0 + 4 q .. +3 of k-row k0 + j hands lane
+// i the four k values k0 .. k0 + 3 of column n0 + i (measured on gfx950).
+template <int BNB>
+__device__ __forceinline__ int kn_swz(int krow) {
+    return (krow % (BNB / 16)) * 2;   // even: keeps a fragment's two chunks adjacent
+}
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t* lds_s4_ptr;
+
+template <int BNB>
+__device__ __forceinline__ bf16x8 kn_fragment(const bf16_t* bt, int kbase, int n0, int lane) {
+    const int grp = lane >> 4, L = lane & 15, q = L & 3, jr = L >> 2;
+    const int n = n0 + 4 * q;
+    const int c = n >> 3, half = (n >> 2) & 1;
+    short4_t v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int k = kbase + 8 * grp + 4 * h + jr;
+        const bf16_t* p = bt + k * BNB + ((c ^ kn_swz<BNB>(k)) << 3) + half * 4;
+        v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)p);
+    }
+    typedef short short8_t __attribute__((ext_vector_type(8)));
+    const short8_t r = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+template <int EPI, int BM, int BNB, int STAGES, int KS, int BKN = 0>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int n_tiles) {
+    static_assert(!BKN || (KS == 64 && !epi_pairs(EPI)), "KN-layout B: K = 64 stages, no pairing");
     constexpr int BK = KS;
     constexpr int CPR = BK / 8;                        // 16-byte chunks per row
     constexpr int ROWS_PER_LOAD = 1024 / (BK * 2);     // rows per 1 KB wave load
@@ -299,7 +335,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     const bf16_t* Bp = (g.b_extra && tl.e == g.extra_group)
                            ? static_cast<const bf16_t*>(g.b_extra)
                            : static_cast<const bf16_t*>(g.b) + (int64_t)tl.e * g.b_stride;
-    const i32x4 rb = make_rsrc(Bp, (uint32_t)((g.b_tiled ? g.b_stride : (int64_t)g.b_rows * K) * 2));
+    const i32x4 rb = make_rsrc(
+        Bp, (uint32_t)((g.b_tiled || BKN ? g.b_stride : (int64_t)g.b_rows * K) * 2));
     // tiled weights: stage kt of a 256-row weight tile is one contiguous
     // block of 256 LDS-image rows; a 128-row n-tile takes half of one
     constexpr uint32_t TILE_STAGE = kTileRows * BK * 2;
@@ -324,6 +361,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             if (ins < LOADS && r < tl.rend)
                 off = (uint32_t)((g.gather ? (int64_t)g.gather[r] : r) * K * 2);
             rowoff[q] = off;
+        } else if (BKN) {
+            // k-row kn_row(q) of the stage, stored chunk lane % CPRn holding
+            // the logical chunk given by the swizzle; column base per lane
+            constexpr int CPRn = BNB / 8, RPLn = 64 / CPRn;
+            const int krow = RPLn * ins + lane / CPRn;
+            const int col = n_base + ((lane % CPRn) ^ kn_swz<BNB>(krow)) * 8;
+            rowoff[q] = col < N ? (uint32_t)krow * (uint32_t)N * 2u + (uint32_t)col * 2u : kOOB;
         } else {
             const int row = ROWS_PER_LOAD * ins + lrow;
             int oc, br;
@@ -340,6 +384,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             // an invalid row stays >= kOOB (offsets are < 2^31); a K-tail chunk -> kOOB
             uint32_t off = rowoff[q] + (uint32_t)kc * 2u;
             off = kc < K ? off : kOOB;
+            if (BKN && q < QB) {   // KN-layout B: whole k-rows of the stage
+                constexpr int CPRn = BNB / 8, RPLn = 64 / CPRn;
+                const int krow = kt * BK + RPLn * ins + lane / CPRn;
+                off = krow < K ? rowoff[q] + (uint32_t)(kt * BK) * (uint32_t)N * 2u : kOOB;
+            }
             if (q < QB && g.b_tiled)
                 off = tile_base + (uint32_t)kt * TILE_STAGE + (uint32_t)ins * 1024u + lane * 16u;
             if (q < QB)
@@ -395,9 +444,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
                     af[kk][i] = *reinterpret_cast<const bf16x8*>(
                         st + swz<BK>(wm * WROWS + 16 * i + fr, kk * 4 + fc));
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    bfr[kk][j] = *reinterpret_cast<const bf16x8*>(
-                        st + BM * BK + swz<BK>(wn * 64 + 16 * j + fr, kk * 4 + fc));
+                for (int j = 0; j < TN; ++j) {
+                    if constexpr (BKN)
+                        bfr[kk][j] = kn_fragment<BNB>(st + BM * BK, kk * 32, wn * 64 + 16 * j, lane);
+                    else
+                        bfr[kk][j] = *reinterpret_cast<const bf16x8*>(
+                            st + BM * BK + swz<BK>(wn * 64 + 16 * j + fr, kk * 4 + fc));
+                }
             }
 #pragma unroll
             for (int kk = 0; kk < BK / 32; ++kk)
@@ -422,7 +475,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int row = wn * 64 + 16 * j + fr;
-                    bfr[j] = *reinterpret_cast<const bf16x8*>(st + BM * BK + swz<BK>(row, kk * 4 + fc));
+                    if constexpr (BKN)
+                        bfr[j] = kn_fragment<BNB>(st + BM * BK, kk * 32, wn * 64 + 16 * j, lane);
+                    else
+                        bfr[j] = *reinterpret_cast<const bf16x8*>(
+                            st + BM * BK + swz<BK>(row, kk * 4 + fc));
                 }
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
@@ -630,14 +687,15 @@ int64_t grid_tiles(const GemmArgs& g, int64_t m_tiles, int64_t n_tiles) {
     return ((groups + 7) / 8) * 8 * gm * n_tiles;
 }
 
-template <int EPI, int BMv, int BNv, int STv, int KS = 64>
+template <int EPI, int BMv, int BNv, int STv, int KS = 64, int BKN = 0>
 hipError_t launch_bf16(hipStream_t s, const GemmArgs& g, int64_t m_tiles) {
     const int opt = epi_pairs(EPI) ? BNv / 2 : BNv;
     const int n_tiles = (g.N + opt - 1) / opt;
     if (g.k_split > (g.K + BK - 1) / BK) return hipErrorInvalidValue;   // each K chunk needs a stage
     if (g.b_tiled && (KS != kTileK || kTileRows % BNv != 0)) return hipErrorInvalidValue;
     const int64_t total = grid_tiles(g, m_tiles, n_tiles);
-    hipLaunchKernelGGL((gemm_bf16<EPI, BMv, BNv, STv, KS>), dim3((unsigned)total), dim3(NT), 0, s, g,
+    if (BKN && g.b_tiled) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_bf16<EPI, BMv, BNv, STv, KS, BKN>), dim3((unsigned)total), dim3(NT), 0, s, g,
                        (int)m_tiles, n_tiles);
     return hipGetLastError();
 }
@@ -646,6 +704,16 @@ template <int EPI>
 hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64_t m_tiles) {
     if (m_tiles <= 0) return hipSuccess;
     if (dtype == 1) {
+        if constexpr (EPI == EPI_DH_SWIGLU || EPI == EPI_DH_GELU || EPI == EPI_DOWN_F32) {
+            if (g.b_kn) {
+                if (bm == 256) return launch_bf16<EPI, 256, 256, 2, 64, 1>(s, g, m_tiles);
+                if (bm == 160) return launch_bf16<EPI, 160, 256, 3, 64, 1>(s, g, m_tiles);
+                if (bm == 64) return launch_bf16<EPI, 64, 128, 5, 64, 1>(s, g, m_tiles);
+                return launch_bf16<EPI, 128, 256, 3, 64, 1>(s, g, m_tiles);
+            }
+        } else {
+            if (g.b_kn) return hipErrorInvalidValue;
+        }
         // (256 x 256 with K = 32 stages, 4 or 5 deep, measured slower than 2 x 64)
         if (bm == 256) return launch_bf16<EPI, 256, 256, 2>(s, g, m_tiles);
         if (bm == 160) return launch_bf16<EPI, 160, 256, 3>(s, g, m_tiles);
