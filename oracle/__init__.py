@@ -74,7 +74,7 @@ def _load():
         lib.oracle_forward.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp,
                                        vp, vp, vp]
         lib.oracle_backward.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                        vp, vp, vp, vp, vp, vp, vp, vp]
+                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, i64]
         lib.oracle_num_threads.restype = ctypes.c_int
         for f in ("oracle_route", "oracle_dispatch", "oracle_expert", "oracle_shared",
                   "oracle_layer", "oracle_forward", "oracle_backward"):
@@ -232,26 +232,37 @@ def forward(cfg, h, tokens=None):
     return idx, w, y
 
 
-def backward(cfg, h, dy):
+def backward(cfg, h, dy, experts=None):
     """Gradient of forward() over all T tokens for the output gradient
     dy[T,D] (any float array, used in fp64).  Returns a dict of fp64 arrays:
     dx[T,D], dW_r[M,D], dW1 / dW2 (and db1 / db2 when the layer has biases,
     dWsh_gu / dWsh_dn when it has a shared expert) in their weights' shapes,
     and the load statistics load_count[M] (int64 slots per expert) and
-    load_score[M] (sum over tokens of each expert's gate value)."""
+    load_score[M] (sum over tokens of each expert's gate value).
+
+    ``experts`` (a list of expert ids) keeps the expert weight and bias
+    gradients of those experts only, stacked in list order (dW1 is then
+    [len(experts), G*F, D]); everything else is unchanged."""
     c = make_cfg(cfg)
     _check_storage(c, x=h["x"], W1=h["W1"], b1=h.get("b1"), W2=h["W2"], b2=h.get("b2"),
                    Wsh_gu=h.get("Wsh_gu"), Wsh_dn=h.get("Wsh_dn"))
     T, D, M, F, Fs = cfg.T, cfg.D, cfg.M, cfg.F, cfg.F_shared
     G = 2 if cfg.act == "swiglu" else 1
     dy = np.ascontiguousarray(dy, dtype=np.float64).reshape(T, D)
+    slot, Mg = None, M
+    if experts is not None:
+        slot = np.full(M, -1, np.int32)
+        for i, e in enumerate(experts):
+            assert 0 <= e < M and slot[e] < 0, "experts must be distinct ids below M"
+            slot[e] = i
+        Mg = len(experts)
     out = {"dx": np.zeros((T, D)), "dW_r": np.zeros((M, D)),
-           "dW1": np.zeros((M, G * F, D)), "dW2": np.zeros((M, D, F)),
+           "dW1": np.zeros((Mg, G * F, D)), "dW2": np.zeros((Mg, D, F)),
            "load_count": np.zeros(M, np.int64), "load_score": np.zeros(M)}
     if h.get("b1") is not None:
-        out["db1"] = np.zeros((M, F))
+        out["db1"] = np.zeros((Mg, F))
     if h.get("b2") is not None:
-        out["db2"] = np.zeros((M, D))
+        out["db2"] = np.zeros((Mg, D))
     if Fs > 0:
         out["dWsh_gu"] = np.zeros((2 * Fs, D))
         out["dWsh_dn"] = np.zeros((D, Fs))
@@ -261,7 +272,7 @@ def backward(cfg, h, dy):
         _ptr(h.get("Wsh_gu")), _ptr(h.get("Wsh_dn")), _ptr(dy), _ptr(out["dx"]),
         _ptr(out["dW_r"]), _ptr(out["dW1"]), _ptr(out.get("db1")), _ptr(out["dW2"]),
         _ptr(out.get("db2")), _ptr(out.get("dWsh_gu")), _ptr(out.get("dWsh_dn")),
-        _ptr(out["load_count"]), _ptr(out["load_score"]))
+        _ptr(out["load_count"]), _ptr(out["load_score"]), _ptr(slot), Mg)
     return out
 
 

@@ -444,11 +444,12 @@ static void add_outer(double* G, int64_t g0, int64_t rows, int64_t cols, const d
 }
 
 /* SwiGLU of width Fw on xv with output gradient dout: accumulates the weight
- * gradients (same layouts as Wgu / Wdn, at offsets gu0 / dn0) and dx; returns
- * the forward output in out. */
+ * gradients (same layouts as Wgu / Wdn, at offsets ggu0 / gdn0 of dWgu /
+ * dWdn; NULL skips them) and dx; returns the forward output in out. */
 static void swiglu_backward(int32_t dtype, int64_t D, int64_t Fw, const void* Wgu, int64_t gu0,
                             const void* Wdn, int64_t dn0, const double* xv, const double* dout,
-                            double* out, double* dWgu, double* dWdn, double* dx)
+                            double* out, double* dWgu, int64_t ggu0, double* dWdn, int64_t gdn0,
+                            double* dx)
 {
     double* a = malloc(sizeof(double) * Fw);
     double* b = malloc(sizeof(double) * Fw);
@@ -471,14 +472,14 @@ static void swiglu_backward(int32_t dtype, int64_t D, int64_t Fw, const void* Wg
         dh[f] = acc;
     }
     if (dWdn)
-        add_outer(dWdn, dn0, D, Fw, dout, h);
+        add_outer(dWdn, gdn0, D, Fw, dout, h);
     for (int64_t f = 0; f < Fw; ++f) {
         da[f] = dh[f] * b[f] * silu_grad(a[f]);
         db[f] = dh[f] * silu(a[f]);
     }
     if (dWgu) {
-        add_outer(dWgu, gu0, Fw, D, da, xv);
-        add_outer(dWgu, gu0 + Fw * D, Fw, D, db, xv);
+        add_outer(dWgu, ggu0, Fw, D, da, xv);
+        add_outer(dWgu, ggu0 + Fw * D, Fw, D, db, xv);
     }
     for (int64_t f = 0; f < Fw; ++f)
         for (int64_t d = 0; d < D; ++d)
@@ -488,12 +489,13 @@ static void swiglu_backward(int32_t dtype, int64_t D, int64_t Fw, const void* Wg
 }
 
 /* GELU FFN W2 gelu(W1 x + b1) + b2 with output gradient dout (a null bias is
- * zero and gets no gradient). */
+ * zero and gets no gradient).  Weight and bias gradients go to expert slot
+ * ge of dW1 / db1 / dW2 / db2; ge < 0 skips them. */
 static void gelu_backward(int32_t dtype, int64_t D, int64_t Fw, const void* W1, int64_t w10,
                           const void* b1, int64_t b10, const void* W2, int64_t w20,
                           const void* b2, int64_t b20, const double* xv, const double* dout,
-                          double* out, double* dW1, double* db1, double* dW2, double* db2,
-                          double* dx)
+                          double* out, int64_t ge, double* dW1, double* db1, double* dW2,
+                          double* db2, double* dx)
 {
     double* z = malloc(sizeof(double) * Fw);
     double* h = malloc(sizeof(double) * Fw);
@@ -510,14 +512,16 @@ static void gelu_backward(int32_t dtype, int64_t D, int64_t Fw, const void* W1, 
             acc += elem(W2, dtype, w20 + d * Fw + f) * dout[d];
         dz[f] = acc * gelu_erf_grad(z[f]);
     }
-    add_outer(dW2, w20, D, Fw, dout, h);
-    if (b2)
-        for (int64_t d = 0; d < D; ++d)
-            db2[b20 + d] += dout[d];
-    add_outer(dW1, w10, Fw, D, dz, xv);
-    if (b1)
-        for (int64_t f = 0; f < Fw; ++f)
-            db1[b10 + f] += dz[f];
+    if (ge >= 0) {
+        add_outer(dW2, ge * D * Fw, D, Fw, dout, h);
+        if (b2)
+            for (int64_t d = 0; d < D; ++d)
+                db2[ge * D + d] += dout[d];
+        add_outer(dW1, ge * Fw * D, Fw, D, dz, xv);
+        if (b1)
+            for (int64_t f = 0; f < Fw; ++f)
+                db1[ge * Fw + f] += dz[f];
+    }
     for (int64_t f = 0; f < Fw; ++f)
         for (int64_t d = 0; d < D; ++d)
             dx[d] += elem(W1, dtype, w10 + f * D + d) * dz[f];
@@ -529,17 +533,18 @@ void oracle_backward(const moe_oracle_cfg* c, const void* x, const float* W_r,
                      const void* b2, const void* Wsh_gu, const void* Wsh_dn, const double* dy,
                      double* dx, double* dW_r, double* dW1, double* db1, double* dW2,
                      double* db2, double* dWsh_gu, double* dWsh_dn, int64_t* load_count,
-                     double* load_score)
+                     double* load_score, const int32_t* expert_slot, int64_t n_slots)
 {
     const int64_t T = c->T, D = c->D, M = c->M, F = c->F, Fs = c->F_shared;
     const int32_t k = c->k;
     const int64_t G = c->act == ORACLE_SWIGLU ? 2 : 1;
+    const int64_t Mg = expert_slot ? n_slots : M;   /* experts whose gradients are kept */
     memset(dx, 0, sizeof(double) * T * D);
     memset(dW_r, 0, sizeof(double) * M * D);
-    memset(dW1, 0, sizeof(double) * M * G * F * D);
-    memset(dW2, 0, sizeof(double) * M * D * F);
-    if (db1) memset(db1, 0, sizeof(double) * M * F);
-    if (db2) memset(db2, 0, sizeof(double) * M * D);
+    memset(dW1, 0, sizeof(double) * Mg * G * F * D);
+    memset(dW2, 0, sizeof(double) * Mg * D * F);
+    if (db1) memset(db1, 0, sizeof(double) * Mg * F);
+    if (db2) memset(db2, 0, sizeof(double) * Mg * D);
     if (Fs > 0) {
         memset(dWsh_gu, 0, sizeof(double) * 2 * Fs * D);
         memset(dWsh_dn, 0, sizeof(double) * D * Fs);
@@ -589,12 +594,14 @@ void oracle_backward(const moe_oracle_cfg* c, const void* x, const float* W_r,
             load_count[e] += 1;
             for (int64_t d = 0; d < D; ++d)
                 dout[d] = w[j] * dyt[d];
+            const int64_t ge = expert_slot ? expert_slot[e] : e;
             if (c->act == ORACLE_SWIGLU)
                 swiglu_backward(c->dtype, D, F, W1, e * 2 * F * D, W2, e * D * F, xv, dout, o,
-                                dW1, dW2, dxt);
+                                ge >= 0 ? dW1 : NULL, ge * 2 * F * D, ge >= 0 ? dW2 : NULL,
+                                ge * D * F, dxt);
             else
                 gelu_backward(c->dtype, D, F, W1, e * F * D, b1, e * F, W2, e * D * F, b2,
-                              e * D, xv, dout, o, dW1, db1, dW2, db2, dxt);
+                              e * D, xv, dout, o, ge, dW1, db1, dW2, db2, dxt);
             double acc = 0.0;
             for (int64_t d = 0; d < D; ++d)
                 acc += dyt[d] * o[d];
@@ -602,8 +609,8 @@ void oracle_backward(const moe_oracle_cfg* c, const void* x, const float* W_r,
         }
         /* shared expert, weight 1 */
         if (Fs > 0)
-            swiglu_backward(c->dtype, D, Fs, Wsh_gu, 0, Wsh_dn, 0, xv, dyt, o, dWsh_gu,
-                            dWsh_dn, dxt);
+            swiglu_backward(c->dtype, D, Fs, Wsh_gu, 0, Wsh_dn, 0, xv, dyt, o, dWsh_gu, 0,
+                            dWsh_dn, 0, dxt);
 
         /* weights -> gate values: w_j = alpha g_j / (sum_S g + eps), or alpha g_j */
         for (int64_t e = 0; e < M; ++e)

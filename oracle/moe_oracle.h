@@ -93,13 +93,17 @@ void oracle_forward(const moe_oracle_cfg* c, const void* x, const float* W_r,
  * the weights pass it through the renormalisation and the gate values to the
  * logits.  Per-expert load statistics of the same pass: load_count[e] slots
  * routed to e, load_score[e] the sum over tokens of e's gate value (softmax
- * probability or sigmoid score).  Single-threaded, for small shapes. */
+ * probability or sigmoid score).  expert_slot (nullable) keeps the expert
+ * weight and bias gradients of some experts only: expert e's go to slot
+ * expert_slot[e] of n_slots-expert arrays, none when it is negative (for
+ * large layers, where all M would not fit); NULL keeps all M in place.
+ * Single-threaded, for small shapes or few tokens. */
 void oracle_backward(const moe_oracle_cfg* c, const void* x, const float* W_r,
                      const float* bias, const void* W1, const void* b1, const void* W2,
                      const void* b2, const void* Wsh_gu, const void* Wsh_dn, const double* dy,
                      double* dx, double* dW_r, double* dW1, double* db1, double* dW2,
                      double* db2, double* dWsh_gu, double* dWsh_dn, int64_t* load_count,
-                     double* load_score);
+                     double* load_score, const int32_t* expert_slot, int64_t n_slots);
 
 /* Number of OpenMP threads the oracle will use. */
 int oracle_num_threads(void);

@@ -569,3 +569,21 @@ def test_backward_alpha_zero_is_shared_swiglu_only():
     db = dh * a * sg
     assert np.allclose(g["dx"], da @ Wg + db @ Wu, rtol=1e-12, atol=1e-12)
     assert np.allclose(g["dWsh_dn"], dy.T @ (a * sg * b), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_backward_expert_selection_is_a_slice(act):
+    """Keeping only some experts' weight gradients (for layers too large to
+    hold all M in fp64) returns exactly those experts' slices of the full
+    gradient, in list order, and leaves every other output unchanged."""
+    cfg, h, dy = _fd_case(scorer="sigmoid" if act == "swiglu" else "softmax", act=act, M=6, k=2,
+                          T=11, Fs=2 if act == "swiglu" else 0, biases=act == "gelu")
+    full = oracle.backward(cfg, h, dy)
+    pick = [4, 0, 3]
+    part = oracle.backward(cfg, h, dy, experts=pick)
+    for key in full:
+        if key in ("dW1", "dW2", "db1", "db2"):
+            assert part[key].shape == (len(pick),) + full[key].shape[1:]
+            assert np.array_equal(part[key], full[key][pick]), key
+        else:
+            assert np.array_equal(part[key], full[key]), key
