@@ -194,3 +194,67 @@ def tiled_weights(L, t):
         if t.get(name) is not None:
             t[name] = B.tile_weights(L.handle, L.desc, name, t[name])
     return t
+
+
+# ---- error allowances of the backward's weight gradients -------------------
+#
+# The backward saves the pre-activations in bf16 and rounds their gradient
+# dz to bf16 before the weight-gradient GEMM.  A rounding delta of a saved
+# pre-activation moves dz by up to |dh| * max|act''| * delta, which is far
+# more than 2^-8 |dz| where the activation's derivative is near zero (GELU'
+# vanishes near z = -0.75, SiLU' near a = -1.28).  The allowances below
+# bound that from the exact (fp64) intermediates; they are error allowances
+# computed with numpy from the same inputs, never expected values.
+
+GELU_D2_MAX = 2.0 / np.sqrt(2.0 * np.pi)   # max |GELU''| (at 0)
+SILU_D1_MAX = 1.0999                          # max |SiLU'| (near a = 2.4)
+SILU_D2_MAX = 0.5                             # max |SiLU''| (at 0)
+
+
+def dz_allowance(act, z, dh):
+    """Per-element error allowance of the pre-activation gradient of rows of
+    tokens.  z[n, F] (GELU, bias included) or z[n, 2F] (gate then up);
+    dh[n, F] = W2^T (w dy), both fp64 from exact inputs.  Each saved value
+    and dz itself carry one bf16 rounding (2^-9 relative; 2^-8 taken)."""
+    from scipy import special
+    r = BF16_REL
+    if act == "gelu":
+        g1 = special.ndtr(z) + z * np.exp(-0.5 * z * z) / np.sqrt(2.0 * np.pi)
+        dz = dh * g1
+        return np.abs(dh) * GELU_D2_MAX * r * np.abs(z) + r * np.abs(dz)
+    F = dh.shape[1]
+    a, b = z[:, :F], z[:, F:]
+    sg = special.expit(a)
+    s, s1 = a * sg, sg * (1.0 + a * (1.0 - sg))
+    da, db = dh * b * s1, dh * s
+    al_a = np.abs(dh) * (np.abs(s1) * r * np.abs(b) + np.abs(b) * SILU_D2_MAX * r * np.abs(a))
+    al_b = np.abs(dh) * SILU_D1_MAX * r * np.abs(a)
+    return np.concatenate([al_a + r * np.abs(da), al_b + r * np.abs(db)], axis=1)
+
+
+def ffn_grad_allowances(act, X, W1, b1, W2, dO):
+    """Allowances of one expert's weight gradients from the rows X[n, D] that
+    reach it (W1[GF, D], b1[F] or None, W2[D, F]) with down-projection output
+    gradients dO[n, D] (gate weight times dy): dW1 = sum_t dz_t x_t^T via
+    dz_allowance; dW2 = sum_t dO_t H_t^T, whose factors carry one bf16
+    rounding each (2^-8 together; 2^-7 taken) of every term, so
+    2^-7 sum_t |dO_t| |H_t|^T (terms of opposite sign may cancel in the sum,
+    their rounding errors do not).  Returns (allow_dW1[GF, D],
+    allow_dW2[D, F])."""
+    z = X @ W1.T
+    if b1 is not None:
+        z = z + b1
+    dh = dO @ W2
+    F = W2.shape[1]
+    if act == "gelu":
+        H = 0.5 * z * (1.0 + _erf(z / np.sqrt(2.0)))
+    else:
+        a = z[:, :F]
+        H = a / (1.0 + np.exp(-a)) * z[:, F:]
+    return (dz_allowance(act, z, dh).T @ np.abs(X),
+            2.0 * BF16_REL * (np.abs(dO).T @ np.abs(H)))
+
+
+def _erf(v):
+    from scipy import special
+    return special.erf(v)

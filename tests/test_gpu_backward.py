@@ -8,7 +8,8 @@ import torch
 import oracle
 import workloads
 from sparse_mixture_experts_15_amd import binding as B
-from tests.gpu_util import check_route, new_layer, run_route, to_np
+from tests.gpu_util import (TIE_GAP, check_route, new_layer, run_route, to_np,
+                            ffn_grad_allowances, widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,27 +71,13 @@ def test_backward_parity(name):
     ref = oracle.backward(cfg, h, dy.float().cpu().numpy().astype(np.float64))
     assert (to_np(g["load_count"]) == ref["load_count"]).all()
     assert np.allclose(to_np(g["load_score"]), ref["load_score"], rtol=1e-5, atol=1e-5)
+    allow = _ffn_allowances(cfg, h, idx_o, w_o, dy.float().cpu().numpy(), range(cfg.M))
     report = {}
-    # The kernels round H, the pre-activations, dZ and w dy to bf16 once
-    # each (2^-9 relative) and accumulate in fp32: the gradients' RMS error is
-    # ~1-1.3 x 2^-9 of their RMS (measured 0.14-0.26%), and an element carries
-    # at most about two such roundings of its own size (a one-row weight
-    # gradient is a single product): every element must be within
-    # 3e-2 x RMS (~12 x the RMS error: the extreme of thousands of elements'
-    # accumulated rounding noise, with margin) + 2^-7 x |ref| (two bf16
-    # roundings of its own size, with margin).  A missing or wrong term shows
-    # as an O(1) error.
     for key in ref:
         if key.startswith("load"):
             continue
         got = to_np(g[key]).astype(np.float64).reshape(ref[key].shape)
-        mx, rm = _ratio(got, ref[key])
-        report[key] = (mx, rm)
-        nz = ref[key] != 0
-        scale = float(np.sqrt(np.mean(ref[key][nz] ** 2))) if nz.any() else 1.0
-        bound = 3e-2 * scale + 2.0 ** -7 * np.abs(ref[key])
-        assert rm <= 5e-3, (key, rm)
-        assert (np.abs(got - ref[key]) <= bound).all(), (key, mx)
+        report[key] = _check_grad(key, got, ref[key], allow.get(key))
     print(name, {k: f"{v[0]:.2e}/{v[1]:.2e}" for k, v in report.items()})
 
 
@@ -118,3 +105,121 @@ def test_backward_is_deterministic():
     _, g2 = run_backward(cfg, t, dy)
     for key in g1:
         assert torch.equal(g1[key], g2[key]), key
+
+
+def _check_grad(key, got, ref, allow=None):
+    """The kernels round H, the pre-activations, dZ and w dy to bf16 once
+    each (2^-9 relative) and accumulate in fp32: the gradients' RMS error is
+    ~1-1.3 x 2^-9 of their RMS (measured 0.14-0.26%); it must stay below
+    5e-3.  Elementwise, dx and dW_r carry at most about two such roundings of their own size: each
+    element within 3e-2 x RMS (~12 x the RMS error: the extreme of millions
+    of elements' accumulated rounding noise, with margin) + 2^-7 x |ref|
+    (two roundings of its own size, with margin).  Expert weight gradients
+    are sums of per-token outer products whose terms may cancel, and the
+    first-layer ones carry far more than two roundings where the
+    activation's derivative nears zero: they are held to the allowance
+    built from the exact intermediates (``allow``) + 1e-3 x RMS.  A missing
+    or wrong term shows as an O(1) error.  RMS is over the reference's
+    nonzero entries."""
+    mx, rm = _ratio(got, ref)
+    nz = ref != 0
+    scale = float(np.sqrt(np.mean(ref[nz] ** 2))) if nz.any() else 1.0
+    if allow is None:
+        bound = 3e-2 * scale + 2.0 ** -7 * np.abs(ref)
+    else:
+        bound = allow + 1e-3 * scale
+    assert rm <= 5e-3, (key, rm)
+    worst = np.abs(got - ref) - bound
+    assert (worst <= 0).all(), (key, mx, float(worst.max() / scale))
+    return mx, rm
+
+
+def _ffn_allowances(cfg, h, idx, w, dy, experts):
+    """Error allowances of dW1 and dW2 for the listed experts (stacked in
+    list order) and of the shared expert's weight gradients, from the rows
+    that reach each: idx, w are the oracle's top-k and weights [T, k],
+    dy[T, D] the output gradient."""
+    X = widen(h["x"])
+    dy = np.asarray(dy, np.float64)
+    a1, a2 = [], []
+    for e in experts:
+        tt, jj = np.nonzero(idx == e)
+        b1 = widen(h["b1"][e]) if h.get("b1") is not None else None
+        u, v = ffn_grad_allowances(cfg.act, X[tt], widen(h["W1"][e]), b1, widen(h["W2"][e]),
+                                   w[tt, jj][:, None] * dy[tt])
+        a1.append(u)
+        a2.append(v)
+    out = {"dW1": np.stack(a1), "dW2": np.stack(a2)}
+    if cfg.F_shared:
+        out["dWsh_gu"], out["dWsh_dn"] = ffn_grad_allowances(
+            "swiglu", X, widen(h["Wsh_gu"]), None, widen(h["Wsh_dn"]), dy)
+    return out
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["glam", "glm45", "decode"])
+def test_backward_full_size(name):
+    """The full-size layer backward, in the launch configuration the
+    benchmark times, with an output gradient that is nonzero on a few
+    sampled tokens only.  Every other token then contributes exactly
+    nothing, so the oracle, run on the sampled tokens alone (a token's
+    routing does not depend on the others), gives the whole gradient: dx of
+    the sampled rows (the rest must be exactly zero), dW_r, the shared
+    expert's weight gradients, and the weight gradients of three experts the
+    samples reach (the most reached one first).  Experts no sampled token
+    reaches must get exactly zero weight gradients.  The load statistics
+    cover all T tokens: counts bit-exact against the oracle's top-k, scores
+    against the sum of the oracle router's gate values."""
+    from scipy import special
+
+    cfg = workloads.get(name)
+    print(f"full-size backward parity: {cfg.name}", flush=True)
+    t = workloads.generate(cfg, seed=0, device="cuda")
+    h = workloads.host_inputs(t)
+    idx_o, w_o, gap_o, logits, sel_o = oracle.route(cfg, h["x"], h["W_r"], h["bias"],
+                                                    want_logits=True, want_sel=True)
+    rng = np.random.default_rng(11)
+    clear = np.nonzero(gap_o >= TIE_GAP)[0]
+    toks = np.sort(rng.choice(clear, size=min(8, clear.size), replace=False))
+    dy = torch.zeros(cfg.T, cfg.D, dtype=torch.bfloat16, device="cuda")
+    dy[torch.from_numpy(toks).cuda()] = _dy(cfg.replace(T=len(toks)))
+    L, g = run_backward(cfg, t, dy)
+    idx_g, w_g = run_route(L, L.desc, t)
+    mism = check_route(cfg, to_np(idx_g).reshape(cfg.T, cfg.k), to_np(w_g), idx_o, w_o, gap_o,
+                       sel_o)
+    assert not mism[toks].any()
+
+    counts_o = np.bincount(idx_o.reshape(-1), minlength=cfg.M)
+    if not mism.any():
+        assert (to_np(g["load_count"]) == counts_o).all()
+    gate = special.softmax(logits, axis=1) if cfg.scorer == "softmax" else special.expit(logits)
+    assert np.allclose(to_np(g["load_score"]), gate.sum(axis=0), rtol=1e-5, atol=1e-3)
+
+    hit = np.bincount(idx_o[toks].reshape(-1), minlength=cfg.M)
+    reached = [int(e) for e in np.argsort(-hit, kind="stable") if hit[e] > 0]
+    pick = reached[:1] + [int(e) for e in rng.choice(reached[1:], size=min(2, len(reached) - 1),
+                                                      replace=False)]
+    for e in np.nonzero(hit == 0)[0]:
+        for key in ("dW1", "dW2"):
+            assert not g[key][int(e)].any(), f"{key} of unreached expert {e}"
+    rest = torch.ones(cfg.T, dtype=torch.bool, device="cuda")
+    rest[torch.from_numpy(toks).cuda()] = False
+    assert not g["dx"][rest].any(), "dx of tokens with zero output gradient"
+
+    got = {k: to_np(v).astype(np.float64) for k, v in g.items()
+           if k not in ("dW1", "dW2", "db1", "db2", "load_count", "load_score")}
+    got["dx"] = got["dx"][toks]
+    for key in ("dW1", "dW2"):
+        got[key] = np.stack([to_np(g[key][e]).astype(np.float64) for e in pick])
+    del L, g, t, dy
+    torch.cuda.empty_cache()
+
+    sub = dict(h)
+    sub["x"] = np.ascontiguousarray(h["x"][toks])
+    dy_sub = _dy(cfg.replace(T=len(toks))).float().cpu().numpy().astype(np.float64)
+    print(f"  {len(toks)} sampled tokens reach {len(reached)} experts; oracle on experts {pick}",
+          flush=True)
+    ref = oracle.backward(cfg.replace(T=len(toks)), sub, dy_sub, experts=pick)
+    allow = _ffn_allowances(cfg.replace(T=len(toks)), sub, idx_o[toks], w_o[toks], dy_sub, pick)
+    report = {key: _check_grad(key, got[key], ref[key], allow.get(key)) for key in got}
+    print("  " + ", ".join(f"{k} {v[0]:.2e}/{v[1]:.2e}" for k, v in report.items()), flush=True)

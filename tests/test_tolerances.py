@@ -1,0 +1,74 @@
+"""The weight-gradient allowances used by the backward parity tests hold for
+a numpy emulation of the bf16 path's roundings (saved pre-activations and
+the pre-activation gradient in bf16, everything else exact), on shapes with
+many pre-activations near the zeros of the activations' derivatives; and a
+plain relative bound would not."""
+import numpy as np
+import pytest
+from scipy import special
+
+from tests.gpu_util import ffn_grad_allowances
+
+
+def _bf16(a):
+    u = np.asarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _act_grad(act, z, dh):
+    F = dh.shape[1]
+    if act == "gelu":
+        return dh * (special.ndtr(z) + z * np.exp(-0.5 * z * z) / np.sqrt(2 * np.pi))
+    a, b = z[:, :F], z[:, F:]
+    sg = special.expit(a)
+    return np.concatenate([dh * b * sg * (1 + a * (1 - sg)), dh * a * sg], axis=1)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_w1_allowance_covers_bf16_roundings(act):
+    rng = np.random.default_rng(4)
+    n, D, F = 24, 96, 512
+    G = 2 if act == "swiglu" else 1
+    X = _bf16(rng.normal(0, 1, (n, D)))
+    W1 = _bf16(rng.normal(0, 1 / np.sqrt(D), (G * F, D)))
+    W2 = _bf16(rng.normal(0, 1 / np.sqrt(F), (D, F)))
+    b1 = _bf16(rng.normal(0, 0.1, F)) if act == "gelu" else None
+    dO = rng.normal(0, 1, (n, D)) * rng.uniform(0.1, 1.0, (n, 1))
+    z = X @ W1.T + (b1 if b1 is not None else 0.0)
+    dh = dO @ W2
+    exact = _act_grad(act, z, dh).T @ X
+    # the bf16 path: z through fp32 then bf16, dh in fp32, dz rounded to bf16
+    zs = _bf16(np.float32(z))
+    dz = _bf16(np.float32(_act_grad(act, zs, np.float64(np.float32(dh)))))
+    emul = dz.T @ X
+    err = np.abs(emul - exact)
+    allow = ffn_grad_allowances(act, X, W1, b1, W2, dO)[0]
+    rms = np.sqrt(np.mean(exact ** 2))
+    assert (err <= allow + 1e-3 * rms).all(), float((err - allow).max() / rms)
+    # many pre-activations sit near the derivative's zero, where a relative
+    # bound of a few bf16 roundings breaks down
+    rel = err / np.maximum(np.abs(exact), 1e-300)
+    assert (rel > 4 * 2.0 ** -8).any()
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_w2_allowance_covers_bf16_roundings(act):
+    rng = np.random.default_rng(5)
+    n, D, F = 16, 128, 256
+    G = 2 if act == "swiglu" else 1
+    X = _bf16(rng.normal(0, 1, (n, D)))
+    W1 = _bf16(rng.normal(0, 1 / np.sqrt(D), (G * F, D)))
+    W2 = _bf16(rng.normal(0, 1 / np.sqrt(F), (D, F)))
+    dO = rng.normal(0, 1, (n, D))
+    z = X @ W1.T
+    H = (0.5 * z * (1 + special.erf(z / np.sqrt(2))) if act == "gelu"
+         else special.expit(z[:, :F]) * z[:, :F] * z[:, F:])
+    exact = dO.T @ H
+    emul = _bf16(dO).T @ _bf16(np.float32(H))
+    allow = ffn_grad_allowances(act, X, W1, None, W2, dO)[1]
+    rms = np.sqrt(np.mean(exact ** 2))
+    err = np.abs(emul - exact)
+    assert (err <= allow + 1e-3 * rms).all()
+    # cancellation across tokens: a bound relative to |dW2| alone fails
+    assert (err > 2.0 ** -7 * np.abs(exact) + 1e-3 * rms).any()
