@@ -677,6 +677,11 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
     w1.koff = poff;
     w1.kgroups = (int)M;
     w1.c_group_stride = GF * D;
+    // weight gradients write far more than they read: workgroups walk their
+    // tiles so one tile's stores drain while the next one loads
+    const char* penv = getenv("MOE_WGRAD_PERSIST");   // tuning override
+    const int persist = penv ? (atoi(penv) != 0) : 1;
+    w1.persist = w2.persist = persist;
     TRY(run(h, s, L_B_WGRAD, [&] {
         hipError_t e = launch_gemm(s, 1, b.bm_w2, EPI_DOWN_F32, w2, (D + b.bm_w2 - 1) / b.bm_w2);
         if (e != hipSuccess) return e;
@@ -699,6 +704,7 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
         }));
         GemmArgs s2 = dense_args(dyT, HshT, dWsh_dn, D, Fs, b.Tp, Fs);
         GemmArgs s1 = dense_args(dZshT, xT, dWsh_gu, 2 * Fs, D, b.Tp, D);
+        s1.persist = s2.persist = persist;
         TRY(run(h, s, L_B_WGRAD, [&] {
             hipError_t e = launch_gemm(s, 1, b.bm_sh2, EPI_DOWN_F32, s2, (D + b.bm_sh2 - 1) / b.bm_sh2);
             if (e != hipSuccess) return e;

@@ -29,6 +29,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
+// Four bf16 at p (8-byte aligned) to fp32, and back.
+__device__ __forceinline__ void load_bf16x4(const bf16_t* p, float (&v)[4]) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(u.x << 16);
+    v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16);
+    v[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+__device__ __forceinline__ void store_bf16x4(bf16_t* p, float a, float b, float c, float d) {
+    uint2 u;
+    u.x = pack_bf16x2(a, b);
+    u.y = pack_bf16x2(c, d);
+    *reinterpret_cast<uint2*>(p) = u;
+}
 
 // Activations in fp32.
 // SiLU(z) = z sigmoid(z); the hardware reciprocal (1 ulp) in place of a
@@ -121,6 +135,8 @@ struct GemmArgs {
     int group_m;              // m-tiles per group of the tile order (0 = 4)
     int b_tiled;              // b holds tiled blocks (bf16): b_stride = one expert's blocks
     int b_kn;                 // b[e] is [K, N] row-major (b_stride = K * N); bf16, K = 64 stages
+    int persist;              // bf16: 1 = about one workgroup per CU walking the tiles
+                              // (the launcher passes the tile count to the kernel here)
     int xcd_mode;             // workgroup order: 0 groups dealt to XCDs in turn, 1 plain,
                               // 2 contiguous slices per XCD
     const void* b_extra;      // grouped: weights of group extra_group, in place of

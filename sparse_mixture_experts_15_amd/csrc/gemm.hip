@@ -26,6 +26,8 @@
 // few m-tiles x all n-tiles, so those resident together on one XCD share
 // operand K slabs in its L2.  fp32 path: a plain SIMT tile kernel (64 x 64,
 // K step 16).
+#include <algorithm>
+#include <atomic>
 #include <cstdlib>
 
 #include "common.hpp"
@@ -205,6 +207,7 @@ __device__ __forceinline__ void dh_epilogue(const GemmArgs& g, const Tile& tl,
     const bf16_t* zp = static_cast<const bf16_t*>(g.c2);
     const bf16_t* hp = static_cast<const bf16_t*>(g.aux);
     bf16_t* out = static_cast<bf16_t*>(g.c);
+    const bool vec = (N % 4) == 0;   // 8-byte aligned 4-column groups
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         if (i >= wlive) continue;   // wave-uniform
@@ -216,6 +219,35 @@ __device__ __forceinline__ void dh_epilogue(const GemmArgs& g, const Tile& tl,
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int n = n_base + 64 * wn + 16 * j + lc;
+                if (vec && n + 4 <= N) {
+                    float hv[4] = {0.f, 0.f, 0.f, 0.f}, o[2][4];
+                    if (hp) load_bf16x4(hp + r * N + n, hv);
+                    if (EPI == EPI_DH_SWIGLU) {
+                        float gt[4], up[4];
+                        load_bf16x4(zp + r * 2 * N + n, gt);
+                        load_bf16x4(zp + r * 2 * N + N + n, up);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float a = acc[i][j][q], dh = wr * a;
+                            if (hp) pw += hv[q] * a;
+                            o[0][q] = dh * up[q] * silu_grad_f32(gt[q]);
+                            o[1][q] = dh * silu_f32(gt[q]);
+                        }
+                        store_bf16x4(out + r * 2 * N + n, o[0][0], o[0][1], o[0][2], o[0][3]);
+                        store_bf16x4(out + r * 2 * N + N + n, o[1][0], o[1][1], o[1][2], o[1][3]);
+                    } else {
+                        float z[4];
+                        load_bf16x4(zp + r * N + n, z);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float a = acc[i][j][q];
+                            if (hp) pw += hv[q] * a;
+                            o[0][q] = wr * a * gelu_grad_f32(z[q]);
+                        }
+                        store_bf16x4(out + r * N + n, o[0][0], o[0][1], o[0][2], o[0][3]);
+                    }
+                    continue;
+                }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     if (n + q >= N) continue;
@@ -278,8 +310,10 @@ __device__ __forceinline__ bf16x8 kn_fragment(const bf16_t* bt, int kbase, int n
     return __builtin_bit_cast(bf16x8, r);
 }
 
-template <int EPI, int BM, int BNB, int STAGES, int KS, int BKN = 0>
-__global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int n_tiles) {
+// One output tile (workgroup-uniform tile id p) through the LDS ring sm.
+template <int EPI, int BM, int BNB, int STAGES, int KS, int BKN>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int m_tiles, int n_tiles, int p_tile,
+                                          bf16_t* sm) {
     static_assert(!BKN || (KS == 64 && !epi_pairs(EPI)), "KN-layout B: K = 64 stages, no pairing");
     constexpr int BK = KS;
     constexpr int CPR = BK / 8;                        // 16-byte chunks per row
@@ -301,13 +335,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     static_assert(WM * WN == 8 && TM >= 1 && WROWS % 16 == 0, "eight waves");
     static_assert(STAGES >= 2 && STAGES <= 5 && LPW * (STAGES - 2) < 64, "pipeline depth");
     static_assert(BK == 64 || BK == 32, "stage depth");
-    __shared__ __attribute__((aligned(1024))) bf16_t sm[STAGES * STAGE];
 
     // grouped: the valid m-tile count follows the tile table
     const int m_valid = g.tiles ? min(m_tiles, g.tiles[2 * m_tiles]) : m_tiles;
     // split-K (dense fp32 output only): chunk kc of g.k_split covers a K range
     const int nsplit = g.k_split > 1 ? g.k_split : 1;
-    int kc_id = 0, kg = 0, p = (int)blockIdx.x, mt, nt;
+    int kc_id = 0, kg = 0, p = p_tile, mt, nt;
     if (g.koff) {       // K-grouped: group-major ids, plain order inside a group
         kg = p / max(m_valid * n_tiles, 1);
         if (kg >= g.kgroups) return;
@@ -537,6 +570,17 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
                 // pre-activations for the backward: gate and up (SwiGLU, row
                 // stride 2N) or z = acc + b1 (GELU, row stride N), bf16
                 bf16_t* zp = static_cast<bf16_t*>(g.c2);
+                if (vec && n + 4 <= N) {
+                    const floatx4 a0 = acc[i][j];
+                    if (EPI == EPI_SWIGLU_SAVE) {
+                        const floatx4 a1 = acc[i][j + 2];
+                        store_bf16x4(zp + r * 2 * N + n, a0[0], a0[1], a0[2], a0[3]);
+                        store_bf16x4(zp + r * 2 * N + N + n, a1[0], a1[1], a1[2], a1[3]);
+                    } else {
+                        store_bf16x4(zp + r * N + n, a0[0] + bv[j][0], a0[1] + bv[j][1],
+                                     a0[2] + bv[j][2], a0[3] + bv[j][3]);
+                    }
+                } else
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     if (n + q >= N) continue;
@@ -584,6 +628,28 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             }
         }
     }
+    }
+}
+
+// One tile per workgroup, or with g.persist = the tile count a grid of
+// about one workgroup per CU walking tiles p, p + grid, ...: a tile's
+// epilogue stores drain while the next tile's first stages load (a stage
+// wait also waits for the older stores, so nothing overtakes them).
+template <int EPI, int BM, int BNB, int STAGES, int KS, int BKN = 0>
+__global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int n_tiles) {
+    __shared__ __attribute__((aligned(1024))) bf16_t sm[STAGES * (BM + BNB) * KS];
+    if constexpr (EPI != EPI_DOWN_F32) {
+        // (the loop costs the other epilogues ~20 VGPRs; only fp32-output
+        // GEMMs take the persistent launch)
+        gemm_tile<EPI, BM, BNB, STAGES, KS, BKN>(g, m_tiles, n_tiles, (int)blockIdx.x, sm);
+    } else {
+        const int end = g.persist ? g.persist : (int)blockIdx.x + 1;
+        for (int p = (int)blockIdx.x; p < end; p += (int)gridDim.x) {
+            gemm_tile<EPI, BM, BNB, STAGES, KS, BKN>(g, m_tiles, n_tiles, p, sm);
+            // every wave has finished reading the ring before the next
+            // tile's loads overwrite it (workgroup-uniform branch)
+            if (g.persist) __builtin_amdgcn_s_barrier();
+        }
     }
 }
 
@@ -675,6 +741,22 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs g) {
     }
 }
 
+// Compute units of the current device (cached per device id).
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 // Workgroups to launch for m_tiles x n_tiles tiles (m_tiles may bound the
 // valid count from above): mode 0 deals whole groups to the eight XCDs in
 // turn, so the grid is rounded up to eight groups.
@@ -695,8 +777,17 @@ hipError_t launch_bf16(hipStream_t s, const GemmArgs& g, int64_t m_tiles) {
     if (g.b_tiled && (KS != kTileK || kTileRows % BNv != 0)) return hipErrorInvalidValue;
     const int64_t total = grid_tiles(g, m_tiles, n_tiles);
     if (BKN && g.b_tiled) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_bf16<EPI, BMv, BNv, STv, KS, BKN>), dim3((unsigned)total), dim3(NT), 0, s, g,
-                       (int)m_tiles, n_tiles);
+    int64_t grid = total;
+    GemmArgs ga = g;
+    ga.persist = 0;
+    if (g.persist && EPI != EPI_DOWN_F32) return hipErrorInvalidValue;
+    if (g.persist && total > 0) {
+        if (total >= (int64_t)1 << 31) return hipErrorInvalidValue;
+        ga.persist = (int)total;
+        grid = std::min<int64_t>(total, device_cu_count());
+    }
+    hipLaunchKernelGGL((gemm_bf16<EPI, BMv, BNv, STv, KS, BKN>), dim3((unsigned)grid), dim3(NT), 0, s,
+                       ga, (int)m_tiles, n_tiles);
     return hipGetLastError();
 }
 
