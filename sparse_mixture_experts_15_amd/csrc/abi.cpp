@@ -677,15 +677,18 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
     w1.koff = poff;
     w1.kgroups = (int)M;
     w1.c_group_stride = GF * D;
-    // weight gradients write far more than they read: workgroups walk their
-    // tiles so one tile's stores drain while the next one loads
-    const char* penv = getenv("MOE_WGRAD_PERSIST");   // tuning override
-    const int persist = penv ? (atoi(penv) != 0) : 1;
-    w1.persist = w2.persist = persist;
+    // the weight-gradient kernel (store-bound products); MOE_WGRAD_GEMM=0
+    // runs them on the general GEMM instead (tuning comparison)
+    const char* wenv = getenv("MOE_WGRAD_GEMM");
+    const bool wk = !(wenv && atoi(wenv) == 0);
+    auto wgrad = [&](const GemmArgs& g, int bm, int64_t rows) {
+        return wk ? launch_wgrad(s, g)
+                  : launch_gemm(s, 1, bm, EPI_DOWN_F32, g, (rows + bm - 1) / bm);
+    };
     TRY(run(h, s, L_B_WGRAD, [&] {
-        hipError_t e = launch_gemm(s, 1, b.bm_w2, EPI_DOWN_F32, w2, (D + b.bm_w2 - 1) / b.bm_w2);
+        hipError_t e = wgrad(w2, b.bm_w2, D);
         if (e != hipSuccess) return e;
-        return launch_gemm(s, 1, b.bm_w1, EPI_DOWN_F32, w1, (GF + b.bm_w1 - 1) / b.bm_w1);
+        return wgrad(w1, b.bm_w1, GF);
     }));
     if (Fs > 0) {
         void* dyT = at<char>(ws, b.dyT);
@@ -704,12 +707,10 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
         }));
         GemmArgs s2 = dense_args(dyT, HshT, dWsh_dn, D, Fs, b.Tp, Fs);
         GemmArgs s1 = dense_args(dZshT, xT, dWsh_gu, 2 * Fs, D, b.Tp, D);
-        s1.persist = s2.persist = persist;
         TRY(run(h, s, L_B_WGRAD, [&] {
-            hipError_t e = launch_gemm(s, 1, b.bm_sh2, EPI_DOWN_F32, s2, (D + b.bm_sh2 - 1) / b.bm_sh2);
+            hipError_t e = wgrad(s2, b.bm_sh2, D);
             if (e != hipSuccess) return e;
-            return launch_gemm(s, 1, b.bm_sh1, EPI_DOWN_F32, s1,
-                               (2 * Fs + b.bm_sh1 - 1) / b.bm_sh1);
+            return wgrad(s1, b.bm_sh1, 2 * Fs);
         }));
     }
     // router weight gradient: dl split exactly into three bf16 planes, so the

@@ -135,8 +135,6 @@ struct GemmArgs {
     int group_m;              // m-tiles per group of the tile order (0 = 4)
     int b_tiled;              // b holds tiled blocks (bf16): b_stride = one expert's blocks
     int b_kn;                 // b[e] is [K, N] row-major (b_stride = K * N); bf16, K = 64 stages
-    int persist;              // bf16: 1 = about one workgroup per CU walking the tiles
-                              // (the launcher passes the tile count to the kernel here)
     int xcd_mode;             // workgroup order: 0 groups dealt to XCDs in turn, 1 plain,
                               // 2 contiguous slices per XCD
     const void* b_extra;      // grouped: weights of group extra_group, in place of
@@ -220,6 +218,7 @@ constexpr int64_t kSmallT = 1024;
 hipError_t launch_perm_small(hipStream_t s, const int32_t* idx, int64_t T, int k, int64_t M,
                              int32_t* counts, int32_t* offsets, int32_t* sorted_token,
                              int32_t* sorted_slot, int32_t* slot_row);
+hipError_t launch_wgrad(hipStream_t s, const GemmArgs& g);
 hipError_t launch_gemm(hipStream_t s, int dtype, int bm, int epi, const GemmArgs& g,
                        int64_t m_tiles);
 hipError_t launch_combine(hipStream_t s, int out_dtype, const float* O, const int32_t* slot_row,
