@@ -1,9 +1,9 @@
-"""moe_forward captured in a HIP graph (torch.cuda.CUDAGraph) replays to the
-eager result bitwise: the call enqueues only kernels and event
-dependencies (no host synchronisation, no memset nodes), and the shared
-expert's fork onto the second stream and its join are captured as graph
-edges.  Each replay follows unrelated eager work and a synchronisation, and
-is checked on its own."""
+"""moe_forward and moe_backward captured in HIP graphs (torch.cuda.CUDAGraph)
+replay to the eager results bitwise: the calls enqueue only kernels and
+event dependencies (no host synchronisation, no memset nodes), and the
+forward's shared-expert fork onto the second stream and its join are
+captured as graph edges.  Each replay follows unrelated eager work and a
+synchronisation, and is checked on its own."""
 import pytest
 import torch
 
@@ -65,3 +65,45 @@ def test_graph_replay_matches_eager(name, tiled):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(_bits(y), _bits(y_eager)), f"replay {rep}"
+
+
+@pytest.mark.parametrize("name", ["glm45_shared", "decode"])
+def test_backward_graph_replay_matches_eager(name):
+    """moe_backward captured in a HIP graph replays to the eager gradients
+    bitwise (kernels only on one stream; zero fills are kernels)."""
+    from sparse_mixture_experts_15_amd import binding as B
+    cfg = GRAPH[name]
+    t = workloads.generate(cfg, seed=2, device="cuda")
+    L = new_layer(cfg)
+    d = L.desc
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    dy = torch.randn(cfg.T, cfg.D, generator=gen, device="cuda").to(torch.bfloat16)
+    ws = torch.empty(B.moe_backward_workspace_size(d), dtype=torch.uint8, device="cuda")
+    g_eager = B.backward_grads(d)
+    g_graph = B.backward_grads(d)
+    main = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    main.wait_stream(torch.cuda.current_stream())
+
+    def bwd(g):
+        B.moe_backward(L.handle, d, t["x"], t["W_r"], t["bias"], t["W1"], None, t["W2"], None,
+                       t["Wsh_gu"], t["Wsh_dn"], dy, g, ws, stream=main)
+
+    with torch.cuda.stream(main):
+        bwd(g_eager)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=main):
+        bwd(g_graph)
+    torch.cuda.synchronize()
+    scratch = B.backward_grads(d)
+    for rep in range(3):
+        with torch.cuda.stream(main):
+            bwd(scratch)   # unrelated eager work on the same workspace
+        for v in g_graph.values():
+            v.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for key in g_eager:
+            assert torch.equal(g_graph[key], g_eager[key]), (rep, key)
