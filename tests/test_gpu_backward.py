@@ -24,6 +24,8 @@ BWD = {
     "glam_softmax_k3_ragged": S(workloads.GLAM_4K, T=333, D=72, F=40).replace(M=6, k=3),
     "glam_gelu_biases": S(workloads.GLAM_4K, T=190, D=96, F=64).replace(M=8, ffn_bias_std=0.1),
     "single_token": S(workloads.GLM45_PREFILL, T=1, D=64, F=48, F_shared=48),
+    "glm45_group_routing": S(workloads.GLM45_GROUPED, T=160, D=128, F=64,
+                             F_shared=64).replace(M=32, k=4, n_group=8, topk_group=3),
 }
 
 
