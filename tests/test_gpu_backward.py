@@ -26,6 +26,9 @@ BWD = {
     "single_token": S(workloads.GLM45_PREFILL, T=1, D=64, F=48, F_shared=48),
     "glm45_group_routing": S(workloads.GLM45_GROUPED, T=160, D=128, F=64,
                              F_shared=64).replace(M=32, k=4, n_group=8, topk_group=3),
+    "max_k16": S(workloads.GLM5_ZIPF, T=70, D=64, F=32, F_shared=0).replace(k=16),
+    "many_experts_1024": S(workloads.GLM45_PREFILL, T=200, D=64, F=32,
+                           F_shared=0).replace(M=1024, k=4),
 }
 
 
