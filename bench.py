@@ -266,8 +266,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the layer's expert-parallel sharding is not "
-              f"part of this build (asked for --gpus {args.gpus})", file=sys.stderr)
+        print(f"bench.py runs on one GPU only: the library implements the layer on one GPU, "
+              f"without expert-parallel sharding (asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
     if args.calib_copy:
