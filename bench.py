@@ -69,6 +69,22 @@ def recorded_traffic(workload, kernel):
     return rec[0]
 
 
+def step_spread(step, stream, n):
+    """Median, min and max of n single steps, each bracketed by HIP events on
+    `stream` (a separate pass after the timed region)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"median": round(per[len(per) // 2], 4), "min": round(per[0], 4),
+            "max": round(per[-1], 4)}
+
+
 def calib_copy():
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -220,6 +236,7 @@ def bench_backward(args):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    spread = step_spread(step, torch.cuda.current_stream(), args.steps)
     dom = max((k for k in split if k in kw), key=split.get)
     fl, by = kw[dom]
     # the bound of the dominant label: whichever of its FLOPs at the bf16
@@ -237,6 +254,7 @@ def bench_backward(args):
         "config": {"workload": cfg.name, "pass": "backward", "touched_experts": U,
                    "weights": "rows"},
         "gradient_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "step_ms": spread,
         "kernel_ms_per_step": {k: round(v, 4) for k, v in split.items()},
         "roofline": {"bound": "hbm" if hbm else "mfma", "kernel": dom,
                      "kernel_ms": round(split[dom], 4), "achieved": round(achieved, 1),
@@ -250,7 +268,8 @@ def bench_backward(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 100 for the decode workload)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="glam")
     ap.add_argument("--seed", type=int, default=0)
@@ -264,6 +283,8 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the layer backward (moe_backward) instead of the forward")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 100 if args.config == "decode" else 20
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the library implements the layer on one GPU, "
@@ -339,6 +360,7 @@ def main():
     B.moe_profile_stop(L.handle)
     launches, tot_ms = B.moe_profile_results(L.handle)[dominant]
     dom_ms = tot_ms / max(launches, 1)
+    spread = step_spread(step, main, args.steps)
 
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_s = cfg.T / (ms_per_step * 1e-3)
@@ -380,6 +402,7 @@ def main():
         "active_tflops": round(active_tflops, 2),
         "alg_hbm_gbps": round(alg_gbps, 1),
         "layer_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),
+        "step_ms": spread,
         "kernel_ms_per_step": {k: round(v, 4) for k, v in split.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
