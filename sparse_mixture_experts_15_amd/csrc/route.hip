@@ -240,6 +240,41 @@ __global__ __launch_bounds__(256) void route_reduce(const float* __restrict__ P,
     L[i] = h + (m + l);
 }
 
+// Small batches (decode): L[t][e] = x_t . W_r[e] accumulated in fp64 (the
+// bf16 x fp32 products are exact in fp64), rounded once to fp32; a cheaper
+// route to the same logits than splitting W_r and running the GEMM, whose
+// tile grid a few dozen tokens cannot fill.  A block of 256 threads covers
+// 4 experts x 4 tokens with 16 lanes per dot product: lane q takes the
+// groups of four k at 4 q + 64 i (a wave reads 256 contiguous bytes of a
+// W_r row per step), four independent fp64 chains per lane, then the chains
+// and the lanes are summed in a fixed order.  Requires D % 4 == 0.
+__global__ __launch_bounds__(256) void route_logits_small(const bf16_t* __restrict__ x,
+                                                          const float* __restrict__ W_r, int T,
+                                                          int D, int M, float* __restrict__ L) {
+    const int kq = threadIdx.x & 15, tl = (threadIdx.x >> 4) & 3, el = threadIdx.x >> 6;
+    const int e = blockIdx.x * 4 + el, t = blockIdx.y * 4 + tl;
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    if (e < M && t < T) {
+        const float* wr = W_r + (int64_t)e * D;
+        const bf16_t* xr = x + (int64_t)t * D;
+#pragma unroll 8
+        for (int k = 4 * kq; k < D; k += 64) {
+            const float4 wv = *reinterpret_cast<const float4*>(wr + k);
+            const uint2 xv = *reinterpret_cast<const uint2*>(xr + k);
+            a0 = fma((double)__uint_as_float(xv.x << 16), (double)wv.x, a0);
+            a1 = fma((double)__uint_as_float(xv.x & 0xffff0000u), (double)wv.y, a1);
+            a2 = fma((double)__uint_as_float(xv.y << 16), (double)wv.z, a2);
+            a3 = fma((double)__uint_as_float(xv.y & 0xffff0000u), (double)wv.w, a3);
+        }
+    }
+    double acc = (a0 + a1) + (a2 + a3);
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    acc += __shfl_xor(acc, 8);
+    if (kq == 0 && e < M && t < T) L[(int64_t)t * M + e] = (float)acc;
+}
+
 // One wave per token: the top-k epilogue on its logits L[t][0..M).
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ L,
                                                   const float* __restrict__ bias,
@@ -328,6 +363,15 @@ hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, con
         float* P = reinterpret_cast<float*>(base + align256((size_t)3 * M * D * 2));
         float* L = reinterpret_cast<float*>(base + align256((size_t)3 * M * D * 2) +
                                             align256((size_t)nK * T * 3 * M * 4));
+        if (T <= kSmallRouteT && D % 4 == 0) {
+            hipLaunchKernelGGL(route_logits_small,
+                               dim3((unsigned)((M + 3) / 4), (unsigned)((T + 3) / 4)), dim3(256),
+                               0, s, static_cast<const bf16_t*>(x), W_r, (int)T, (int)D, (int)M, L);
+            hipLaunchKernelGGL(route_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, L, b,
+                               idx, w, (int)T, (int)M, k, scorer, renorm, alpha, eps, n_group,
+                               topk_group);
+            return hipGetLastError();
+        }
         const int64_t n = M * D;
         hipLaunchKernelGGL(router_split, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s,
                            W_r, W3, n);
