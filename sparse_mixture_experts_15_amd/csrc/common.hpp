@@ -190,7 +190,6 @@ hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, con
 // the fp32 logits L[T][M] at route_logits_offset() bytes into it.
 size_t route_workspace(int dtype, int64_t T, int64_t D, int64_t M);
 size_t route_logits_offset(int dtype, int64_t T, int64_t D, int64_t M);
-constexpr int64_t kSmallRouteT = 256;   // bf16 batches up to this many tokens: fp64 dot router
 int route_ksplit(int64_t T, int64_t D, int64_t M);
 hipError_t launch_perm_count(hipStream_t s, const int32_t* idx, int32_t* hist, int64_t T, int k,
                              int64_t M);

@@ -240,6 +240,8 @@ __global__ __launch_bounds__(256) void route_reduce(const float* __restrict__ P,
     L[i] = h + (m + l);
 }
 
+constexpr int64_t kSmallRouteT = 256;   // bf16 batches up to this many tokens: fp64 dot router
+
 // Small batches (decode): L[t][e] = x_t . W_r[e] accumulated in fp64 (the
 // bf16 x fp32 products are exact in fp64), rounded once to fp32; a cheaper
 // route to the same logits than splitting W_r and running the GEMM, whose
