@@ -12,20 +12,30 @@
 //   down (scaled):  O[r, n] = w[slot(r)] * (H[r] . W2[e, n] + b2[e, n])   (fp32)
 //   down (fp32):    Y[r, n] = H[r] . W2[n]            (shared expert)
 //
-// bf16 path: 128 x 256 workgroup tiles (128 A rows x 256 B rows), eight
-// waves (2 x 4, 64 x 64 each) on v_mfma_f32_16x16x32_bf16.  Operands stream
-// through a 3-stage LDS ring of K = 64 (128-byte row segments, whole cache
-// lines) filled by buffer loads that write LDS directly: two stages load
-// while one is multiplied.  Out-of-range rows and the K tail read
-// as zeros through the buffer bounds.  LDS rows carry an XOR chunk swizzle
+//   backward (bf16; the chain rule of the same steps):
+//   up + save:      H as above, and the pre-activations Z (bf16)
+//   dH (DH_*):      dZ[r] = act'(Z[r]) * w[slot(r)] * (dy[tok(r)] . W2[e])
+//                   plus per-tile partial dots H . dH_raw for the gate gradient
+//   dX (fp32):      dX[r] = dZ[r] . W1[e]                 (W2, W1 read as [K, N])
+//   weight grads:   dW[e] = A_e^T B_e over expert e's rows (wgrad_bf16)
+//
+// bf16 path: workgroup tiles of BM A rows x 256 B rows (BM = 64, 128, 160
+// or 256, chosen per GEMM from the rows per group), eight waves on
+// v_mfma_f32_16x16x32_bf16, each wave 64 B rows x BM/2 A rows.  Operands
+// stream through an LDS ring of K = 64 stages (2-5 deep, up to 160 KB)
+// filled by buffer loads that write LDS directly, with explicit vmcnt waits
+// and one barrier per stage.  Out-of-range rows and the K tail read as zeros
+// through the buffer bounds.  LDS rows carry an XOR chunk swizzle
 // (conflict-free 16-byte fragment reads, measured).  A rows of the up
 // projection are gathered on load through the sorted token list, so the
 // permuted activations are never materialised.  For SwiGLU each wave's 64 B
 // rows are 32 gate rows and the 32 matching up rows, so silu(gate) * up is
-// formed in registers.  Workgroups are ordered XCD by XCD in groups of a
-// few m-tiles x all n-tiles, so those resident together on one XCD share
-// operand K slabs in its L2.  fp32 path: a plain SIMT tile kernel (64 x 64,
-// K step 16).
+// formed in registers.  B may be row-major, tiled (one contiguous block per
+// 256-row tile and stage) or [K, N] (the backward's weights, read in place
+// through transposed LDS reads).  Tiles are taken in groups of a few m-tiles
+// x all n-tiles, dealt to the XCDs in an order chosen per GEMM, so the
+// workgroups resident on one XCD share operand K slabs in its L2.  fp32
+// path: a plain SIMT tile kernel (64 x 64, K step 16).
 #include <cstdlib>
 
 #include "common.hpp"
