@@ -1,0 +1,49 @@
+"""Host-side checks of the benchmark script: its algorithmic work counts
+for the layer shapes (active FLOPs: 2 D F (G + 1) per routed pair, 6 D F_sh
+per token for the shared expert, 2 D M per token for the router; bytes: the
+touched experts' weights, shared weights, router weights, x and y), and
+that it refuses more than one GPU before touching one."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("name,U,tflop,gbytes", [
+    ("glam", 64, 2.201, 17.25),     # every expert reached
+    ("glm45", 160, 3.492, 7.77),    # all 160 experts reached
+    ("glm45", 63, 3.492, 3.19),     # 63 reached
+    ("glm5", 256, 11.18, 19.81),
+    ("decode", 40, 0.0273, 1.94),
+])
+def test_layer_work(name, U, tflop, gbytes):
+    cfg = workloads.get(name)
+    flops, byts = bench.layer_work(cfg, U)
+    assert flops / 1e12 == pytest.approx(tflop, rel=2e-3)
+    assert byts / 1e9 == pytest.approx(gbytes, rel=5e-3)
+
+
+def test_backward_work_counts_all_experts_gradients():
+    cfg = workloads.get("glm45")
+    w, flops = bench.backward_work(cfg, 68)
+    G = 2
+    _, by = w["b_wgrad"]
+    # every expert's weight gradient is written (zeros for unreached ones)
+    assert by >= cfg.M * (G + 1) * cfg.F * cfg.D * 4
+    # the gradients of every forward GEMM: twice the forward's active FLOPs
+    fwd_gemm = 2 * cfg.T * cfg.k * cfg.D * cfg.F * (G + 1) + 6 * cfg.T * cfg.D * cfg.F_shared
+    assert flops >= 2 * fwd_gemm
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
