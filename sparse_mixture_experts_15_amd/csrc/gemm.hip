@@ -24,7 +24,10 @@
 // v_mfma_f32_16x16x32_bf16, each wave 64 B rows x BM/2 A rows.  Operands
 // stream through an LDS ring of K = 64 stages (2-5 deep, up to 160 KB)
 // filled by buffer loads that write LDS directly, with explicit vmcnt waits
-// and one barrier per stage.  Out-of-range rows and the K tail read as zeros
+// and one barrier per stage; in 256-row tiles whose fragments all hold rows
+// each wave reads the next fragment group from LDS among the current
+// group's MFMAs, an order pinned with scheduling-group barriers.
+// Out-of-range rows and the K tail read as zeros
 // through the buffer bounds.  LDS rows carry an XOR chunk swizzle
 // (conflict-free 16-byte fragment reads, measured).  A rows of the up
 // projection are gathered on load through the sorted token list, so the
@@ -462,14 +465,97 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     for (int s0 = 0; s0 < STAGES - 1; ++s0)
         if (s0 < nk) issue(k_first + s0);
     const int fr = lane & 15, fc = lane >> 4;
-    for (int kt = 0; kt < nk; ++kt) {
-        // stage kt has landed once only later stages' loads are pending
-        const int later = min(nk - 1, kt + STAGES - 2) - kt;
-        if (LPW == LPW_LO || wave < LOADS % 8) wait_stages<LPW, STAGES>(later);
-        else wait_stages<LPW_LO, STAGES>(later);
-        __builtin_amdgcn_s_barrier();     // every wave's loads landed; stage kt-1 fully read
-        if (kt + STAGES - 1 < nk) issue(k_first + kt + STAGES - 1);
-        const bf16_t* st = sm + ((k_first + kt) % STAGES) * STAGE;
+    auto kloop = [&](auto&& body) {
+        for (int kt = 0; kt < nk; ++kt) {
+            // stage kt has landed once only later stages' loads are pending
+            const int later = min(nk - 1, kt + STAGES - 2) - kt;
+            if (LPW == LPW_LO || wave < LOADS % 8) wait_stages<LPW, STAGES>(later);
+            else wait_stages<LPW_LO, STAGES>(later);
+            __builtin_amdgcn_s_barrier();     // every wave's loads landed; stage kt-1 fully read
+            if (kt + STAGES - 1 < nk) issue(k_first + kt + STAGES - 1);
+            const bf16_t* st = sm + ((k_first + kt) % STAGES) * STAGE;
+            body(st);
+        }
+    };
+    // the multiply of one stage for tiles whose fragments all hold rows
+    auto body_full256 = [&](const bf16_t* st) {
+        // 256-row tiles, whole fragments: each K half's rows 0-3 then
+        // 4-7, the next group's fragments read among the current
+        // group's MFMAs (pinned with scheduling groups; 22 more VGPRs
+        // than reading per K half, no spills).  Measured against the
+        // general body on one device: GLM-5-shaped routed up projection
+        // 7.56 -> 7.11 ms, GLM-4.5-shaped 2.29 -> 2.13 ms, its backward
+        // 15.1 -> 14.7 ms; outputs bitwise equal.
+        constexpr int RB = BKN ? 2 : 1;   // LDS reads per weight fragment
+        bf16x8 b0[TN], b1[TN], a00[4], a01[4], a10[4], a11[4];
+        auto rdB = [&](int kk, bf16x8(&bb)[TN]) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                if constexpr (BKN)
+                    bb[j] = kn_fragment<BNB>(st + BM * BK, kk * 32, wn * 64 + 16 * j, lane);
+                else
+                    bb[j] = *reinterpret_cast<const bf16x8*>(
+                        st + BM * BK + swz<BK>(wn * 64 + 16 * j + fr, kk * 4 + fc));
+            }
+        };
+        auto rdA = [&](int kk, int i0, bf16x8(&aa)[4]) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                aa[i] = *reinterpret_cast<const bf16x8*>(
+                    st + swz<BK>(wm * WROWS + 16 * (i0 + i) + fr, kk * 4 + fc));
+        };
+        auto mm = [&](int i0, const bf16x8(&aa)[4], const bf16x8(&bb)[TN]) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i0 + i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        bb[j], aa[i], acc[i0 + i][j], 0, 0, 0);
+        };
+        rdB(0, b0);
+        rdA(0, 0, a00);
+        __builtin_amdgcn_sched_group_barrier(0x100, TN * RB + 4, 0);
+        rdA(0, 4, a01);
+        mm(0, a00, b0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        rdB(1, b1);
+        rdA(1, 0, a10);
+        mm(4, a01, b0);
+        if constexpr (BKN) {   // 12 reads among 16 MFMAs
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        } else {   // 8 reads among 16 MFMAs
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+        rdA(1, 4, a11);
+        mm(0, a10, b1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        mm(4, a11, b1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    };
+    // the multiply of one stage in general (fragments past the group's
+    // last row skip their reads and MFMAs)
+    auto body_general = [&](const bf16_t* st) {
         if (TM <= 4 && wlive == TM) {
             // whole fragments: one straight block (every fragment read, then
             // the MFMAs) the scheduler can overlap freely.  Measured faster
@@ -500,7 +586,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[kk][j], af[kk][i],
                                                                             acc[i][j], 0, 0, 0);
-            continue;
+            return;
         }
 #pragma unroll
         for (int kk = 0; kk < BK / 32; ++kk) {
@@ -532,6 +618,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
                 }
             }
         }
+    };
+    // wlive is fixed for the whole loop, so the two bodies get loops of
+    // their own (in one loop their registers add up and spill)
+    if constexpr (TM == 8 && BK == 64) {
+        if (wlive == TM) kloop(body_full256);
+        else kloop(body_general);
+    } else {
+        kloop(body_general);
     }
 
     // Epilogue straight from registers.  The MFMAs take the B fragment as
