@@ -1029,11 +1029,13 @@ hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64
 // evens out the last round of workgroups (GLM-4.5 decode up projection
 // 0.29 -> 0.26 ms; the down projection, K = expert width, is slower so).
 // Groups of hundreds of rows are MFMA-bound: 256-row tiles halve the LDS
-// traffic per MFMA for the up projection; the down projection keeps 128-row
-// tiles there (its short K = expert width favours the 3-stage ring), unless
-// a 256-row tile still covers the whole group.  Dense GEMMs take 256-row
-// tiles when that still leaves at least four workgroups per CU.  Measured on
-// MI355X over the layer shapes the tests use.
+// traffic per MFMA and take the scheduled full-tile K loop, for the down
+// projection too (GLM-4.5 prefill down projection 1.51 -> 1.30 ms against
+// 128-row tiles, GLM-5 4.62 -> 4.01 ms).  Dense GEMMs take 256-row tiles
+// when that still gives every CU a workgroup (GLM-4.5 shared expert: up
+// 0.42 -> 0.32 ms, down 0.79 -> 0.39 ms); the router's narrow logit GEMM
+// keeps 128-row tiles.  Measured on MI355X over the layer shapes the tests
+// use.
 int gemm_block_m(int dtype, int64_t rows, int64_t groups, bool down, int64_t b_rows) {
     if (dtype != 1) return FBM;
     // tuning override: MOE_GEMM_BM_{UP,DN} (grouped) / MOE_GEMM_BM_SH_{UP,DN} (dense)
@@ -1045,14 +1047,13 @@ int gemm_block_m(int dtype, int64_t rows, int64_t groups, bool down, int64_t b_r
     }
     if (groups <= 1) {
         const int64_t tiles256 = (rows / 256) * ((b_rows + 255) / 256);
-        return tiles256 >= 4 * 256 ? 256 : 128;
+        return tiles256 >= 256 ? 256 : 128;
     }
     const int64_t avg = rows / groups;
     if (avg <= 16 && !down) return 64;
     if (avg <= 96) return 128;
     if (avg <= 136) return 160;
-    if (avg <= 224 || !down) return 256;
-    return 128;
+    return 256;
 }
 
 int gemm_group_m(int64_t rows, int64_t groups, int bm) {
