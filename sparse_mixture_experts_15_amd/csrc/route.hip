@@ -246,35 +246,52 @@ constexpr int64_t kSmallRouteT = 256;   // bf16 batches up to this many tokens: 
 // bf16 x fp32 products are exact in fp64), rounded once to fp32; a cheaper
 // route to the same logits than splitting W_r and running the GEMM, whose
 // tile grid a few dozen tokens cannot fill.  A block of 256 threads covers
-// 4 experts x 4 tokens with 16 lanes per dot product: lane q takes the
-// groups of four k at 4 q + 64 i (a wave reads 256 contiguous bytes of a
-// W_r row per step), four independent fp64 chains per lane, then the chains
-// and the lanes are summed in a fixed order.  Requires D % 4 == 0.
+// 4 experts (one per wave) x 4 tokens: a wave reads its expert's W_r row
+// once for the 4 tokens, lane q taking the groups of four k at 4 q + 256 i
+// (1 KB of the row per wave and step), one fp64 chain per token; the lanes
+// are then summed in a fixed order.  Latency bounds this kernel: 64 lanes
+// per dot product take D / 256 steps (20 at D = 5120), and the loop has no
+// branch, so loads of consecutive steps overlap.  GLM-4.5 decode (64 tokens,
+// 160 experts): 13.4 us, against 19.4 us with 16 lanes per dot product, 40 us
+// with a per-token branch in the loop and 28-30 us unrolled 8 or 16 deep.
+// Requires D % 4 == 0.
 __global__ __launch_bounds__(256) void route_logits_small(const bf16_t* __restrict__ x,
                                                           const float* __restrict__ W_r, int T,
                                                           int D, int M, float* __restrict__ L) {
-    const int kq = threadIdx.x & 15, tl = (threadIdx.x >> 4) & 3, el = threadIdx.x >> 6;
-    const int e = blockIdx.x * 4 + el, t = blockIdx.y * 4 + tl;
-    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    if (e < M && t < T) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int e = blockIdx.x * 4 + wv, t0 = blockIdx.y * 4;
+    const int nt = min(4, T - t0);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    if (e < M) {
         const float* wr = W_r + (int64_t)e * D;
-        const bf16_t* xr = x + (int64_t)t * D;
-#pragma unroll 8
-        for (int k = 4 * kq; k < D; k += 64) {
-            const float4 wv = *reinterpret_cast<const float4*>(wr + k);
-            const uint2 xv = *reinterpret_cast<const uint2*>(xr + k);
-            a0 = fma((double)__uint_as_float(xv.x << 16), (double)wv.x, a0);
-            a1 = fma((double)__uint_as_float(xv.x & 0xffff0000u), (double)wv.y, a1);
-            a2 = fma((double)__uint_as_float(xv.y << 16), (double)wv.z, a2);
-            a3 = fma((double)__uint_as_float(xv.y & 0xffff0000u), (double)wv.w, a3);
+        // rows past the batch re-read its last row (no branch in the loop);
+        // their sums are never written
+        const bf16_t* xr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xr[j] = x + (int64_t)(t0 + min(j, nt - 1)) * D;
+#pragma unroll 2
+        for (int k = 4 * lane; k < D; k += 256) {
+            const float4 w4 = *reinterpret_cast<const float4*>(wr + k);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint2 xv = *reinterpret_cast<const uint2*>(xr[j] + k);
+                double a = acc[j];
+                a = fma((double)__uint_as_float(xv.x << 16), (double)w4.x, a);
+                a = fma((double)__uint_as_float(xv.x & 0xffff0000u), (double)w4.y, a);
+                a = fma((double)__uint_as_float(xv.y << 16), (double)w4.z, a);
+                a = fma((double)__uint_as_float(xv.y & 0xffff0000u), (double)w4.w, a);
+                acc[j] = a;
+            }
         }
     }
-    double acc = (a0 + a1) + (a2 + a3);
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 4);
-    acc += __shfl_xor(acc, 8);
-    if (kq == 0 && e < M && t < T) L[(int64_t)t * M + e] = (float)acc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) acc[j] += __shfl_xor(acc[j], off);
+    if (e < M && lane < nt) {
+        const double v = lane == 0 ? acc[0] : lane == 1 ? acc[1] : lane == 2 ? acc[2] : acc[3];
+        L[(int64_t)(t0 + lane) * M + e] = (float)v;
+    }
 }
 
 // One wave per token: the top-k epilogue on its logits L[t][0..M).
