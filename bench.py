@@ -1,6 +1,6 @@
 """Throughput of the MoE layer forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config glam|glm45|glm5|decode|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config glam|glm45|glm5|decode|glm45g|switch|glm45dense|tiny]
 
 One step is one moe_forward over one batch of synthetic, seeded, HBM-resident
 inputs: router, dispatch, expert FFNs, shared expert (second stream) and

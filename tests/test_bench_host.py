@@ -22,6 +22,7 @@ import bench  # noqa: E402
     ("glm45", 63, 3.492, 3.19),     # 63 reached
     ("glm5", 256, 11.18, 19.81),
     ("decode", 40, 0.0273, 1.94),
+    ("glm45dense", 1, 3.479, 0.5925),   # 6 T D F + the one-expert router
 ])
 def test_layer_work(name, U, tflop, gbytes):
     cfg = workloads.get(name)

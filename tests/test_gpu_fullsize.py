@@ -37,7 +37,7 @@ def _sample_tokens(cfg, disp, n_random=24, n_expert=24, seed=0):
     ("tiny", None, "rows"), ("decode", None, "rows"), ("decode", "f32", "rows"),
     ("glm45", None, "rows"), ("glm45", "f32", "rows"), ("glam", None, "rows"),
     ("glm5", None, "rows"), ("glam", None, "tiled"), ("decode", None, "tiled"),
-    ("glm45g", None, "tiled"), ("switch", None, "tiled")])
+    ("glm45g", None, "tiled"), ("switch", None, "tiled"), ("glm45dense", None, "tiled")])
 def test_full_size_forward(name, out_dtype, layout):
     cfg = workloads.get(name)
     out_dtype = out_dtype or cfg.dtype

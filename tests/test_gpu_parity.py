@@ -198,6 +198,7 @@ EDGE = {
     "single_token": S(workloads.GLM45_PREFILL, T=1, D=64, F=48, F_shared=48),
     "k_equals_m": S(workloads.GLM45_PREFILL, T=40, D=64, F=48, F_shared=0).replace(M=6, k=6),
     "one_expert_top1": S(workloads.GLAM_4K, T=130, D=72, F=56).replace(M=1, k=1),
+    "dense_prefix_swiglu": S(workloads.GLM45_DENSE, T=300, D=96, F=200),
     "switch_top1": S(workloads.GLAM_4K, T=300, D=128, F=64).replace(M=16, k=1),
     "alpha_zero": S(workloads.GLM45_PREFILL, T=50, D=64, F=48, F_shared=32).replace(alpha=0.0),
     "no_renorm_softmax": S(workloads.GLAM_4K, T=90, D=64, F=40).replace(renorm=False, alpha=1.5),

@@ -364,6 +364,18 @@ def test_single_expert_collapses_to_dense_ffn(scorer, act):
     assert np.allclose(y, cfg.alpha * ref, rtol=1e-12, atol=1e-12)
 
 
+def test_dense_prefix_layer_is_one_swiglu():
+    # the dense prefix workload: one expert, top-1 softmax, alpha 1: the gate
+    # weight is 1 exactly and the layer is a plain SwiGLU of the expert's width
+    cfg = workloads.shrink(workloads.GLM45_DENSE, T=9, D=32, F=24)
+    h = _host(cfg, seed=5)
+    idx, w, _ = oracle.route(cfg, h["x"], h["W_r"], h["bias"])
+    assert (idx == 0).all() and (w == 1.0).all()
+    y = oracle.layer(cfg, h["x"], idx, w, h["W1"], None, h["W2"], None)
+    ref = dense_swiglu(widen(h["x"]), widen(h["W1"])[0], widen(h["W2"])[0])
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
 def test_alpha_zero_leaves_plain_shared_swiglu():
     cfg = _small(workloads.GLM45_PREFILL).replace(alpha=0.0)
     h = _host(cfg, seed=8)

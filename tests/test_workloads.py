@@ -8,11 +8,15 @@ import workloads
 
 def test_configs_shapes():
     c = workloads.CONFIGS
-    assert [x.T for x in c] == [64, 4096, 8192, 16384, 64, 8192, 4096]
-    assert [x.M for x in c] == [8, 64, 160, 256, 160, 160, 64]
-    assert [x.k for x in c] == [2, 2, 8, 8, 8, 8, 1]
-    assert [(x.n_group, x.topk_group) for x in c] == [(0, 0)] * 5 + [(8, 4), (0, 0)]
+    assert [x.T for x in c] == [64, 4096, 8192, 16384, 64, 8192, 4096, 8192]
+    assert [x.M for x in c] == [8, 64, 160, 256, 160, 160, 64, 1]
+    assert [x.k for x in c] == [2, 2, 8, 8, 8, 8, 1, 1]
+    assert [(x.n_group, x.topk_group) for x in c] == [(0, 0)] * 5 + [(8, 4), (0, 0), (0, 0)]
     assert not workloads.SWITCH_TOP1.renorm
+    dense = workloads.GLM45_DENSE
+    # the dense prefix layer: one SwiGLU as wide as the MoE layer's active width
+    assert (dense.F, dense.F_shared, dense.act) == (8 * 1536 + 1536, 0, "swiglu")
+    assert dense.scorer == "softmax" and dense.alpha == 1.0 and dense.renorm
     assert workloads.GLM45_DECODE.D == workloads.GLM45_PREFILL.D
     assert workloads.get("glm45") is workloads.GLM45_PREFILL
 

@@ -102,14 +102,24 @@ GLM45_GROUPED = GLM45_PREFILL.replace(name="glm45_grouped_t8192_d5120_m160_f1536
 # renormalised weight would always be 1.
 SWITCH_TOP1 = GLAM_4K.replace(name="switch_top1_t4096_d4096_m64_f16384", k=1, renorm=False)
 
+# A dense prefix layer of the GLM-4.5-shaped model (the "Shared Expert" note,
+# "How it works": the first blocks hold one wide SwiGLU and no shared
+# expert) through the same kernels: one expert, top-1, softmax, so the gate
+# weight is exactly 1 and the layer is that plain SwiGLU.  The page gives no
+# width; this takes the MoE layer's active width per token (8 x 1536 routed
+# + 1536 shared = 13,824), so both layers do the same work per token.
+GLM45_DENSE = GLM45_PREFILL.replace(
+    name="glm45_dense_t8192_d5120_f13824", M=1, k=1, F=13824, F_shared=0,
+    scorer="softmax", alpha=1.0, router_bias_std=0.0)
+
 CONFIGS = [GLAM_TINY_FP32, GLAM_4K, GLM45_PREFILL, GLM5_ZIPF, GLM45_DECODE, GLM45_GROUPED,
-           SWITCH_TOP1]
+           SWITCH_TOP1, GLM45_DENSE]
 BY_NAME = {c.name: c for c in CONFIGS}
 # Short aliases used by the harness command line.
 ALIASES = {
     "tiny": GLAM_TINY_FP32, "glam": GLAM_4K, "glm45": GLM45_PREFILL,
     "glm5": GLM5_ZIPF, "decode": GLM45_DECODE, "glm45g": GLM45_GROUPED,
-    "switch": SWITCH_TOP1,
+    "switch": SWITCH_TOP1, "glm45dense": GLM45_DENSE,
 }
 
 
