@@ -326,7 +326,7 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
         up.b_extra = Wsh_gu;
         up.extra_group = (int)d->M;
     }
-    up.xcd_mode = gemm_xcd_mode(true, false);
+    up.xcd_mode = gemm_xcd_mode(true, false, d->M == 1 && !merged);
     up.offsets = offsets;
     up.a_rows = d->T;
     up.b_rows = (int)((swiglu ? 2 : 1) * d->F);
@@ -567,7 +567,7 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
     up.N = (int)F;
     up.F_split = (int)F;
     up.group_m = gemm_group_m(S, M, p.bm_up);
-    up.xcd_mode = gemm_xcd_mode(true, false);
+    up.xcd_mode = gemm_xcd_mode(true, false, M == 1);
     TRY(run(h, s, L_B_UP, [&] {
         return launch_gemm(s, 1, p.bm_up, swiglu ? EPI_SWIGLU_SAVE : EPI_GELU_SAVE, up,
                            p.max_tiles_up);

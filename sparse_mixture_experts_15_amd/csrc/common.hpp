@@ -175,8 +175,8 @@ int gemm_group_m(int64_t rows, int64_t groups, int bm);
 // output columns on the tile height bm.
 int gemm_part_cols(int bm, int64_t N);
 // Workgroup order (GemmArgs::xcd_mode) of a grouped or dense up or down
-// projection.
-int gemm_xcd_mode(bool grouped, bool down);
+// projection; one_group: a grouped GEMM whose rows all belong to one group.
+int gemm_xcd_mode(bool grouped, bool down, bool one_group = false);
 
 }  // namespace moe
 

@@ -1069,18 +1069,22 @@ int gemm_group_m(int64_t rows, int64_t groups, int bm) {
 // keep the hardware order: their tiles' cost follows the rows each expert
 // received, and dealing single tiles to the XCDs in turn balances them
 // best; measured faster than per-XCD groups by ~1% (GLM-4.5 prefill) to 9%
-// (GLM-5, Zipf-skewed).  The grouped down projections and the dense GEMMs
-// deal whole groups to the XCDs, which keeps a group's operand slabs in
-// one L2 (GLM-4.5 down projection 1.34 ms against 1.61 ms in hardware
-// order).
-int gemm_xcd_mode(bool grouped, bool down) {
+// (GLM-5, Zipf-skewed).  An up projection over one group (a single-expert
+// layer) has no such skew and gives each XCD a contiguous eighth of the
+// tiles (dense GLM-4.5-shaped prefix layer 3.15 -> 2.92 ms).  The grouped
+// down projections and the dense GEMMs deal whole groups to the XCDs, which
+// keeps a group's operand slabs in one L2 (GLM-4.5 down projection on
+// 128-row tiles 1.34 ms against 1.61 ms in hardware order; on 256-row tiles
+// the two orders are within 1%).
+int gemm_xcd_mode(bool grouped, bool down, bool one_group) {
     const char* name = grouped ? (down ? "MOE_XCD_DN" : "MOE_XCD_UP")
                                : (down ? "MOE_XCD_SH_DN" : "MOE_XCD_SH_UP");
     if (const char* env = getenv(name)) {   // tuning override
         const int v = atoi(env);
         if (v >= 0 && v <= 2) return v;
     }
-    return grouped && !down ? 1 : 0;
+    if (grouped && !down) return one_group ? 2 : 1;
+    return 0;
 }
 
 // Weight-gradient GEMM (wgrad_bf16): rows = g.dense_rows, one group per
