@@ -276,8 +276,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-aux-stream", action="store_true")
-    ap.add_argument("--weights", choices=["tiled", "rows"], default="tiled",
-                    help="expert/shared weight layout (tiled: copied once before timing)")
+    ap.add_argument("--weights", choices=["tiled", "rows"], default=None,
+                    help="expert/shared weight layout (tiled: copied once before timing); "
+                         "default tiled for bf16 layers, rows for fp32 (the tiled copy is bf16 only)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
     ap.add_argument("--backward", action="store_true",
@@ -307,6 +308,8 @@ def main():
     cfg = workloads.get(args.config)
     log(f"workload {cfg.name}: generating inputs on the GPU")
     t = workloads.generate(cfg, seed=args.seed, device="cuda")
+    if args.weights is None:
+        args.weights = "tiled" if cfg.dtype == "bf16" else "rows"
     L = MoELayer(B.make_desc(cfg, weight_layout=args.weights))
     d = L.desc
     tg = dict(t)   # what the GPU reads; t keeps the row-major weights for the oracle
