@@ -29,6 +29,9 @@ BWD = {
     "max_k16": S(workloads.GLM5_ZIPF, T=70, D=64, F=32, F_shared=0).replace(k=16),
     "many_experts_1024": S(workloads.GLM45_PREFILL, T=200, D=64, F=32,
                            F_shared=0).replace(M=1024, k=4),
+    # one expert, top-1 softmax: the gate is 1 exactly, so no gradient
+    # reaches the router and dW_r is zero on both sides
+    "dense_prefix_swiglu": S(workloads.GLM45_DENSE, T=200, D=96, F=200),
 }
 
 
