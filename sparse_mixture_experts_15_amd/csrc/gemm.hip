@@ -321,6 +321,90 @@ __device__ __forceinline__ bf16x8 kn_fragment(const bf16_t* bt, int kbase, int n
     return __builtin_bit_cast(bf16x8, r);
 }
 
+// The multiply of one K = 64 stage of a 256 x 256 tile whose fragments all
+// hold rows: eight waves, each 128 A rows (wave row wm) x 64 B rows (wave
+// column wn), accumulators acc[8][4]; the A rows sit at the stage's start,
+// the 256 B rows after them (row-major, or [K, N] when BKN).
+template <int BNB, int BKN>
+__device__ __forceinline__ void mfma_stage_full256(const bf16_t* st, floatx4 (&acc)[8][4], int wm,
+                                                   int wn, int lane) {
+    constexpr int BM = 256, BK = 64, TN = 4, WROWS = 128;
+    const int fr = lane & 15, fc = lane >> 4;
+    // 256-row tiles, whole fragments: each K half's rows 0-3 then
+    // 4-7, the next group's fragments read among the current
+    // group's MFMAs (pinned with scheduling groups; 22 more VGPRs
+    // than reading per K half, no spills).  Measured against the
+    // general body on one device: GLM-5-shaped routed up projection
+    // 7.56 -> 7.11 ms, GLM-4.5-shaped 2.29 -> 2.13 ms, its backward
+    // 15.1 -> 14.7 ms; outputs bitwise equal.
+    constexpr int RB = BKN ? 2 : 1;   // LDS reads per weight fragment
+    bf16x8 b0[TN], b1[TN], a00[4], a01[4], a10[4], a11[4];
+    auto rdB = [&](int kk, bf16x8(&bb)[TN]) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            if constexpr (BKN)
+                bb[j] = kn_fragment<BNB>(st + BM * BK, kk * 32, wn * 64 + 16 * j, lane);
+            else
+                bb[j] = *reinterpret_cast<const bf16x8*>(
+                    st + BM * BK + swz<BK>(wn * 64 + 16 * j + fr, kk * 4 + fc));
+        }
+    };
+    auto rdA = [&](int kk, int i0, bf16x8(&aa)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            aa[i] = *reinterpret_cast<const bf16x8*>(
+                st + swz<BK>(wm * WROWS + 16 * (i0 + i) + fr, kk * 4 + fc));
+    };
+    auto mm = [&](int i0, const bf16x8(&aa)[4], const bf16x8(&bb)[TN]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i0 + i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    bb[j], aa[i], acc[i0 + i][j], 0, 0, 0);
+    };
+    rdB(0, b0);
+    rdA(0, 0, a00);
+    __builtin_amdgcn_sched_group_barrier(0x100, TN * RB + 4, 0);
+    rdA(0, 4, a01);
+    mm(0, a00, b0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    rdB(1, b1);
+    rdA(1, 0, a10);
+    mm(4, a01, b0);
+    if constexpr (BKN) {   // 12 reads among 16 MFMAs
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    } else {   // 8 reads among 16 MFMAs
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    }
+    rdA(1, 4, a11);
+    mm(0, a10, b1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    mm(4, a11, b1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+}
+
 template <int EPI, int BM, int BNB, int STAGES, int KS, int BKN = 0>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int n_tiles) {
     static_assert(!BKN || (KS == 64 && !epi_pairs(EPI)), "KN-layout B: K = 64 stages, no pairing");
@@ -477,81 +561,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             body(st);
         }
     };
-    // the multiply of one stage for tiles whose fragments all hold rows
+    // the multiply of one stage for 256-row tiles whose fragments all hold rows
     auto body_full256 = [&](const bf16_t* st) {
-        // 256-row tiles, whole fragments: each K half's rows 0-3 then
-        // 4-7, the next group's fragments read among the current
-        // group's MFMAs (pinned with scheduling groups; 22 more VGPRs
-        // than reading per K half, no spills).  Measured against the
-        // general body on one device: GLM-5-shaped routed up projection
-        // 7.56 -> 7.11 ms, GLM-4.5-shaped 2.29 -> 2.13 ms, its backward
-        // 15.1 -> 14.7 ms; outputs bitwise equal.
-        constexpr int RB = BKN ? 2 : 1;   // LDS reads per weight fragment
-        bf16x8 b0[TN], b1[TN], a00[4], a01[4], a10[4], a11[4];
-        auto rdB = [&](int kk, bf16x8(&bb)[TN]) {
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                if constexpr (BKN)
-                    bb[j] = kn_fragment<BNB>(st + BM * BK, kk * 32, wn * 64 + 16 * j, lane);
-                else
-                    bb[j] = *reinterpret_cast<const bf16x8*>(
-                        st + BM * BK + swz<BK>(wn * 64 + 16 * j + fr, kk * 4 + fc));
-            }
-        };
-        auto rdA = [&](int kk, int i0, bf16x8(&aa)[4]) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                aa[i] = *reinterpret_cast<const bf16x8*>(
-                    st + swz<BK>(wm * WROWS + 16 * (i0 + i) + fr, kk * 4 + fc));
-        };
-        auto mm = [&](int i0, const bf16x8(&aa)[4], const bf16x8(&bb)[TN]) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i0 + i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        bb[j], aa[i], acc[i0 + i][j], 0, 0, 0);
-        };
-        rdB(0, b0);
-        rdA(0, 0, a00);
-        __builtin_amdgcn_sched_group_barrier(0x100, TN * RB + 4, 0);
-        rdA(0, 4, a01);
-        mm(0, a00, b0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        rdB(1, b1);
-        rdA(1, 0, a10);
-        mm(4, a01, b0);
-        if constexpr (BKN) {   // 12 reads among 16 MFMAs
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-        } else {   // 8 reads among 16 MFMAs
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-        }
-        rdA(1, 4, a11);
-        mm(0, a10, b1);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        mm(4, a11, b1);
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        if constexpr (TM == 8 && BK == 64) mfma_stage_full256<BNB, BKN>(st, acc, wm, wn, lane);
     };
     // the multiply of one stage in general (fragments past the group's
     // last row skip their reads and MFMAs)
@@ -829,23 +841,27 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16(GemmArgs g, int m_tiles, int
         __builtin_amdgcn_s_barrier();   // every wave's loads landed; stage kt-1 fully read
         if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
         const bf16_t* st = sm + (kt % STAGES) * STAGE;
+        if constexpr (BM == 256 && BNB == 256 && BK == 64) {
+            mfma_stage_full256<BNB, 0>(st, acc, wm, wn, lane);   // rows past the end read zeros
+        } else {
 #pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
-            bf16x8 af[TM], bfr[TN];
+            for (int kk = 0; kk < BK / 32; ++kk) {
+                bf16x8 af[TM], bfr[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(
-                    st + swz<BK>(wm * WROWS + 16 * i + fr, kk * 4 + fc));
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(
-                    st + BM * BK + swz<BK>(wn * 64 + 16 * j + fr, kk * 4 + fc));
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < TM; ++i)
+                    af[i] = *reinterpret_cast<const bf16x8*>(
+                        st + swz<BK>(wm * WROWS + 16 * i + fr, kk * 4 + fc));
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j],
-                                                                        0, 0, 0);
+                    bfr[j] = *reinterpret_cast<const bf16x8*>(
+                        st + BM * BK + swz<BK>(wn * 64 + 16 * j + fr, kk * 4 + fc));
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i],
+                                                                            acc[i][j], 0, 0, 0);
+            }
         }
     }
     // results straight from the accumulators: lane l holds row 16 i + l % 16
