@@ -148,6 +148,12 @@ def layer_work(cfg, U):
     return float(flops), float(byts)
 
 
+def default_weight_layout(cfg):
+    """The weights' layout when --weights is not given: the tiled copy for
+    bf16 layers (it exists for bf16 only), row-major for fp32 ones."""
+    return "tiled" if cfg.dtype == "bf16" else "rows"
+
+
 def cpu_baseline(cfg, t, target_s: float):
     """The oracle's whole per-token forward (router, experts, shared expert,
     sum) on a bounded token sample, on this host's cores."""
@@ -309,7 +315,7 @@ def main():
     log(f"workload {cfg.name}: generating inputs on the GPU")
     t = workloads.generate(cfg, seed=args.seed, device="cuda")
     if args.weights is None:
-        args.weights = "tiled" if cfg.dtype == "bf16" else "rows"
+        args.weights = default_weight_layout(cfg)
     L = MoELayer(B.make_desc(cfg, weight_layout=args.weights))
     d = L.desc
     tg = dict(t)   # what the GPU reads; t keeps the row-major weights for the oracle

@@ -31,6 +31,13 @@ def test_layer_work(name, U, tflop, gbytes):
     assert byts / 1e9 == pytest.approx(gbytes, rel=5e-3)
 
 
+def test_default_weight_layout_follows_dtype():
+    # the tiled weight copy is bf16 only: fp32 layers default to row-major
+    for cfg in workloads.CONFIGS:
+        assert bench.default_weight_layout(cfg) == ("tiled" if cfg.dtype == "bf16" else "rows")
+    assert bench.default_weight_layout(workloads.get("tiny")) == "rows"
+
+
 def test_backward_work_counts_all_experts_gradients():
     cfg = workloads.get("glm45")
     w, flops = bench.backward_work(cfg, 68)
