@@ -102,7 +102,22 @@ enum { MOE_WEIGHT_W1 = 0, MOE_WEIGHT_W2 = 1, MOE_WEIGHT_SH_GU = 2, MOE_WEIGHT_SH
  *            experts, only the topk_group best groups (lower group index on
  *            an exact tie) stay candidates for the top-k.  Requires
  *            n_group | M, n_group <= 64 and k <= topk_group * M / n_group.
- *            n_group <= 1: no grouping.                                  */
+ *            n_group <= 1: no grouping.
+ *
+ * Launch tuning (zero everywhere = the library's own choice; outputs are
+ * bitwise the same for every setting, only speed and the workspace size
+ * change, so moe_workspace_size must see the same values as the call):
+ *   tile_rows[4]  rows per workgroup tile of the bf16 GEMMs, in the order
+ *                 routed up, routed down, shared up, shared down projection:
+ *                 0 (choose), 64, 128, 160 or 256
+ *   tile_order[4] workgroup order of the same four GEMMs over the 8 XCDs:
+ *                 0 (choose), 1 whole tile groups dealt to the XCDs in turn,
+ *                 2 hardware order, 3 one contiguous eighth per XCD
+ *   group_m       m-tiles per group of the tile order: 0 (choose) or 1..16
+ *   shared_mode   0 (choose), 1 the shared expert in launches of its own
+ *                 (on aux_stream when given), 2 the shared expert as one
+ *                 more group of the routed GEMM launches (needs F_shared ==
+ *                 F, SwiGLU, bf16 and T <= 1024; otherwise as 1)        */
 typedef struct moe_desc {
     int64_t T, D, M, F, F_shared;
     int32_t k;
@@ -116,7 +131,14 @@ typedef struct moe_desc {
     int32_t weight_layout;
     int32_t n_group;
     int32_t topk_group;
+    int32_t tile_rows[4];
+    int32_t tile_order[4];
+    int32_t group_m;
+    int32_t shared_mode;
 } moe_desc;
+
+/* Indices of moe_desc.tile_rows / tile_order. */
+enum { MOE_GEMM_UP = 0, MOE_GEMM_DOWN = 1, MOE_GEMM_SHARED_UP = 2, MOE_GEMM_SHARED_DOWN = 3 };
 
 typedef struct moe_handle moe_handle;
 

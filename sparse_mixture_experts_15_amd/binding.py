@@ -39,7 +39,9 @@ class moe_desc(ctypes.Structure):
                 ("out_dtype", ctypes.c_int32), ("renorm", ctypes.c_int32),
                 ("alpha", ctypes.c_float), ("eps", ctypes.c_float),
                 ("weight_layout", ctypes.c_int32), ("n_group", ctypes.c_int32),
-                ("topk_group", ctypes.c_int32)]
+                ("topk_group", ctypes.c_int32), ("tile_rows", ctypes.c_int32 * 4),
+                ("tile_order", ctypes.c_int32 * 4), ("group_m", ctypes.c_int32),
+                ("shared_mode", ctypes.c_int32)]
 
 
 class moe_kernel_time(ctypes.Structure):
@@ -112,11 +114,19 @@ def _check(fn: str, rc: int):
         raise MoEError(fn, rc, last_error_detail())
 
 
+GEMMS = ("up", "down", "shared_up", "shared_down")   # order of tile_rows / tile_order
+ORDER = {"auto": 0, "xcd_groups": 1, "hardware": 2, "xcd_slices": 3}
+SHARED_MODE = {"auto": 0, "separate": 1, "merged": 2}
+
+
 def make_desc(cfg=None, **kw) -> moe_desc:
     """Descriptor from a layer config object (T, D, M, F, F_shared, k,
     scorer, act, dtype, renorm, alpha, eps) with keyword overrides; enum
     fields accept their names ("softmax", "swiglu", "bf16", "tiled", ...).
-    out_dtype defaults to dtype, weight_layout to "rows"."""
+    out_dtype defaults to dtype, weight_layout to "rows".  Launch tuning
+    (default: the library's choice): tile_rows and tile_order as dicts keyed
+    by GEMMS names or 4-sequences, group_m, shared_mode ("separate",
+    "merged")."""
     f = {}
     if cfg is not None:
         for n in ("T", "D", "M", "F", "F_shared", "k", "scorer", "act", "dtype", "renorm",
@@ -128,13 +138,27 @@ def make_desc(cfg=None, **kw) -> moe_desc:
     sc, ac, dt = f["scorer"], f["act"], f["dtype"]
     od = f.get("out_dtype", dt)
     wl = f.get("weight_layout", "rows")
+    def four(v, names=None):
+        if v is None:
+            return (ctypes.c_int32 * 4)(0, 0, 0, 0)
+        if isinstance(v, dict):
+            v = [v.get(g, 0) for g in GEMMS]
+        if isinstance(v, (int, str)):
+            v = [v] * 4
+        return (ctypes.c_int32 * 4)(*[int(names.get(x, x) if names else x) for x in v])
+
+    sm = f.get("shared_mode", 0)
     return moe_desc(T=int(f["T"]), D=int(f["D"]), M=int(f["M"]), F=int(f["F"]),
                     F_shared=int(f.get("F_shared", 0)), k=int(f["k"]),
                     scorer=SCORER.get(sc, sc), act=ACT.get(ac, ac), dtype=DTYPE.get(dt, dt),
                     out_dtype=DTYPE.get(od, od),
                     renorm=int(bool(f.get("renorm", 1))), alpha=float(f.get("alpha", 1.0)),
                     eps=float(f.get("eps", 1e-20)), weight_layout=LAYOUT.get(wl, wl),
-                    n_group=int(f.get("n_group", 0)), topk_group=int(f.get("topk_group", 0)))
+                    n_group=int(f.get("n_group", 0)), topk_group=int(f.get("topk_group", 0)),
+                    tile_rows=four(f.get("tile_rows")),
+                    tile_order=four(f.get("tile_order"), ORDER),
+                    group_m=int(f.get("group_m", 0)),
+                    shared_mode=int(SHARED_MODE.get(sm, sm)))
 
 
 def _ptr(t, name, dtype=None, numel=None):

@@ -2,7 +2,6 @@
 // fork/join and kernel launches.  Every check runs before the first
 // launch, so an error leaves the outputs and the streams untouched.
 #include <algorithm>
-#include <cstdlib>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -61,16 +60,18 @@ Plan make_plan(const moe_desc* d, bool allow_merge = true) {
     // A shared expert of one routed expert's shape joins the routed GEMMs
     // when the batch is decode-sized: alone its GEMMs have a handful of
     // workgroups and only contend with the router on the second stream.
-    const char* menv = getenv("MOE_MERGE_SHARED");   // tuning override: 0 keeps them apart
-    p.merged = allow_merge && d->F_shared > 0 && d->F_shared == d->F &&
-               d->act == MOE_ACT_SWIGLU && d->dtype == MOE_DTYPE_BF16 && d->T <= kSmallT &&
-               d->M + 1 <= 1024 && !(menv && atoi(menv) == 0);
+    // shared_mode 1 keeps it separate, 2 merges it wherever the shape allows.
+    const bool can_merge = d->F_shared > 0 && d->F_shared == d->F &&
+                           d->act == MOE_ACT_SWIGLU && d->dtype == MOE_DTYPE_BF16 &&
+                           d->T <= kSmallT && d->M + 1 <= 1024;
+    p.merged = allow_merge && can_merge && d->shared_mode != 1;
     const int64_t groups = d->M + (p.merged ? 1 : 0);
     p.Sx = p.S + (p.merged ? d->T : 0);
-    p.bm_up = gemm_block_m(d->dtype, p.Sx, groups, false, G * d->F);
-    p.bm_dn = gemm_block_m(d->dtype, p.Sx, groups, true, d->D);
-    p.bm_sh_up = gemm_block_m(d->dtype, d->T, 1, false, 2 * d->F_shared);
-    p.bm_sh_dn = gemm_block_m(d->dtype, d->T, 1, true, d->D);
+    p.bm_up = gemm_block_m(d->dtype, p.Sx, groups, false, G * d->F, d->tile_rows[MOE_GEMM_UP]);
+    p.bm_dn = gemm_block_m(d->dtype, p.Sx, groups, true, d->D, d->tile_rows[MOE_GEMM_DOWN]);
+    p.bm_sh_up = gemm_block_m(d->dtype, d->T, 1, false, 2 * d->F_shared,
+                              d->tile_rows[MOE_GEMM_SHARED_UP]);
+    p.bm_sh_dn = gemm_block_m(d->dtype, d->T, 1, true, d->D, d->tile_rows[MOE_GEMM_SHARED_DOWN]);
     // ceil(Sx / bm) tiles plus at most one partial tile per non-empty group
     const int64_t partial = groups < p.Sx ? groups : p.Sx;
     p.max_tiles_up = (p.Sx + p.bm_up - 1) / p.bm_up + partial;
@@ -137,6 +138,16 @@ int validate(const moe_desc* d) {
             return fail(MOE_ERR_INVALID, "topk_group=%d must be in [1, n_group] and keep >= k "
                         "experts", d->topk_group);
     }
+    for (int i = 0; i < 4; ++i) {
+        const int r = d->tile_rows[i], o = d->tile_order[i];
+        if (r != 0 && r != 64 && r != 128 && r != 160 && r != 256)
+            return fail(MOE_ERR_INVALID, "tile_rows[%d]=%d is not 0, 64, 128, 160 or 256", i, r);
+        if (o < 0 || o > 3) return fail(MOE_ERR_INVALID, "tile_order[%d]=%d is not in [0, 3]", i, o);
+    }
+    if (d->group_m < 0 || d->group_m > 16)
+        return fail(MOE_ERR_INVALID, "group_m=%d is not in [0, 16]", d->group_m);
+    if (d->shared_mode < 0 || d->shared_mode > 2)
+        return fail(MOE_ERR_INVALID, "shared_mode=%d is not in [0, 2]", d->shared_mode);
     if (d->weight_layout != MOE_LAYOUT_ROWS && d->weight_layout != MOE_LAYOUT_TILED)
         return fail(MOE_ERR_INVALID, "unknown weight_layout %d", d->weight_layout);
     if (d->weight_layout == MOE_LAYOUT_TILED && d->dtype != MOE_DTYPE_BF16)
@@ -321,12 +332,12 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     up.c = H;
     up.tiles = tiles_up;
     up.dense_rows = rows;
-    up.group_m = gemm_group_m(rows, d->M, p.bm_up);
+    up.group_m = gemm_group_m(rows, d->M, p.bm_up, d->group_m);
     if (merged) {
         up.b_extra = Wsh_gu;
         up.extra_group = (int)d->M;
     }
-    up.xcd_mode = gemm_xcd_mode(true, false, d->M == 1 && !merged);
+    up.xcd_mode = gemm_xcd_mode(true, false, d->M == 1 && !merged, d->tile_order[MOE_GEMM_UP]);
     up.offsets = offsets;
     up.a_rows = d->T;
     up.b_rows = (int)((swiglu ? 2 : 1) * d->F);
@@ -347,12 +358,12 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     dn.dense_rows = rows;
     dn.c = O;
     dn.tiles = tiles_dn;
-    dn.group_m = gemm_group_m(rows, d->M, p.bm_dn);
+    dn.group_m = gemm_group_m(rows, d->M, p.bm_dn, d->group_m);
     if (merged) {
         dn.b_extra = Wsh_dn;
         dn.extra_group = (int)d->M;
     }
-    dn.xcd_mode = gemm_xcd_mode(true, true);
+    dn.xcd_mode = gemm_xcd_mode(true, true, false, d->tile_order[MOE_GEMM_DOWN]);
     dn.offsets = offsets;
     dn.a_rows = rows;
     dn.b_rows = (int)d->D;
@@ -380,7 +391,7 @@ int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, co
     up.K = (int)d->D;
     up.N = (int)d->F_shared;
     up.F_split = (int)d->F_shared;
-    up.xcd_mode = gemm_xcd_mode(false, false);
+    up.xcd_mode = gemm_xcd_mode(false, false, false, d->tile_order[MOE_GEMM_SHARED_UP]);
     TRY(run(h, s, L_SHARED_UP,
             [&] { return launch_gemm(s, d->dtype, p.bm_sh_up, EPI_SWIGLU, up, mt_up); }));
     GemmArgs dn{};
@@ -394,7 +405,7 @@ int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, co
     dn.b_rows = (int)d->D;
     dn.K = (int)d->F_shared;
     dn.N = (int)d->D;
-    dn.xcd_mode = gemm_xcd_mode(false, true);
+    dn.xcd_mode = gemm_xcd_mode(false, true, false, d->tile_order[MOE_GEMM_SHARED_DOWN]);
     return run(h, s, L_SHARED_DOWN,
                [&] { return launch_gemm(s, d->dtype, p.bm_sh_dn, EPI_DOWN_F32, dn, mt_dn); });
 }
@@ -566,8 +577,8 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
     up.K = (int)D;
     up.N = (int)F;
     up.F_split = (int)F;
-    up.group_m = gemm_group_m(S, M, p.bm_up);
-    up.xcd_mode = gemm_xcd_mode(true, false, M == 1);
+    up.group_m = gemm_group_m(S, M, p.bm_up, d->group_m);
+    up.xcd_mode = gemm_xcd_mode(true, false, M == 1, d->tile_order[MOE_GEMM_UP]);
     TRY(run(h, s, L_B_UP, [&] {
         return launch_gemm(s, 1, p.bm_up, swiglu ? EPI_SWIGLU_SAVE : EPI_GELU_SAVE, up,
                            p.max_tiles_up);
@@ -611,8 +622,8 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
     dxg.b_rows = (int)D;
     dxg.K = (int)GF;
     dxg.N = (int)D;
-    dxg.group_m = gemm_group_m(S, M, bm_dx);
-    dxg.xcd_mode = gemm_xcd_mode(true, true);
+    dxg.group_m = gemm_group_m(S, M, bm_dx, d->group_m);
+    dxg.xcd_mode = gemm_xcd_mode(true, true, false, d->tile_order[MOE_GEMM_DOWN]);
     TRY(run(h, s, L_B_DX, [&] {
         return launch_gemm(s, 1, bm_dx, EPI_DOWN_F32, dxg,
                            dx_up ? p.max_tiles_up : p.max_tiles_dn);
@@ -683,14 +694,8 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
     w1.koff = poff;
     w1.kgroups = (int)M;
     w1.c_group_stride = GF * D;
-    // the weight-gradient kernel (store-bound products); MOE_WGRAD_GEMM=0
-    // runs them on the general GEMM instead (tuning comparison)
-    const char* wenv = getenv("MOE_WGRAD_GEMM");
-    const bool wk = !(wenv && atoi(wenv) == 0);
-    auto wgrad = [&](const GemmArgs& g, int bm, int64_t rows) {
-        return wk ? launch_wgrad(s, g)
-                  : launch_gemm(s, 1, bm, EPI_DOWN_F32, g, (rows + bm - 1) / bm);
-    };
+    // the weight-gradient kernel (store-bound products)
+    auto wgrad = [&](const GemmArgs& g, int, int64_t) { return launch_wgrad(s, g); };
     TRY(run(h, s, L_B_WGRAD, [&] {
         hipError_t e = wgrad(w2, b.bm_w2, D);
         if (e != hipSuccess) return e;

@@ -170,13 +170,15 @@ hipError_t launch_tile_weights(hipStream_t s, const void* src, void* dst, int64_
 // m-tiles per group of the tile order for a grouped GEMM: about the m-tiles
 // one expert spans, so that the workgroups one XCD runs together share that
 // expert's weight tiles and rows in its L2.
-int gemm_group_m(int64_t rows, int64_t groups, int bm);
+// `request` (1..16) overrides the choice.
+int gemm_group_m(int64_t rows, int64_t groups, int bm, int request = 0);
 // Columns of the EPI_DH_* partial-dot buffer (part_ld) for a GEMM of N
 // output columns on the tile height bm.
 int gemm_part_cols(int bm, int64_t N);
 // Workgroup order (GemmArgs::xcd_mode) of a grouped or dense up or down
 // projection; one_group: a grouped GEMM whose rows all belong to one group.
-int gemm_xcd_mode(bool grouped, bool down, bool one_group = false);
+// `request` (moe_desc.tile_order: 1..3) overrides the choice.
+int gemm_xcd_mode(bool grouped, bool down, bool one_group = false, int request = 0);
 
 }  // namespace moe
 
@@ -257,7 +259,9 @@ hipError_t launch_fill_zero(hipStream_t s, float* p, int64_t n);
 // Rows per m-tile of a GEMM for a dtype, given its total rows, the number of
 // groups (experts) sharing them, whether it is a down projection and the
 // rows of its weight matrix (output columns, both halves for SwiGLU).
-int gemm_block_m(int dtype, int64_t rows, int64_t groups, bool down, int64_t b_rows);
+// `request` (64, 128, 160 or 256; moe_desc.tile_rows) overrides the choice.
+int gemm_block_m(int dtype, int64_t rows, int64_t groups, bool down, int64_t b_rows,
+                 int request = 0);
 // Token block of the permute kernels.
 constexpr int kPermBlock = 256;
 }  // namespace moe

@@ -39,8 +39,6 @@
 // x all n-tiles, dealt to the XCDs in an order chosen per GEMM, so the
 // workgroups resident on one XCD share operand K slabs in its L2.  fp32
 // path: a plain SIMT tile kernel (64 x 64, K step 16).
-#include <cstdlib>
-
 #include "common.hpp"
 
 namespace moe {
@@ -1052,15 +1050,10 @@ hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64
 // 0.42 -> 0.32 ms, down 0.79 -> 0.39 ms); the router's narrow logit GEMM
 // keeps 128-row tiles.  Measured on MI355X over the layer shapes the tests
 // use.
-int gemm_block_m(int dtype, int64_t rows, int64_t groups, bool down, int64_t b_rows) {
+int gemm_block_m(int dtype, int64_t rows, int64_t groups, bool down, int64_t b_rows,
+                 int request) {
     if (dtype != 1) return FBM;
-    // tuning override: MOE_GEMM_BM_{UP,DN} (grouped) / MOE_GEMM_BM_SH_{UP,DN} (dense)
-    const char* name = groups > 1 ? (down ? "MOE_GEMM_BM_DN" : "MOE_GEMM_BM_UP")
-                                  : (down ? "MOE_GEMM_BM_SH_DN" : "MOE_GEMM_BM_SH_UP");
-    if (const char* env = getenv(name)) {
-        const int v = atoi(env);
-        if (v == 64 || v == 128 || v == 160 || v == 256) return v;
-    }
+    if (request == 64 || request == 128 || request == 160 || request == 256) return request;
     if (groups <= 1) {
         const int64_t tiles256 = (rows / 256) * ((b_rows + 255) / 256);
         return tiles256 >= 256 ? 256 : 128;
@@ -1072,11 +1065,8 @@ int gemm_block_m(int dtype, int64_t rows, int64_t groups, bool down, int64_t b_r
     return 256;
 }
 
-int gemm_group_m(int64_t rows, int64_t groups, int bm) {
-    if (const char* env = getenv("MOE_GEMM_GROUP_M")) {   // tuning override
-        const int v = atoi(env);
-        if (v >= 1 && v <= 16) return v;
-    }
+int gemm_group_m(int64_t rows, int64_t groups, int bm, int request) {
+    if (request >= 1 && request <= 16) return request;
     const int64_t per = (rows / (groups > 0 ? groups : 1) + bm / 2) / bm;
     return per < 1 ? 1 : per > 4 ? 4 : (int)per;
 }
@@ -1092,13 +1082,10 @@ int gemm_group_m(int64_t rows, int64_t groups, int bm) {
 // keeps a group's operand slabs in one L2 (GLM-4.5 down projection on
 // 128-row tiles 1.34 ms against 1.61 ms in hardware order; on 256-row tiles
 // the two orders are within 1%).
-int gemm_xcd_mode(bool grouped, bool down, bool one_group) {
-    const char* name = grouped ? (down ? "MOE_XCD_DN" : "MOE_XCD_UP")
-                               : (down ? "MOE_XCD_SH_DN" : "MOE_XCD_SH_UP");
-    if (const char* env = getenv(name)) {   // tuning override
-        const int v = atoi(env);
-        if (v >= 0 && v <= 2) return v;
-    }
+int gemm_xcd_mode(bool grouped, bool down, bool one_group, int request) {
+    // request: 1 groups dealt to the XCDs (mode 0), 2 hardware order (mode
+    // 1), 3 contiguous eighths (mode 2)
+    if (request >= 1 && request <= 3) return request - 1;
     if (grouped && !down) return one_group ? 2 : 1;
     return 0;
 }

@@ -35,11 +35,13 @@ def test_descriptor_layout_matches_header(tmp_path):
     prog = tmp_path / "layout.c"
     prog.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
-        'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_kernel_time),'
-        ' sizeof(moe_desc),'
+        'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n",'
+        ' sizeof(moe_kernel_time), sizeof(moe_desc),'
         ' offsetof(moe_desc,k), offsetof(moe_desc,renorm), offsetof(moe_desc,alpha),'
         ' offsetof(moe_desc,eps), offsetof(moe_desc,weight_layout),'
-        ' offsetof(moe_desc,topk_group)); return 0;}\n')
+        ' offsetof(moe_desc,topk_group), offsetof(moe_desc,tile_rows),'
+        ' offsetof(moe_desc,tile_order), offsetof(moe_desc,group_m),'
+        ' offsetof(moe_desc,shared_mode)); return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)],
                    check=True)
@@ -48,7 +50,8 @@ def test_descriptor_layout_matches_header(tmp_path):
     d = B.moe_desc
     assert got == [ctypes.sizeof(B.moe_kernel_time), ctypes.sizeof(d), d.k.offset,
                    d.renorm.offset, d.alpha.offset, d.eps.offset, d.weight_layout.offset,
-                   d.topk_group.offset]
+                   d.topk_group.offset, d.tile_rows.offset, d.tile_order.offset,
+                   d.group_m.offset, d.shared_mode.offset]
 
 
 def _ws(desc):
@@ -76,11 +79,17 @@ def test_workspace_size_covers_intermediates():
     ("D", 0, B.MOE_ERR_INVALID), ("F_shared", -8, B.MOE_ERR_INVALID),
     ("D", 12, B.MOE_ERR_UNSUPPORTED), ("F", 20, B.MOE_ERR_UNSUPPORTED),
     ("F_shared", 4, B.MOE_ERR_UNSUPPORTED), ("weight_layout", 2, B.MOE_ERR_INVALID),
+    ("tile_rows", 96, B.MOE_ERR_INVALID), ("tile_rows", -64, B.MOE_ERR_INVALID),
+    ("tile_order", 4, B.MOE_ERR_INVALID), ("group_m", 17, B.MOE_ERR_INVALID),
+    ("shared_mode", 3, B.MOE_ERR_INVALID),
 ])
 def test_bad_descriptor_rejected(field, value, status):
     cfg = workloads.shrink(workloads.GLAM_4K, T=16, D=64, F=32).replace(M=8)
     d = B.make_desc(cfg)
-    setattr(d, field, value)
+    if field in ("tile_rows", "tile_order"):
+        getattr(d, field)[1] = value
+    else:
+        setattr(d, field, value)
     n = ctypes.c_size_t(123)
     rc = B.load_library().moe_workspace_size(ctypes.byref(d), ctypes.byref(n))
     assert rc == status, B.last_error_detail()
@@ -198,3 +207,27 @@ def test_backward_workspace_and_unsupported_layers():
         rc = lib.moe_backward_workspace_size(ctypes.byref(d2), ctypes.byref(out))
         assert rc == B.MOE_ERR_UNSUPPORTED, B.last_error_detail()
         assert out.value == 5
+
+
+def test_tuning_fields_select_the_plan_not_the_result_shape():
+    """The launch tuning in the descriptor (no environment variables) is
+    accepted for every valid value and changes only the workspace plan: the
+    tile tables grow with smaller tiles.  The library reads no environment."""
+    cfg = workloads.GLM45_PREFILL
+    base = B.moe_workspace_size(B.make_desc(cfg))
+    for rows in (64, 128, 160, 256):
+        for order in ("xcd_groups", "hardware", "xcd_slices"):
+            d = B.make_desc(cfg, tile_rows=rows, tile_order=order, group_m=3,
+                            shared_mode="separate")
+            n = B.moe_workspace_size(d)
+            assert abs(n - base) < 4 * 2**20
+    small = B.moe_workspace_size(B.make_desc(cfg, tile_rows={"up": 64, "down": 64}))
+    assert small >= B.moe_workspace_size(B.make_desc(cfg, tile_rows={"up": 256, "down": 256}))
+    # decode: the merged shared expert needs room for its rows in H and O
+    dec = workloads.GLM45_DECODE
+    sep = B.moe_workspace_size(B.make_desc(dec, shared_mode="separate"))
+    mer = B.moe_workspace_size(B.make_desc(dec, shared_mode="merged"))
+    assert mer != sep
+    out = subprocess.run(["nm", "-D", "--undefined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert not re.search(r"\bgetenv\b", out), "the library reads the environment"

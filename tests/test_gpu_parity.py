@@ -51,11 +51,12 @@ PARITY = {
 }
 
 
-def _stage_parity(cfg, seed=0, out_dtype=None, tiled=False):
+def _stage_parity(cfg, seed=0, out_dtype=None, tiled=False, **tuning):
     out_dtype = out_dtype or cfg.dtype
     t = workloads.generate(cfg, seed=seed, device="cuda")
     h = workloads.host_inputs(t)
-    L = new_layer(cfg, out_dtype=out_dtype, weight_layout="tiled" if tiled else "rows")
+    L = new_layer(cfg, out_dtype=out_dtype, weight_layout="tiled" if tiled else "rows",
+                  **tuning)
     d = L.desc
     if tiled:   # the GPU gets the tiled copies; the oracle keeps the row-major h
         t = tiled_weights(L, t)
@@ -174,24 +175,26 @@ def test_forward_deterministic_and_stream_invariant(name):
 # ------------------------------------------------------------------ edges
 
 # Every bf16 tile height on every GEMM (the library picks one per shape; the
-# MOE_GEMM_BM_* overrides force the others), covering both activations, the
-# grouped and dense GEMMs and every epilogue.
+# descriptor's tile_rows forces the others), covering both activations, the
+# grouped and dense GEMMs and every epilogue, and every workgroup order.
 @pytest.mark.parametrize("bm", [64, 128, 160, 256])
 @pytest.mark.parametrize("name", ["glam_tiles", "glm45_small", "glam_mid"])
-def test_tile_heights(name, bm, monkeypatch):
-    for var in ("MOE_GEMM_BM_UP", "MOE_GEMM_BM_DN", "MOE_GEMM_BM_SH_UP", "MOE_GEMM_BM_SH_DN"):
-        monkeypatch.setenv(var, str(bm))
-    _stage_parity(PARITY[name])
+def test_tile_heights(name, bm):
+    _stage_parity(PARITY[name], tile_rows=bm)
 
 
 # The same on the tiled weight copies: 64-row tiles read half of each 256-row
 # weight block.
 @pytest.mark.parametrize("bm", [64, 128, 160, 256])
 @pytest.mark.parametrize("name", ["glam_tiles", "glm45_small"])
-def test_tile_heights_tiled(name, bm, monkeypatch):
-    for var in ("MOE_GEMM_BM_UP", "MOE_GEMM_BM_DN", "MOE_GEMM_BM_SH_UP", "MOE_GEMM_BM_SH_DN"):
-        monkeypatch.setenv(var, str(bm))
-    _stage_parity(PARITY[name], tiled=True)
+def test_tile_heights_tiled(name, bm):
+    _stage_parity(PARITY[name], tiled=True, tile_rows=bm)
+
+
+@pytest.mark.parametrize("order", ["xcd_groups", "hardware", "xcd_slices"])
+@pytest.mark.parametrize("name", ["glm45_small", "glm5_rows"])
+def test_tile_orders(name, order):
+    _stage_parity(PARITY[name], tile_order=order, group_m=2)
 
 
 EDGE = {
