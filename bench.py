@@ -1,6 +1,6 @@
 """Throughput of the MoE layer forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config glam|glm45|glm5|decode|glm45g|switch|glm45dense|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config glm45|glam|glm5|decode|glm45g|switch|glm45dense|tiny]
 
 One step is one moe_forward over one batch of synthetic, seeded, HBM-resident
 inputs: router, dispatch, expert FFNs, shared expert (second stream) and
@@ -12,9 +12,11 @@ combine.  Prints ONE JSON line on stdout (logs go to stderr):
   over its average launch time, measured with HIP events on its own stream
   during the timed steps, against MI355X's published peak;
 * cpu_baseline = the CPU oracle timed on this host on a bounded sample of
-  the same workload.
-The default workload is the GLaM-shaped layer (T=4096, D=4096, 64 experts,
-top-2, GELU 16384).
+  the same workload (all host threads; also one thread, and the router and
+  dispatch over every token).
+The default workload is the GLM-4.5-shaped prefill layer (T=8192, D=5120,
+160 experts, top-8 sigmoid routing with correction bias, SwiGLU 1536, one
+shared SwiGLU expert 1536) on the tiled weight copies.
 """
 from __future__ import annotations
 
@@ -100,24 +102,27 @@ def calib_copy():
 
 def kernel_work(cfg, counts):
     """Algorithmic FLOPs and HBM bytes per launch of each kernel, from the
-    layer shape and the realised per-expert counts (touched experts only)."""
+    layer shape and the realised per-expert counts.  Bytes are the layer's
+    algorithmic ones that the kernel moves: the touched experts' weights, the
+    shared and router weights, x read and y written.  The intermediates (the
+    hidden activations H, the gate-scaled expert rows O, the shared rows Ysh,
+    the dispatch arrays) are implementation traffic and not credited."""
     esz = 2 if cfg.dtype == "bf16" else 4
     T, D, M, F, k, Fs, G = cfg.T, cfg.D, cfg.M, cfg.F, cfg.k, cfg.F_shared, cfg.G
     S = T * k
     U = int(sum(1 for c in counts if c > 0))
     w = {}
-    w["route"] = (2.0 * T * D * M, T * D * esz + M * D * 4 + S * 8)
-    w["ffn_up"] = (2.0 * S * D * G * F, U * G * F * D * esz + T * D * esz + S * F * esz)
-    # the expert rows O are fp32
-    w["ffn_down"] = (2.0 * S * F * D, U * D * F * esz + S * F * esz + S * D * 4)
-    w["combine"] = (float(S * D), S * D * 4 + (T * D * 4 if Fs else 0) + T * D * esz)
-    w["perm_count"] = (0.0, S * 4)
+    w["route"] = (2.0 * T * D * M, T * D * esz + M * D * 4)
+    w["ffn_up"] = (2.0 * S * D * G * F, U * G * F * D * esz + T * D * esz)
+    w["ffn_down"] = (2.0 * S * F * D, U * D * F * esz)
+    w["combine"] = (float(S * D), T * D * esz)
+    w["perm_count"] = (0.0, 0)
     w["perm_scan"] = (0.0, 0)
-    w["perm_scatter"] = (0.0, S * 4 * 4)
+    w["perm_scatter"] = (0.0, 0)
     w["tile_table"] = (0.0, 0)
     if Fs:
-        w["shared_up"] = (2.0 * T * D * 2 * Fs, 2 * Fs * D * esz + T * D * esz + T * Fs * esz)
-        w["shared_down"] = (2.0 * T * Fs * D, D * Fs * esz + T * Fs * esz + T * D * 4)
+        w["shared_up"] = (2.0 * T * D * 2 * Fs, 2 * Fs * D * esz + T * D * esz)
+        w["shared_down"] = (2.0 * T * Fs * D, D * Fs * esz)
     return w, U
 
 
@@ -154,9 +159,29 @@ def default_weight_layout(cfg):
     return "tiled" if cfg.dtype == "bf16" else "rows"
 
 
+def _timed_sample(cfg, h, rng, target_s, nthr):
+    """Tokens/s of the oracle's whole per-token forward on a random token
+    sample sized to take about target_s with nthr threads."""
+    import oracle
+    probe = max(nthr, 2)
+    toks = rng.choice(cfg.T, size=min(cfg.T, probe), replace=False)
+    t0 = time.perf_counter()
+    oracle.forward(cfg, h, tokens=toks)
+    per_tok = (time.perf_counter() - t0) / len(toks)
+    n = int(min(cfg.T, max(len(toks), target_s / max(per_tok, 1e-9))))
+    n = max(nthr, (n // nthr) * nthr) if n >= nthr else n
+    toks = rng.choice(cfg.T, size=min(cfg.T, n), replace=False)
+    t0 = time.perf_counter()
+    oracle.forward(cfg, h, tokens=toks)
+    dt = time.perf_counter() - t0
+    return len(toks) / dt, len(toks), dt
+
+
 def cpu_baseline(cfg, t, target_s: float):
-    """The oracle's whole per-token forward (router, experts, shared expert,
-    sum) on a bounded token sample, on this host's cores."""
+    """The oracle on this host's cores: its whole per-token forward (router,
+    experts, shared expert, sum) on a bounded random token sample with every
+    host thread and with one thread, and its router plus dispatch over all T
+    tokens."""
     import numpy as np
 
     import oracle
@@ -164,21 +189,26 @@ def cpu_baseline(cfg, t, target_s: float):
     h = workloads.host_inputs(t)
     nthr = oracle.num_threads()
     rng = np.random.default_rng(0)
-    probe = max(nthr, 4)
-    toks = rng.choice(cfg.T, size=min(cfg.T, probe), replace=False)
+    value, n, dt = _timed_sample(cfg, h, rng, target_s, nthr)
+    oracle.set_num_threads(1)
+    try:
+        v1, n1, dt1 = _timed_sample(cfg, h, rng, target_s / 4, 1)
+    finally:
+        oracle.set_num_threads(nthr)
     t0 = time.perf_counter()
-    oracle.forward(cfg, h, tokens=toks)
-    dt = time.perf_counter() - t0
-    per_tok = dt / len(toks)
-    n = int(min(cfg.T, max(len(toks), target_s / max(per_tok, 1e-9))))
-    n = max(nthr, (n // nthr) * nthr) if n >= nthr else n
-    toks = rng.choice(cfg.T, size=min(cfg.T, n), replace=False)
+    idx, _, _ = oracle.route(cfg, h["x"], h["W_r"], h["bias"])
+    t_route = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oracle.forward(cfg, h, tokens=toks)
-    dt = time.perf_counter() - t0
-    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
-            "sample": f"{len(toks)} random tokens of {cfg.name} (seed 0), whole per-token "
-                      f"forward in fp64, {dt:.1f} s"}
+    oracle.dispatch(cfg.T, cfg.k, cfg.M, idx)
+    t_disp = time.perf_counter() - t0
+    return {"value": value, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+            "sample": f"{n} random tokens of {cfg.name} (seed 0), whole per-token forward "
+                      f"in fp64, {dt:.1f} s on {nthr} threads",
+            "single_core": {"value": v1, "unit": "tokens/s", "sample": f"{n1} tokens, "
+                            f"{dt1:.1f} s on 1 thread"},
+            "router_dispatch_all_tokens": {"route_s": round(t_route, 3),
+                                           "dispatch_s": round(t_disp, 4), "tokens": cfg.T,
+                                           "threads": nthr}}
 
 
 def backward_work(cfg, U):
@@ -277,7 +307,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 20; 100 for the decode workload)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="glam")
+    ap.add_argument("--config", default="glm45")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

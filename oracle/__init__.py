@@ -76,6 +76,8 @@ def _load():
         lib.oracle_backward.argtypes = [cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, i64]
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         for f in ("oracle_route", "oracle_dispatch", "oracle_expert", "oracle_shared",
                   "oracle_layer", "oracle_forward", "oracle_backward"):
             getattr(lib, f).restype = None
@@ -85,6 +87,12 @@ def _load():
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (timing only; results are the
+    same for any count)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def make_cfg(cfg) -> _Cfg:

@@ -72,6 +72,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads the oracle's parallel loops use from now on (timing only: the
+ * results do not depend on it, every token is computed on its own). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Router for one token [GLaM router and TopK; GLM45 sigmoid router]. */
 static void route_token(const moe_oracle_cfg* c, const void* x, const float* W_r,
                         const float* bias, int64_t t, int32_t* idx_out,

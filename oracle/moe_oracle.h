@@ -107,6 +107,7 @@ void oracle_backward(const moe_oracle_cfg* c, const void* x, const float* W_r,
 
 /* Number of OpenMP threads the oracle will use. */
 int oracle_num_threads(void);
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

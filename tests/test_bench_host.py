@@ -55,3 +55,29 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_kernel_work_credits_only_algorithmic_bytes():
+    """Per kernel, only the touched weights, x and y are credited: no hidden
+    activations H, no fp32 expert rows O, no shared rows Ysh."""
+    cfg = workloads.get("glm45")
+    counts = [100] * 68 + [0] * (cfg.M - 68)
+    w, U = bench.kernel_work(cfg, counts)
+    assert U == 68
+    T, D, F, S = cfg.T, cfg.D, cfg.F, cfg.T * cfg.k
+    assert w["ffn_up"] == (2.0 * S * D * 2 * F, 68 * 2 * F * D * 2 + T * D * 2)
+    assert w["ffn_down"] == (2.0 * S * F * D, 68 * D * F * 2)
+    assert w["shared_up"][1] == 2 * cfg.F_shared * D * 2 + T * D * 2
+    assert w["shared_down"][1] == D * cfg.F_shared * 2
+    assert w["combine"][1] == T * D * 2
+    # the up projection is MFMA-bound at this shape: its FLOPs over its bytes
+    # exceed the ridge of 2.5 PFLOP/s over 8 TB/s
+    fl, by = w["ffn_up"]
+    assert fl / by > bench.PEAK_BF16_TFLOPS / bench.PEAK_HBM_GBPS * 1e3
+
+
+def test_default_workload_is_the_glm45_prefill_layer():
+    import argparse
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert 'ap.add_argument("--config", default="glm45")' in src
+    assert workloads.get("glm45").name == "glm45_t8192_d5120_m160_f1536"

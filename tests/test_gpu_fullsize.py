@@ -2,9 +2,11 @@
 expert on a second stream (the configuration the benchmark times).
 
 Every token's top-k and the whole dispatch are compared bit-exactly with
-the oracle (tie rule aside); the layer output is compared on a sample of
-tokens the oracle evaluates one by one: the first token of each of several
-experts (cold and hot) plus a seeded random fill.
+the oracle (tie rule aside); the layer output is compared on at least 512
+tokens the oracle evaluates one by one: the first and last token of every
+expert that received rows, then a seeded random fill.  The bar is
+max|err| <= 2e-2 * RMS(oracle) on the output as returned, bf16 included,
+with no allowance for its rounding.
 """
 import gc
 
@@ -19,25 +21,32 @@ from tests.gpu_util import (check_float, check_dispatch_props, check_route, forw
 
 pytestmark = pytest.mark.gpu
 
+N_SAMPLE = 512
 
-def _sample_tokens(cfg, disp, n_random=24, n_expert=24, seed=0):
+
+def _sample_tokens(cfg, disp, n_total=N_SAMPLE, seed=0):
     offs, st = disp["offsets"], disp["sorted_token"]
-    touched = [e for e in range(cfg.M) if offs[e + 1] > offs[e]]
-    by_count = sorted(touched, key=lambda e: offs[e + 1] - offs[e])
-    pick = by_count[: n_expert // 2] + by_count[-(n_expert // 2):]
-    toks = {int(st[offs[e]]) for e in pick}
-    toks |= {int(st[offs[e + 1] - 1]) for e in pick}
+    toks = {0, cfg.T - 1}
+    for e in range(cfg.M):
+        if offs[e + 1] > offs[e]:
+            toks.add(int(st[offs[e]]))
+            toks.add(int(st[offs[e + 1] - 1]))
     rng = np.random.default_rng(seed)
-    toks |= set(rng.choice(cfg.T, size=min(n_random, cfg.T), replace=False).tolist())
-    toks |= {0, cfg.T - 1}
+    rest = np.setdiff1d(np.arange(cfg.T), np.fromiter(toks, np.int64))
+    need = max(0, min(n_total, cfg.T) - len(toks))
+    toks |= set(rng.choice(rest, size=need, replace=False).tolist())
     return np.array(sorted(toks), dtype=np.int64)
 
 
-@pytest.mark.parametrize("name,out_dtype,layout", [
+CASES = [
     ("tiny", None, "rows"), ("decode", None, "rows"), ("decode", "f32", "rows"),
     ("glm45", None, "rows"), ("glm45", "f32", "rows"), ("glam", None, "rows"),
     ("glm5", None, "rows"), ("glam", None, "tiled"), ("decode", None, "tiled"),
-    ("glm45g", None, "tiled"), ("switch", None, "tiled"), ("glm45dense", None, "tiled")])
+    ("glm45", None, "tiled"), ("glm45", "f32", "tiled"), ("glm5", None, "tiled"),
+    ("glm45g", None, "tiled"), ("switch", None, "tiled"), ("glm45dense", None, "tiled")]
+
+
+@pytest.mark.parametrize("name,out_dtype,layout", CASES)
 def test_full_size_forward(name, out_dtype, layout):
     cfg = workloads.get(name)
     out_dtype = out_dtype or cfg.dtype
@@ -74,10 +83,11 @@ def test_full_size_forward(name, out_dtype, layout):
 
     toks = _sample_tokens(cfg, disp_o)
     toks = toks[~mism[toks]]
+    assert len(toks) >= min(N_SAMPLE, cfg.T) - int(mism.sum())
     y_o = oracle.layer(cfg, h["x"], idx_o, w_o, h["W1"], h["b1"], h["W2"], h["b2"],
                        h["Wsh_gu"], h["Wsh_dn"], tokens=toks)
-    err, scale = check_float(cfg, yh[toks], y_o, f"{cfg.name} y on {len(toks)} tokens",
-                             plain=True, out_bf16=out_dtype == "bf16")
-    print(f"  y max|err| {err:.3e}  RMS {scale:.3e}  ratio {err / scale:.2e}", flush=True)
+    err, scale = check_float(cfg, yh[toks], y_o, f"{cfg.name} y on {len(toks)} tokens")
+    print(f"  y max|err| {err:.3e}  RMS {scale:.3e}  ratio {err / scale:.2e} on {len(toks)} "
+          f"tokens", flush=True)
     del h
     gc.collect()
