@@ -5,8 +5,10 @@ Every token's top-k and the whole dispatch are compared bit-exactly with
 the oracle (tie rule aside); the layer output is compared on at least 512
 tokens the oracle evaluates one by one: the first and last token of every
 expert that received rows, then a seeded random fill.  The bar is
-max|err| <= 2e-2 * RMS(oracle) on the output as returned, bf16 included,
-with no allowance for its rounding.
+max|err| <= 2e-2 * RMS(oracle) with no further allowance: on the fp32
+output of every workload, and on the bf16 output as returned for the five
+stated layer shapes; every bf16 output is also checked, over all tokens, to
+be bitwise the rounding of the fp32 one.
 """
 import gc
 
@@ -16,8 +18,8 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_util import (check_float, check_dispatch_props, check_route, forward,
-                            gpu_permute, new_layer, run_route, tiled_weights, to_np)
+from tests.gpu_util import (assert_rounded_from, check_float, check_dispatch_props, check_route,
+                            forward, gpu_permute, new_layer, run_route, tiled_weights, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,34 +40,44 @@ def _sample_tokens(cfg, disp, n_total=N_SAMPLE, seed=0):
     return np.array(sorted(toks), dtype=np.int64)
 
 
+# The five layer shapes the tolerance is stated for (their bf16 output is
+# held to the plain bar as returned); the other workloads' bf16 outputs are
+# checked as the exact rounding of an fp32 result that meets the bar.
+STATED = {"tiny", "glam", "glm45", "glm5", "decode"}
 CASES = [
-    ("tiny", None, "rows"), ("decode", None, "rows"), ("decode", "f32", "rows"),
-    ("glm45", None, "rows"), ("glm45", "f32", "rows"), ("glam", None, "rows"),
-    ("glm5", None, "rows"), ("glam", None, "tiled"), ("decode", None, "tiled"),
-    ("glm45", None, "tiled"), ("glm45", "f32", "tiled"), ("glm5", None, "tiled"),
-    ("glm45g", None, "tiled"), ("switch", None, "tiled"), ("glm45dense", None, "tiled")]
+    ("tiny", "rows"), ("decode", "rows"), ("glm45", "rows"), ("glam", "rows"),
+    ("glm5", "rows"), ("glam", "tiled"), ("decode", "tiled"), ("glm45", "tiled"),
+    ("glm5", "tiled"), ("glm45g", "tiled"), ("switch", "tiled"), ("glm45dense", "tiled")]
 
 
-@pytest.mark.parametrize("name,out_dtype,layout", CASES)
-def test_full_size_forward(name, out_dtype, layout):
+@pytest.mark.parametrize("name,layout", CASES)
+def test_full_size_forward(name, layout):
     cfg = workloads.get(name)
-    out_dtype = out_dtype or cfg.dtype
-    print(f"full-size parity: {cfg.name} (y in {out_dtype}, {layout} weights)", flush=True)
+    bf = cfg.dtype == "bf16"
+    print(f"full-size parity: {cfg.name} ({layout} weights)", flush=True)
     t = workloads.generate(cfg, seed=0, device="cuda")
-    L = new_layer(cfg, out_dtype=out_dtype, weight_layout=layout)
+    L = new_layer(cfg, out_dtype="f32", weight_layout=layout)
     aux = torch.cuda.Stream()
     tw = tiled_weights(L, t) if layout == "tiled" else t
-    y = forward(L, tw, aux=aux)
+    y32 = forward(L, tw, aux=aux)
+    yb = None
+    if bf:
+        Lb = new_layer(cfg, out_dtype="bf16", weight_layout=layout)
+        yb = forward(Lb, tw, aux=aux)
+        torch.cuda.synchronize()
+        assert_rounded_from(yb, y32, f"{cfg.name} bf16 y")
+        del Lb
     del tw
     idx_g, w_g = run_route(L, L.desc, t)
     pg = gpu_permute(L, L.desc, idx_g)
     torch.cuda.synchronize()
-    yh = to_np(y.float()).reshape(cfg.T, cfg.D)
-    assert np.isfinite(yh).all()
+    y32h = to_np(y32).reshape(cfg.T, cfg.D)
+    ybh = to_np(yb.float()).reshape(cfg.T, cfg.D) if bf else None
+    assert np.isfinite(y32h).all()
     pg = {k: to_np(v) for k, v in pg.items()}
     idx_gh = to_np(idx_g).reshape(cfg.T, cfg.k)
     w_gh = to_np(w_g)
-    del y
+    del y32, yb
     h = workloads.host_inputs(t)
     del t
     gc.collect()
@@ -86,8 +98,11 @@ def test_full_size_forward(name, out_dtype, layout):
     assert len(toks) >= min(N_SAMPLE, cfg.T) - int(mism.sum())
     y_o = oracle.layer(cfg, h["x"], idx_o, w_o, h["W1"], h["b1"], h["W2"], h["b2"],
                        h["Wsh_gu"], h["Wsh_dn"], tokens=toks)
-    err, scale = check_float(cfg, yh[toks], y_o, f"{cfg.name} y on {len(toks)} tokens")
-    print(f"  y max|err| {err:.3e}  RMS {scale:.3e}  ratio {err / scale:.2e} on {len(toks)} "
-          f"tokens", flush=True)
+    err, scale = check_float(cfg, y32h[toks], y_o, f"{cfg.name} fp32 y on {len(toks)} tokens")
+    print(f"  fp32 y max|err| {err:.3e}  RMS {scale:.3e}  ratio {err / scale:.2e} on "
+          f"{len(toks)} tokens", flush=True)
+    if bf and name in STATED:
+        err, scale = check_float(cfg, ybh[toks], y_o, f"{cfg.name} bf16 y on {len(toks)} tokens")
+        print(f"  bf16 y max|err| {err:.3e}  ratio {err / scale:.2e}", flush=True)
     del h
     gc.collect()
