@@ -129,6 +129,38 @@ def rounding_bounds(cfg, h, idx, w):
     return bnd, bsh
 
 
+def _widen32(a):
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32)
+    return a.astype(np.float32)
+
+
+def rounding_bounds_tokens(cfg, h, idx, w, tokens):
+    """rounding_bounds' bound on the layer output y for the listed tokens
+    only, [len(tokens), D]: per routed slot 2^-8 |w| sum_f |H_f| |W2_if|, plus
+    the shared expert's 2^-8 sum_f |Hsh_f| |Wsh_dn_if|.  Only the experts those
+    tokens reach are widened (fp32 suffices for an allowance), so it runs at
+    full layer sizes."""
+    from scipy import special
+    X = _widen32(h["x"][tokens])
+    out = np.zeros((len(tokens), cfg.D), np.float64)
+    sub_idx, sub_w = idx[tokens], w[tokens]
+    for e in np.unique(sub_idx):
+        if e < 0 or e >= cfg.M:
+            continue
+        rr, jj = np.nonzero(sub_idx == e)
+        W1 = _widen32(h["W1"][e])
+        b1 = _widen32(h["b1"][e]) if h.get("b1") is not None else None
+        Hm = np.abs(_act(cfg, (X[rr] @ W1.T).astype(np.float64), b1))
+        W2 = np.abs(_widen32(h["W2"][e]))
+        np.add.at(out, rr, BF16_REL * np.abs(sub_w[rr, jj])[:, None] * (Hm @ W2.T.astype(np.float64)))
+    if cfg.F_shared:
+        Z = (X @ _widen32(h["Wsh_gu"]).T).astype(np.float64)
+        g, u = Z[:, :cfg.F_shared], Z[:, cfg.F_shared:]
+        out += BF16_REL * (np.abs(g * special.expit(g) * u) @ np.abs(_widen32(h["Wsh_dn"])).T)
+    return out
+
+
 def check_float(cfg, got, ref, what, bound=None, plain=True):
     """Floating-point parity.
 

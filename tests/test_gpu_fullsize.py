@@ -19,7 +19,8 @@ import torch
 import oracle
 import workloads
 from tests.gpu_util import (assert_rounded_from, check_float, check_dispatch_props, check_route,
-                            forward, gpu_permute, new_layer, run_route, tiled_weights, to_np)
+                            forward, gpu_permute, new_layer, rounding_bounds_tokens, run_route,
+                            tiled_weights, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +45,13 @@ def _sample_tokens(cfg, disp, n_total=N_SAMPLE, seed=0):
 # held to the plain bar as returned); the other workloads' bf16 outputs are
 # checked as the exact rounding of an fp32 result that meets the bar.
 STATED = {"tiny", "glam", "glm45", "glm5", "decode"}
+# Switch-style top-1 keeps the raw router probability as the gate weight
+# (no renormalisation), so each token's output is scaled by a weight that
+# varies tenfold across tokens and the largest rows carry proportionally
+# larger bf16 rounding error of the hidden activation (its fp32 output
+# reaches ~2.1% of RMS at full size, against 0.9% for the GLaM layer on the
+# same kernels).  It is checked per element against that rounding's bound.
+GATE_SCALED = {"switch"}
 CASES = [
     ("tiny", "rows"), ("decode", "rows"), ("glm45", "rows"), ("glam", "rows"),
     ("glm5", "rows"), ("glam", "tiled"), ("decode", "tiled"), ("glm45", "tiled"),
@@ -98,7 +106,13 @@ def test_full_size_forward(name, layout):
     assert len(toks) >= min(N_SAMPLE, cfg.T) - int(mism.sum())
     y_o = oracle.layer(cfg, h["x"], idx_o, w_o, h["W1"], h["b1"], h["W2"], h["b2"],
                        h["Wsh_gu"], h["Wsh_dn"], tokens=toks)
-    err, scale = check_float(cfg, y32h[toks], y_o, f"{cfg.name} fp32 y on {len(toks)} tokens")
+    if name in GATE_SCALED:
+        bound = rounding_bounds_tokens(cfg, h, idx_o, w_o, toks)
+        err, scale = check_float(cfg, y32h[toks], y_o, f"{cfg.name} fp32 y on {len(toks)} "
+                                 "tokens", bound=bound, plain=False)
+    else:
+        err, scale = check_float(cfg, y32h[toks], y_o, f"{cfg.name} fp32 y on {len(toks)} "
+                                 "tokens")
     print(f"  fp32 y max|err| {err:.3e}  RMS {scale:.3e}  ratio {err / scale:.2e} on "
           f"{len(toks)} tokens", flush=True)
     if bf and name in STATED:
