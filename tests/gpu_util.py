@@ -89,8 +89,19 @@ BF16_REL = 2.0 ** -8     # largest relative error of one bf16 rounding
 # Expert widths from which the intermediate sorted rows O and shared rows Ysh
 # are held to the plain bar (narrower ones: the bf16 rounding bound of the
 # hidden activation).  The layer output y is held to the plain bar at every
-# width.
+# width from Y_PLAIN_MIN_WIDTH.
 PLAIN_MIN_WIDTH = 512
+# Expert and shared widths from which the layer output y is held to the
+# plain bar; narrower reduced test shapes (few terms per output, so the
+# hidden activation's bf16 rounding averages out less) are checked against
+# that rounding's bound instead.
+Y_PLAIN_MIN_WIDTH = 128
+
+
+def y_plain(cfg) -> bool:
+    """Whether the layer output of cfg is held to the plain bar."""
+    return cfg.F >= Y_PLAIN_MIN_WIDTH and (cfg.F_shared == 0 or
+                                            cfg.F_shared >= Y_PLAIN_MIN_WIDTH)
 SLACK = 1e-3             # fp32 accumulation and activation error, as a fraction of RMS
 
 

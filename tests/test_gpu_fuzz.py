@@ -25,12 +25,11 @@ import oracle
 import workloads
 from tests.gpu_util import (assert_rounded_from, check_dispatch_props, check_float, check_route,
                             forward, gpu_permute, new_layer, rounding_bounds, run_route,
-                            tiled_weights, to_np)
+                            tiled_weights, to_np, y_plain)
 
 pytestmark = pytest.mark.gpu
 
 N_CASES = 48
-Y_PLAIN_MIN_WIDTH = 128   # expert and shared widths from which y meets the plain bar
 
 
 def _cases(n=N_CASES, seed=20261203):
@@ -128,7 +127,7 @@ def test_fuzz_case(case):
                        h["Wsh_gu"], h["Wsh_dn"])
     keep = ~mism
     got = to_np(y_f).reshape(cfg.T, cfg.D)[keep]
-    wide = cfg.F >= Y_PLAIN_MIN_WIDTH and (cfg.F_shared == 0 or cfg.F_shared >= Y_PLAIN_MIN_WIDTH)
+    wide = y_plain(cfg)
     bound = None
     if bf and not wide:
         bnd, bsh = rounding_bounds(cfg, h, idx_o, w_o)
