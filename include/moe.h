@@ -143,7 +143,9 @@ enum { MOE_GEMM_UP = 0, MOE_GEMM_DOWN = 1, MOE_GEMM_SHARED_UP = 2, MOE_GEMM_SHAR
 typedef struct moe_handle moe_handle;
 
 /* Create a handle bound to HIP device `device` (it becomes current during
- * calls).  Allocates only host state and two timing-free HIP events. */
+ * calls).  Allocates only host state and two timing-free HIP events, and
+ * looks up (once per device) the address of that device's fixed scratch
+ * used by moe_forward_no_alloc. */
 int moe_create(int device, moe_handle** out);
 int moe_destroy(moe_handle* h);
 
@@ -258,6 +260,25 @@ int moe_forward(moe_handle* h, const moe_desc* d, const void* x, const float* W_
                 const float* bias, const void* W1, const void* b1, const void* W2,
                 const void* b2, const void* Wsh_gu, const void* Wsh_dn, void* y,
                 void* ws, size_t ws_bytes, void* stream, void* aux_stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as moe_forward, same arguments and results (bitwise), but the
+ * workspace is a fixed scratch array compiled into the library, one per GPU,
+ * MOE_NO_ALLOC_SCRATCH_BYTES (64 MiB) each, held until the process ends.
+ * It allocates and frees nothing.  Layers whose moe_workspace_size exceeds
+ * the scratch (prefill-sized batches; at the GLM-4.5 decode shape, batches
+ * of more than about 250 tokens) return MOE_ERR_UNSUPPORTED before anything
+ * is enqueued.  Every call on one GPU uses that GPU's one scratch: calls
+ * that may overlap in time on one GPU (on different streams, or from
+ * different host threads) race and must be ordered by the caller.  The
+ * scratch keeps the last call's contents; nothing in it needs to start
+ * zeroed. */
+#define MOE_NO_ALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_no_alloc(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
+                         const float* bias, const void* W1, const void* b1, const void* W2,
+                         const void* b2, const void* Wsh_gu, const void* Wsh_dn, void* y,
+                         void* stream, void* aux_stream);
 
 /* Layer backward (training).  Gradient of moe_forward for the output
  * gradient dy[T,D] (bf16): the chain rule through each step of the forward

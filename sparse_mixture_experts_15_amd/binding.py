@@ -29,7 +29,9 @@ EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_size", "moe_route", "moe_
            "moe_expert_ffn", "moe_shared_expert", "moe_combine", "moe_forward",
            "moe_profile_start", "moe_profile_stop", "moe_profile_results",
            "moe_status_string", "moe_last_error_detail", "moe_tiled_weight_size",
-           "moe_tile_weights", "moe_backward_workspace_size", "moe_backward")
+           "moe_tile_weights", "moe_backward_workspace_size", "moe_backward",
+           "moe_forward_no_alloc")
+NO_ALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class moe_desc(ctypes.Structure):
@@ -80,6 +82,7 @@ def load_library() -> ctypes.CDLL:
         "moe_shared_expert": [vp, dp, vp, vp, vp, vp, vp, sz, vp],
         "moe_combine": [vp, dp, vp, vp, vp, vp, vp],
         "moe_forward": [vp, dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp],
+        "moe_forward_no_alloc": [vp, dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "moe_profile_start": [vp, i32, ctypes.c_char_p],
         "moe_profile_stop": [vp],
         "moe_profile_results": [vp, ctypes.POINTER(moe_kernel_time), i32,
@@ -287,6 +290,23 @@ def moe_forward(h, d, x, W_r, bias, W1, b1, W2, b2, Wsh_gu, Wsh_dn, y, ws, strea
         _ptr(Wsh_dn, "Wsh_dn", dt, _wnumel(d, "Wsh_dn", D * Fs) if Fs else None),
         _ptr(y, "y", _odt(d), T * D), _ptr(ws, "ws", torch.uint8),
         ws.numel() if ws is not None else 0, _stream(stream), aux))
+
+
+def moe_forward_no_alloc(h, d, x, W_r, bias, W1, b1, W2, b2, Wsh_gu, Wsh_dn, y, stream=None,
+                         aux_stream=None):
+    """moe_forward on the library's fixed per-GPU scratch (no workspace)."""
+    T, D, M, F, Fs = d.T, d.D, d.M, d.F, d.F_shared
+    G = 2 if d.act == 0 else 1
+    dt = _dt(d)
+    aux = None if aux_stream is None else _stream(aux_stream)
+    _check("moe_forward_no_alloc", load_library().moe_forward_no_alloc(
+        h, ctypes.byref(d), _ptr(x, "x", dt, T * D), _ptr(W_r, "W_r", torch.float32, M * D),
+        _ptr(bias, "bias", torch.float32, M), _ptr(W1, "W1", dt, _wnumel(d, "W1", M * G * F * D)),
+        _ptr(b1, "b1", dt, M * F), _ptr(W2, "W2", dt, _wnumel(d, "W2", M * D * F)),
+        _ptr(b2, "b2", dt, M * D),
+        _ptr(Wsh_gu, "Wsh_gu", dt, _wnumel(d, "Wsh_gu", 2 * Fs * D) if Fs else None),
+        _ptr(Wsh_dn, "Wsh_dn", dt, _wnumel(d, "Wsh_dn", D * Fs) if Fs else None),
+        _ptr(y, "y", _odt(d), T * D), _stream(stream), aux))
 
 
 def moe_backward_workspace_size(d: moe_desc) -> int:

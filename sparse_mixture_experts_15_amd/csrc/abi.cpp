@@ -2,6 +2,7 @@
 // fork/join and kernel launches.  Every check runs before the first
 // launch, so an error leaves the outputs and the streams untouched.
 #include <algorithm>
+#include <mutex>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -211,10 +212,40 @@ struct DeviceGuard {
     }
 };
 
+// Fixed device scratch of moe_forward_no_alloc: one copy per GPU, kept until
+// the process ends.  Host code never passes the array's name to a kernel or
+// a copy (on the host it is only a stand-in for the symbol): it uses the
+// device address hipGetSymbolAddress returns, resolved once per device in
+// moe_create with that device current.
+constexpr size_t kScratchBytes = (size_t)MOE_NO_ALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device `dev` (resolved once).
+int scratch_address(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 }  // namespace
 
 struct moe_handle {
     int device = 0;
+    void* scratch = nullptr;   // this device's fixed scratch (moe_forward_no_alloc)
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     // profiling
     bool prof_on = false;
@@ -756,6 +787,83 @@ int do_backward(moe_handle* h, const moe_desc* d, const BwdPlan& b, const void* 
         if (!(p)) return fail(MOE_ERR_INVALID, "%s is NULL", name);          \
     } while (0)
 
+// moe_forward, and moe_forward_no_alloc (fixed: the workspace is this
+// device's static scratch, for callers that cannot allocate).
+int forward_impl(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
+                 const float* bias, const void* W1, const void* b1, const void* W2,
+                 const void* b2, const void* Wsh_gu, const void* Wsh_dn, void* y, void* ws,
+                 size_t ws_bytes, void* stream, void* aux_stream, bool fixed) {
+    CHECK_HANDLE(h);
+    TRY(validate(d));
+    if (d->T == 0) return MOE_OK;
+    NEED(x, "x");
+    NEED(W_r, "W_r");
+    NEED(W1, "W1");
+    NEED(W2, "W2");
+    NEED(y, "y");
+    if (d->F_shared > 0) {
+        NEED(Wsh_gu, "Wsh_gu");
+        NEED(Wsh_dn, "Wsh_dn");
+    }
+    if (y == x) return fail(MOE_ERR_INVALID, "y aliases x");
+    const Plan p = make_plan(d);
+    if (fixed) {
+        if (p.total > kScratchBytes)
+            return fail(MOE_ERR_UNSUPPORTED,
+                        "the layer needs %zu bytes of workspace; the fixed scratch of "
+                        "moe_forward_no_alloc holds %zu (use moe_forward)", p.total,
+                        kScratchBytes);
+        ws = h->scratch;
+        ws_bytes = kScratchBytes;
+    }
+    TRY(check_ws(p, ws, ws_bytes));
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t aux = static_cast<hipStream_t>(aux_stream);
+    int32_t* idx = at<int32_t>(ws, p.idx);
+    float* w = at<float>(ws, p.w);
+    int32_t* counts = at<int32_t>(ws, p.counts);
+    int32_t* offsets = at<int32_t>(ws, p.offsets);
+    int32_t* sorted_token = at<int32_t>(ws, p.sorted_token);
+    int32_t* sorted_slot = at<int32_t>(ws, p.sorted_slot);
+    int32_t* slot_row = at<int32_t>(ws, p.slot_row);
+    float* O = at<float>(ws, p.O);
+    float* Ysh = d->F_shared > 0 ? at<float>(ws, p.Ysh) : nullptr;
+
+    if (p.merged) {
+        // the shared expert is group M of the routed GEMMs; Ysh is O's tail
+        TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
+        TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
+        TRY(do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O,
+                          ws, s, Wsh_gu, Wsh_dn));
+        return do_combine(h, d, O, slot_row, Ysh, y, s);
+    }
+    const bool fork = Ysh && aux && aux != s;
+    if (Ysh) {
+        if (fork) {
+            hipError_t e;
+            if ((e = hipEventRecord(h->ev_fork, s)) != hipSuccess ||
+                (e = hipStreamWaitEvent(aux, h->ev_fork, 0)) != hipSuccess)
+                return fail(MOE_ERR_HIP, "stream fork: %s", hipGetErrorString(e));
+            TRY(do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, aux));
+            if ((e = hipEventRecord(h->ev_join, aux)) != hipSuccess)
+                return fail(MOE_ERR_HIP, "stream join: %s", hipGetErrorString(e));
+        } else {
+            TRY(do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, s));
+        }
+    }
+    TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
+    TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
+    TRY(do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O, ws, s));
+    if (fork) {
+        const hipError_t e = hipStreamWaitEvent(s, h->ev_join, 0);
+        if (e != hipSuccess) return fail(MOE_ERR_HIP, "stream join: %s", hipGetErrorString(e));
+    }
+    return do_combine(h, d, O, slot_row, Ysh, y, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -783,8 +891,11 @@ int moe_create(int device, moe_handle** out) {
         return fail(MOE_ERR_INVALID, "device %d not in [0, %d)", device, n);
     DeviceGuard g(device);
     if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+    void* scr = nullptr;
+    TRY(scratch_address(device, &scr));
     moe_handle* h = new moe_handle();
     h->device = device;
+    h->scratch = scr;
     if ((e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming)) != hipSuccess) {
         if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
@@ -946,66 +1057,16 @@ int moe_forward(moe_handle* h, const moe_desc* d, const void* x, const float* W_
                 const float* bias, const void* W1, const void* b1, const void* W2, const void* b2,
                 const void* Wsh_gu, const void* Wsh_dn, void* y, void* ws, size_t ws_bytes,
                 void* stream, void* aux_stream) {
-    CHECK_HANDLE(h);
-    TRY(validate(d));
-    if (d->T == 0) return MOE_OK;
-    NEED(x, "x");
-    NEED(W_r, "W_r");
-    NEED(W1, "W1");
-    NEED(W2, "W2");
-    NEED(y, "y");
-    if (d->F_shared > 0) {
-        NEED(Wsh_gu, "Wsh_gu");
-        NEED(Wsh_dn, "Wsh_dn");
-    }
-    if (y == x) return fail(MOE_ERR_INVALID, "y aliases x");
-    const Plan p = make_plan(d);
-    TRY(check_ws(p, ws, ws_bytes));
-    DeviceGuard g(h->device);
-    if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+    return forward_impl(h, d, x, W_r, bias, W1, b1, W2, b2, Wsh_gu, Wsh_dn, y, ws, ws_bytes,
+                        stream, aux_stream, false);
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipStream_t aux = static_cast<hipStream_t>(aux_stream);
-    int32_t* idx = at<int32_t>(ws, p.idx);
-    float* w = at<float>(ws, p.w);
-    int32_t* counts = at<int32_t>(ws, p.counts);
-    int32_t* offsets = at<int32_t>(ws, p.offsets);
-    int32_t* sorted_token = at<int32_t>(ws, p.sorted_token);
-    int32_t* sorted_slot = at<int32_t>(ws, p.sorted_slot);
-    int32_t* slot_row = at<int32_t>(ws, p.slot_row);
-    float* O = at<float>(ws, p.O);
-    float* Ysh = d->F_shared > 0 ? at<float>(ws, p.Ysh) : nullptr;
-
-    if (p.merged) {
-        // the shared expert is group M of the routed GEMMs; Ysh is O's tail
-        TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
-        TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
-        TRY(do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O,
-                          ws, s, Wsh_gu, Wsh_dn));
-        return do_combine(h, d, O, slot_row, Ysh, y, s);
-    }
-    const bool fork = Ysh && aux && aux != s;
-    if (Ysh) {
-        if (fork) {
-            hipError_t e;
-            if ((e = hipEventRecord(h->ev_fork, s)) != hipSuccess ||
-                (e = hipStreamWaitEvent(aux, h->ev_fork, 0)) != hipSuccess)
-                return fail(MOE_ERR_HIP, "stream fork: %s", hipGetErrorString(e));
-            TRY(do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, aux));
-            if ((e = hipEventRecord(h->ev_join, aux)) != hipSuccess)
-                return fail(MOE_ERR_HIP, "stream join: %s", hipGetErrorString(e));
-        } else {
-            TRY(do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, s));
-        }
-    }
-    TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
-    TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
-    TRY(do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O, ws, s));
-    if (fork) {
-        const hipError_t e = hipStreamWaitEvent(s, h->ev_join, 0);
-        if (e != hipSuccess) return fail(MOE_ERR_HIP, "stream join: %s", hipGetErrorString(e));
-    }
-    return do_combine(h, d, O, slot_row, Ysh, y, s);
+int moe_forward_no_alloc(moe_handle* h, const moe_desc* d, const void* x, const float* W_r,
+                         const float* bias, const void* W1, const void* b1, const void* W2,
+                         const void* b2, const void* Wsh_gu, const void* Wsh_dn, void* y,
+                         void* stream, void* aux_stream) {
+    return forward_impl(h, d, x, W_r, bias, W1, b1, W2, b2, Wsh_gu, Wsh_dn, y, nullptr, 0,
+                        stream, aux_stream, true);
 }
 
 int moe_backward_workspace_size(const moe_desc* d, size_t* bytes) {
