@@ -315,6 +315,9 @@ def main():
     ap.add_argument("--weights", choices=["tiled", "rows"], default=None,
                     help="expert/shared weight layout (tiled: copied once before timing); "
                          "default tiled for bf16 layers, rows for fp32 (the tiled copy is bf16 only)")
+    ap.add_argument("--schedule", default="auto",
+                    choices=["auto", "in_step", "pingpong64", "pingpong32"],
+                    help="main loop of the 256-row GEMM tiles (descriptor tuning)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
     ap.add_argument("--backward", action="store_true",
@@ -346,7 +349,7 @@ def main():
     t = workloads.generate(cfg, seed=args.seed, device="cuda")
     if args.weights is None:
         args.weights = default_weight_layout(cfg)
-    L = MoELayer(B.make_desc(cfg, weight_layout=args.weights))
+    L = MoELayer(B.make_desc(cfg, weight_layout=args.weights, schedule=args.schedule))
     d = L.desc
     tg = dict(t)   # what the GPU reads; t keeps the row-major weights for the oracle
     if args.weights == "tiled":
@@ -437,7 +440,8 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "D": cfg.D, "M": cfg.M, "F": cfg.F,
                    "k": cfg.k, "F_shared": cfg.F_shared, "scorer": cfg.scorer, "act": cfg.act,
                    "alpha": cfg.alpha, "seed": args.seed, "touched_experts": U,
-                   "aux_stream": aux is not None, "weights": args.weights},
+                   "aux_stream": aux is not None, "weights": args.weights,
+                   "schedule": args.schedule},
         "active_tflops": round(active_tflops, 2),
         "alg_hbm_gbps": round(alg_gbps, 1),
         "layer_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),
