@@ -318,6 +318,12 @@ def main():
     ap.add_argument("--schedule", default="auto",
                     choices=["auto", "in_step", "pingpong64", "pingpong32"],
                     help="main loop of the 256-row GEMM tiles (descriptor tuning)")
+    ap.add_argument("--tile-order", default=None,
+                    help="workgroup order per GEMM (descriptor tuning): one name for all four, "
+                         "or up,down,shared_up,shared_down; names auto, xcd_groups, hardware, "
+                         "xcd_slices")
+    ap.add_argument("--group-m", type=int, default=0,
+                    help="m-tiles per group of the tile order (descriptor tuning; 0 = choose)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
     ap.add_argument("--backward", action="store_true",
@@ -349,7 +355,12 @@ def main():
     t = workloads.generate(cfg, seed=args.seed, device="cuda")
     if args.weights is None:
         args.weights = default_weight_layout(cfg)
-    L = MoELayer(B.make_desc(cfg, weight_layout=args.weights, schedule=args.schedule))
+    order = None
+    if args.tile_order:
+        parts = args.tile_order.split(",")
+        order = parts * 4 if len(parts) == 1 else parts
+    L = MoELayer(B.make_desc(cfg, weight_layout=args.weights, schedule=args.schedule,
+                             tile_order=order, group_m=args.group_m))
     d = L.desc
     tg = dict(t)   # what the GPU reads; t keeps the row-major weights for the oracle
     if args.weights == "tiled":
@@ -441,7 +452,8 @@ def main():
                    "k": cfg.k, "F_shared": cfg.F_shared, "scorer": cfg.scorer, "act": cfg.act,
                    "alpha": cfg.alpha, "seed": args.seed, "touched_experts": U,
                    "aux_stream": aux is not None, "weights": args.weights,
-                   "schedule": args.schedule},
+                   "schedule": args.schedule, "tile_order": args.tile_order or "auto",
+                   "group_m": args.group_m},
         "active_tflops": round(active_tflops, 2),
         "alg_hbm_gbps": round(alg_gbps, 1),
         "layer_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),
