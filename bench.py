@@ -316,7 +316,7 @@ def main():
                     help="expert/shared weight layout (tiled: copied once before timing); "
                          "default tiled for bf16 layers, rows for fp32 (the tiled copy is bf16 only)")
     ap.add_argument("--schedule", default="auto",
-                    choices=["auto", "in_step", "pingpong64", "pingpong32"],
+                    choices=["auto", "in_step", "pingpong64", "pingpong32", "interleaved"],
                     help="main loop of the 256-row GEMM tiles (descriptor tuning)")
     ap.add_argument("--tile-order", default=None,
                     help="workgroup order per GEMM (descriptor tuning): one name for all four, "

@@ -122,7 +122,8 @@ enum { MOE_WEIGHT_W1 = 0, MOE_WEIGHT_W2 = 1, MOE_WEIGHT_SH_GU = 2, MOE_WEIGHT_SH
  *                 1 every wave loads, reads and multiplies each K stage in
  *                 step, 2 ping-pong over 64-K units (the two waves sharing a
  *                 SIMD alternate between multiplying and reading), 3
- *                 ping-pong over 32-K units                              */
+ *                 ping-pong over 32-K units, 4 in step with each wave's
+ *                 loads of the next stage issued among its MFMAs         */
 typedef struct moe_desc {
     int64_t T, D, M, F, F_shared;
     int32_t k;

@@ -120,7 +120,7 @@ def _check(fn: str, rc: int):
 GEMMS = ("up", "down", "shared_up", "shared_down")   # order of tile_rows / tile_order
 ORDER = {"auto": 0, "xcd_groups": 1, "hardware": 2, "xcd_slices": 3}
 SHARED_MODE = {"auto": 0, "separate": 1, "merged": 2}
-SCHEDULE = {"auto": 0, "in_step": 1, "pingpong64": 2, "pingpong32": 3}
+SCHEDULE = {"auto": 0, "in_step": 1, "pingpong64": 2, "pingpong32": 3, "interleaved": 4}
 
 
 def make_desc(cfg=None, **kw) -> moe_desc:

@@ -149,8 +149,8 @@ int validate(const moe_desc* d) {
         return fail(MOE_ERR_INVALID, "group_m=%d is not in [0, 16]", d->group_m);
     if (d->shared_mode < 0 || d->shared_mode > 2)
         return fail(MOE_ERR_INVALID, "shared_mode=%d is not in [0, 2]", d->shared_mode);
-    if (d->schedule < 0 || d->schedule > 3)
-        return fail(MOE_ERR_INVALID, "schedule=%d is not in [0, 3]", d->schedule);
+    if (d->schedule < 0 || d->schedule > 4)
+        return fail(MOE_ERR_INVALID, "schedule=%d is not in [0, 4]", d->schedule);
     if (d->weight_layout != MOE_LAYOUT_ROWS && d->weight_layout != MOE_LAYOUT_TILED)
         return fail(MOE_ERR_INVALID, "unknown weight_layout %d", d->weight_layout);
     if (d->weight_layout == MOE_LAYOUT_TILED && d->dtype != MOE_DTYPE_BF16)
@@ -306,6 +306,7 @@ int gemm_schedule(const moe_desc* d) {
         case 1: return 0;
         case 2: return 1;
         case 3: return 2;
+        case 4: return 3;
         default: return 0;
     }
 }

@@ -428,9 +428,12 @@ __device__ __forceinline__ bf16x8 kn_fragment(const bf16_t* bt, int kbase, int n
 // hold rows: eight waves, each 128 A rows (wave row wm) x 64 B rows (wave
 // column wn), accumulators acc[8][4]; the A rows sit at the stage's start,
 // the 256 B rows after them (row-major, or [K, N] when BKN).
-template <int BNB, int BKN>
+// ld(q), q < 8: issues the wave's q-th global->LDS load of a later stage
+// among the first 32 MFMAs (a no-op when the caller issued them already),
+// so no wave waits at the memory pipeline's queue before its MFMAs start.
+template <int BNB, int BKN, class LD>
 __device__ __forceinline__ void mfma_stage_full256(const bf16_t* st, floatx4 (&acc)[8][4], int wm,
-                                                   int wn, int lane) {
+                                                   int wn, int lane, LD&& ld) {
     constexpr int BM = 256, BK = 64, TN = 4, WROWS = 128;
     const int fr = lane & 15, fc = lane >> 4;
     // 256-row tiles, whole fragments: each K half's rows 0-3 then
@@ -470,20 +473,26 @@ __device__ __forceinline__ void mfma_stage_full256(const bf16_t* st, floatx4 (&a
     rdA(0, 0, a00);
     __builtin_amdgcn_sched_group_barrier(0x100, TN * RB + 4, 0);
     rdA(0, 4, a01);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ld(q);
     mm(0, a00, b0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     rdB(1, b1);
     rdA(1, 0, a10);
+#pragma unroll
+    for (int q = 4; q < 8; ++q) ld(q);
     mm(4, a01, b0);
     if constexpr (BKN) {   // 12 reads among 16 MFMAs
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -495,6 +504,7 @@ __device__ __forceinline__ void mfma_stage_full256(const bf16_t* st, floatx4 (&a
         for (int q = 0; q < 8; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (q & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
     }
     rdA(1, 4, a11);
@@ -605,11 +615,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             rowoff[q] = oc < N ? (uint32_t)br * (uint32_t)K * 2u : kOOB;
         }
     }
-    auto issue = [&](int kt) {
+    // load q of this wave for stage kt (all offsets out of bounds when
+    // !live: the load then reads zeros and touches no memory)
+    auto issue_q = [&](int kt, int q, bool live = true) {
         bf16_t* st = sm + (kt % STAGES) * STAGE;
         const int kc = kt * BK + lchunk * 8;
-#pragma unroll
-        for (int q = 0; q < LPW; ++q) {
+        {
             const int ins = wave + 8 * q;
             // an invalid row stays >= kOOB (offsets are < 2^31); a K-tail chunk -> kOOB
             uint32_t off = rowoff[q] + (uint32_t)kc * 2u;
@@ -621,6 +632,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             }
             if (q < QB && g.b_tiled)
                 off = tile_base + (uint32_t)kt * TILE_STAGE + (uint32_t)ins * 1024u + lane * 16u;
+            off = live ? off : kOOB;
             if (q < QB)
                 llvm_amdgcn_raw_buffer_load_lds(rb, (lds_u32_ptr)(st + BM * BK + ins * 512), 16,
                                                 (int)off, 0, 0, 0);
@@ -628,6 +640,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
                 llvm_amdgcn_raw_buffer_load_lds(ra, (lds_u32_ptr)(st + (ins - B_LOADS) * 512), 16,
                                                 (int)off, 0, 0, 0);
         }
+    };
+    auto issue = [&](int kt) {
+#pragma unroll
+        for (int q = 0; q < LPW; ++q) issue_q(kt, q);
     };
 
     floatx4 acc[TM][TN];
@@ -666,7 +682,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     };
     // the multiply of one stage for 256-row tiles whose fragments all hold rows
     auto body_full256 = [&](const bf16_t* st) {
-        if constexpr (TM == 8 && BK == 64) mfma_stage_full256<BNB, BKN>(st, acc, wm, wn, lane);
+        if constexpr (TM == 8 && BK == 64)
+            mfma_stage_full256<BNB, BKN>(st, acc, wm, wn, lane, [](int) {});
+    };
+    // the same with the next stage's loads issued among the first MFMAs
+    auto kloop_interleaved = [&]() {
+        if constexpr (TM == 8 && BK == 64 && LPW == 8 && STAGES == 2) {
+            for (int kt = 0; kt < nk; ++kt) {
+                wait_vmcnt<0>();                  // stage kt landed
+                __builtin_amdgcn_s_barrier();     // every wave's loads landed; stage kt-1 fully read
+                // past the last stage the loads read zeros into the slot of
+                // stage kt - 1, which no wave reads again (no branch, so the
+                // loads interleave with the MFMAs)
+                const bool more = kt + 1 < nk;
+                const int next = k_first + kt + 1;
+                const bf16_t* st = sm + ((k_first + kt) % STAGES) * STAGE;
+                mfma_stage_full256<BNB, BKN>(st, acc, wm, wn, lane,
+                                             [&](int q) { issue_q(next, q, more); });
+            }
+        }
     };
     // the multiply of one stage in general (fragments past the group's
     // last row skip their reads and MFMAs)
@@ -737,7 +771,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     // wlive is fixed for the whole loop, so the two bodies get loops of
     // their own (in one loop their registers add up and spill)
     if constexpr (TM == 8 && BK == 64) {
-        if (wlive == TM) kloop(body_full256);
+        if (wlive == TM && g.schedule == 3 && LPW == 8 && STAGES == 2) kloop_interleaved();
+        else if (wlive == TM) kloop(body_full256);
         else kloop(body_general);
     } else {
         kloop(body_general);
@@ -1039,7 +1074,8 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16(GemmArgs g, int m_tiles, int
         if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
         const bf16_t* st = sm + (kt % STAGES) * STAGE;
         if constexpr (BM == 256 && BNB == 256 && BK == 64) {
-            mfma_stage_full256<BNB, 0>(st, acc, wm, wn, lane);   // rows past the end read zeros
+            mfma_stage_full256<BNB, 0>(st, acc, wm, wn, lane,
+                                       [](int) {});   // rows past the end read zeros
         } else {
 #pragma unroll
             for (int kk = 0; kk < BK / 32; ++kk) {
@@ -1229,7 +1265,7 @@ hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64
                                  EPI == EPI_DOWN_F32 || EPI == EPI_SWIGLU_SAVE ||
                                  EPI == EPI_GELU_SAVE;
             if constexpr (fwd) {
-                if (g.schedule != 0 && g.k_split <= 1 && !g.koff) {
+                if ((g.schedule == 1 || g.schedule == 2) && g.k_split <= 1 && !g.koff) {
                     if (g.schedule == 2) return launch_pp<EPI, 32>(s, g, m_tiles);
                     return launch_pp<EPI, 64>(s, g, m_tiles);
                 }

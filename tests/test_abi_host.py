@@ -81,7 +81,7 @@ def test_workspace_size_covers_intermediates():
     ("F_shared", 4, B.MOE_ERR_UNSUPPORTED), ("weight_layout", 2, B.MOE_ERR_INVALID),
     ("tile_rows", 96, B.MOE_ERR_INVALID), ("tile_rows", -64, B.MOE_ERR_INVALID),
     ("tile_order", 4, B.MOE_ERR_INVALID), ("group_m", 17, B.MOE_ERR_INVALID),
-    ("shared_mode", 3, B.MOE_ERR_INVALID), ("schedule", 4, B.MOE_ERR_INVALID),
+    ("shared_mode", 3, B.MOE_ERR_INVALID), ("schedule", 5, B.MOE_ERR_INVALID),
 ])
 def test_bad_descriptor_rejected(field, value, status):
     cfg = workloads.shrink(workloads.GLAM_4K, T=16, D=64, F=32).replace(M=8)

@@ -286,7 +286,7 @@ def test_small_workspace_rejected_before_launch():
 # The ping-pong main loops of the 256-row tiles: every stage against the
 # oracle, and the layer bitwise equal to the in-step loop (each output
 # element's MFMA sequence over K is the same).
-@pytest.mark.parametrize("sched", ["pingpong64", "pingpong32"])
+@pytest.mark.parametrize("sched", ["pingpong64", "pingpong32", "interleaved"])
 @pytest.mark.parametrize("name,tiled", [("glm45_mid", False), ("glm5_rows", False),
                                         ("glam_mid", False), ("glm45_small", False),
                                         ("glam_tiles", False), ("glm45_small", True),
