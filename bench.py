@@ -315,9 +315,6 @@ def main():
     ap.add_argument("--weights", choices=["tiled", "rows"], default=None,
                     help="expert/shared weight layout (tiled: copied once before timing); "
                          "default tiled for bf16 layers, rows for fp32 (the tiled copy is bf16 only)")
-    ap.add_argument("--schedule", default="auto",
-                    choices=["auto", "in_step", "pingpong64", "pingpong32", "interleaved"],
-                    help="main loop of the 256-row GEMM tiles (descriptor tuning)")
     ap.add_argument("--tile-order", default=None,
                     help="workgroup order per GEMM (descriptor tuning): one name for all four, "
                          "or up,down,shared_up,shared_down; names auto, xcd_groups, hardware, "
@@ -359,8 +356,8 @@ def main():
     if args.tile_order:
         parts = args.tile_order.split(",")
         order = parts * 4 if len(parts) == 1 else parts
-    L = MoELayer(B.make_desc(cfg, weight_layout=args.weights, schedule=args.schedule,
-                             tile_order=order, group_m=args.group_m))
+    L = MoELayer(B.make_desc(cfg, weight_layout=args.weights, tile_order=order,
+                             group_m=args.group_m))
     d = L.desc
     tg = dict(t)   # what the GPU reads; t keeps the row-major weights for the oracle
     if args.weights == "tiled":
@@ -452,7 +449,7 @@ def main():
                    "k": cfg.k, "F_shared": cfg.F_shared, "scorer": cfg.scorer, "act": cfg.act,
                    "alpha": cfg.alpha, "seed": args.seed, "touched_experts": U,
                    "aux_stream": aux is not None, "weights": args.weights,
-                   "schedule": args.schedule, "tile_order": args.tile_order or "auto",
+                   "tile_order": args.tile_order or "auto",
                    "group_m": args.group_m},
         "active_tflops": round(active_tflops, 2),
         "alg_hbm_gbps": round(alg_gbps, 1),

@@ -117,13 +117,7 @@ enum { MOE_WEIGHT_W1 = 0, MOE_WEIGHT_W2 = 1, MOE_WEIGHT_SH_GU = 2, MOE_WEIGHT_SH
  *   shared_mode   0 (choose), 1 the shared expert in launches of its own
  *                 (on aux_stream when given), 2 the shared expert as one
  *                 more group of the routed GEMM launches (needs F_shared ==
- *                 F, SwiGLU, bf16 and T <= 1024; otherwise as 1)
- *   schedule      main loop of the 256-row bf16 GEMM tiles: 0 (choose),
- *                 1 every wave loads, reads and multiplies each K stage in
- *                 step, 2 ping-pong over 64-K units (the two waves sharing a
- *                 SIMD alternate between multiplying and reading), 3
- *                 ping-pong over 32-K units, 4 in step with each wave's
- *                 loads of the next stage issued among its MFMAs         */
+ *                 F, SwiGLU, bf16 and T <= 1024; otherwise as 1)        */
 typedef struct moe_desc {
     int64_t T, D, M, F, F_shared;
     int32_t k;
@@ -141,7 +135,6 @@ typedef struct moe_desc {
     int32_t tile_order[4];
     int32_t group_m;
     int32_t shared_mode;
-    int32_t schedule;
 } moe_desc;
 
 /* Indices of moe_desc.tile_rows / tile_order. */

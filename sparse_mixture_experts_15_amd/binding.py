@@ -43,7 +43,7 @@ class moe_desc(ctypes.Structure):
                 ("weight_layout", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("tile_rows", ctypes.c_int32 * 4),
                 ("tile_order", ctypes.c_int32 * 4), ("group_m", ctypes.c_int32),
-                ("shared_mode", ctypes.c_int32), ("schedule", ctypes.c_int32)]
+                ("shared_mode", ctypes.c_int32)]
 
 
 class moe_kernel_time(ctypes.Structure):
@@ -120,7 +120,6 @@ def _check(fn: str, rc: int):
 GEMMS = ("up", "down", "shared_up", "shared_down")   # order of tile_rows / tile_order
 ORDER = {"auto": 0, "xcd_groups": 1, "hardware": 2, "xcd_slices": 3}
 SHARED_MODE = {"auto": 0, "separate": 1, "merged": 2}
-SCHEDULE = {"auto": 0, "in_step": 1, "pingpong64": 2, "pingpong32": 3, "interleaved": 4}
 
 
 def make_desc(cfg=None, **kw) -> moe_desc:
@@ -130,7 +129,7 @@ def make_desc(cfg=None, **kw) -> moe_desc:
     out_dtype defaults to dtype, weight_layout to "rows".  Launch tuning
     (default: the library's choice): tile_rows and tile_order as dicts keyed
     by GEMMS names or 4-sequences, group_m, shared_mode ("separate",
-    "merged"), schedule ("in_step", "pingpong64", "pingpong32")."""
+    "merged")."""
     f = {}
     if cfg is not None:
         for n in ("T", "D", "M", "F", "F_shared", "k", "scorer", "act", "dtype", "renorm",
@@ -162,8 +161,7 @@ def make_desc(cfg=None, **kw) -> moe_desc:
                     tile_rows=four(f.get("tile_rows")),
                     tile_order=four(f.get("tile_order"), ORDER),
                     group_m=int(f.get("group_m", 0)),
-                    shared_mode=int(SHARED_MODE.get(sm, sm)),
-                    schedule=int(SCHEDULE.get(f.get("schedule", 0), f.get("schedule", 0))))
+                    shared_mode=int(SHARED_MODE.get(sm, sm)))
 
 
 def _ptr(t, name, dtype=None, numel=None):

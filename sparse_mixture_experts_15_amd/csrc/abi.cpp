@@ -149,8 +149,6 @@ int validate(const moe_desc* d) {
         return fail(MOE_ERR_INVALID, "group_m=%d is not in [0, 16]", d->group_m);
     if (d->shared_mode < 0 || d->shared_mode > 2)
         return fail(MOE_ERR_INVALID, "shared_mode=%d is not in [0, 2]", d->shared_mode);
-    if (d->schedule < 0 || d->schedule > 4)
-        return fail(MOE_ERR_INVALID, "schedule=%d is not in [0, 4]", d->schedule);
     if (d->weight_layout != MOE_LAYOUT_ROWS && d->weight_layout != MOE_LAYOUT_TILED)
         return fail(MOE_ERR_INVALID, "unknown weight_layout %d", d->weight_layout);
     if (d->weight_layout == MOE_LAYOUT_TILED && d->dtype != MOE_DTYPE_BF16)
@@ -300,17 +298,6 @@ T* at(void* ws, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-// GemmArgs::schedule of the 256-row tiles for the descriptor's choice.
-int gemm_schedule(const moe_desc* d) {
-    switch (d->schedule) {
-        case 1: return 0;
-        case 2: return 1;
-        case 3: return 2;
-        case 4: return 3;
-        default: return 0;
-    }
-}
-
 // Stage bodies (no validation).
 int do_route(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, const float* W_r,
              const float* bias, int32_t* idx, float* w, void* ws, hipStream_t s) {
@@ -382,7 +369,6 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
         up.extra_group = (int)d->M;
     }
     up.xcd_mode = gemm_xcd_mode(true, false, d->M == 1 && !merged, d->tile_order[MOE_GEMM_UP]);
-    up.schedule = gemm_schedule(d);
     up.offsets = offsets;
     up.a_rows = d->T;
     up.b_rows = (int)((swiglu ? 2 : 1) * d->F);
@@ -409,7 +395,6 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
         dn.extra_group = (int)d->M;
     }
     dn.xcd_mode = gemm_xcd_mode(true, true, false, d->tile_order[MOE_GEMM_DOWN]);
-    dn.schedule = gemm_schedule(d);
     dn.offsets = offsets;
     dn.a_rows = rows;
     dn.b_rows = (int)d->D;
@@ -438,7 +423,6 @@ int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, co
     up.N = (int)d->F_shared;
     up.F_split = (int)d->F_shared;
     up.xcd_mode = gemm_xcd_mode(false, false, false, d->tile_order[MOE_GEMM_SHARED_UP]);
-    up.schedule = gemm_schedule(d);
     TRY(run(h, s, L_SHARED_UP,
             [&] { return launch_gemm(s, d->dtype, p.bm_sh_up, EPI_SWIGLU, up, mt_up); }));
     GemmArgs dn{};
@@ -453,7 +437,6 @@ int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, co
     dn.K = (int)d->F_shared;
     dn.N = (int)d->D;
     dn.xcd_mode = gemm_xcd_mode(false, true, false, d->tile_order[MOE_GEMM_SHARED_DOWN]);
-    dn.schedule = gemm_schedule(d);
     return run(h, s, L_SHARED_DOWN,
                [&] { return launch_gemm(s, d->dtype, p.bm_sh_dn, EPI_DOWN_F32, dn, mt_dn); });
 }

@@ -137,9 +137,6 @@ struct GemmArgs {
     int b_kn;                 // b[e] is [K, N] row-major (b_stride = K * N); bf16, K = 64 stages
     int xcd_mode;             // workgroup order: 0 groups dealt to XCDs in turn, 1 plain,
                               // 2 contiguous slices per XCD
-    int schedule;             // 256 x 256 tiles: 0 every wave in step (gemm_bf16),
-                              // 1 ping-pong on 64-K units, 2 ping-pong on 32-K units,
-                              // 3 in step with the loads interleaved among the MFMAs
     const void* b_extra;      // grouped: weights of group extra_group, in place of
     int extra_group;          // b + extra_group * b_stride (NULL: none)
     // backward epilogues

@@ -428,12 +428,9 @@ __device__ __forceinline__ bf16x8 kn_fragment(const bf16_t* bt, int kbase, int n
 // hold rows: eight waves, each 128 A rows (wave row wm) x 64 B rows (wave
 // column wn), accumulators acc[8][4]; the A rows sit at the stage's start,
 // the 256 B rows after them (row-major, or [K, N] when BKN).
-// ld(q), q < 8: issues the wave's q-th global->LDS load of a later stage
-// among the first 32 MFMAs (a no-op when the caller issued them already),
-// so no wave waits at the memory pipeline's queue before its MFMAs start.
-template <int BNB, int BKN, class LD>
+template <int BNB, int BKN>
 __device__ __forceinline__ void mfma_stage_full256(const bf16_t* st, floatx4 (&acc)[8][4], int wm,
-                                                   int wn, int lane, LD&& ld) {
+                                                   int wn, int lane) {
     constexpr int BM = 256, BK = 64, TN = 4, WROWS = 128;
     const int fr = lane & 15, fc = lane >> 4;
     // 256-row tiles, whole fragments: each K half's rows 0-3 then
@@ -473,26 +470,20 @@ __device__ __forceinline__ void mfma_stage_full256(const bf16_t* st, floatx4 (&a
     rdA(0, 0, a00);
     __builtin_amdgcn_sched_group_barrier(0x100, TN * RB + 4, 0);
     rdA(0, 4, a01);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) ld(q);
     mm(0, a00, b0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     rdB(1, b1);
     rdA(1, 0, a10);
-#pragma unroll
-    for (int q = 4; q < 8; ++q) ld(q);
     mm(4, a01, b0);
     if constexpr (BKN) {   // 12 reads among 16 MFMAs
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -504,7 +495,6 @@ __device__ __forceinline__ void mfma_stage_full256(const bf16_t* st, floatx4 (&a
         for (int q = 0; q < 8; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (q & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
     }
     rdA(1, 4, a11);
@@ -615,9 +605,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             rowoff[q] = oc < N ? (uint32_t)br * (uint32_t)K * 2u : kOOB;
         }
     }
-    // load q of this wave for stage kt (all offsets out of bounds when
-    // !live: the load then reads zeros and touches no memory)
-    auto issue_q = [&](int kt, int q, bool live = true) {
+    // load q of this wave for stage kt
+    auto issue_q = [&](int kt, int q) {
         bf16_t* st = sm + (kt % STAGES) * STAGE;
         const int kc = kt * BK + lchunk * 8;
         {
@@ -632,7 +621,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             }
             if (q < QB && g.b_tiled)
                 off = tile_base + (uint32_t)kt * TILE_STAGE + (uint32_t)ins * 1024u + lane * 16u;
-            off = live ? off : kOOB;
             if (q < QB)
                 llvm_amdgcn_raw_buffer_load_lds(rb, (lds_u32_ptr)(st + BM * BK + ins * 512), 16,
                                                 (int)off, 0, 0, 0);
@@ -683,24 +671,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     // the multiply of one stage for 256-row tiles whose fragments all hold rows
     auto body_full256 = [&](const bf16_t* st) {
         if constexpr (TM == 8 && BK == 64)
-            mfma_stage_full256<BNB, BKN>(st, acc, wm, wn, lane, [](int) {});
-    };
-    // the same with the next stage's loads issued among the first MFMAs
-    auto kloop_interleaved = [&]() {
-        if constexpr (TM == 8 && BK == 64 && LPW == 8 && STAGES == 2) {
-            for (int kt = 0; kt < nk; ++kt) {
-                wait_vmcnt<0>();                  // stage kt landed
-                __builtin_amdgcn_s_barrier();     // every wave's loads landed; stage kt-1 fully read
-                // past the last stage the loads read zeros into the slot of
-                // stage kt - 1, which no wave reads again (no branch, so the
-                // loads interleave with the MFMAs)
-                const bool more = kt + 1 < nk;
-                const int next = k_first + kt + 1;
-                const bf16_t* st = sm + ((k_first + kt) % STAGES) * STAGE;
-                mfma_stage_full256<BNB, BKN>(st, acc, wm, wn, lane,
-                                             [&](int q) { issue_q(next, q, more); });
-            }
-        }
+            mfma_stage_full256<BNB, BKN>(st, acc, wm, wn, lane);
     };
     // the multiply of one stage in general (fragments past the group's
     // last row skip their reads and MFMAs)
@@ -771,8 +742,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     // wlive is fixed for the whole loop, so the two bodies get loops of
     // their own (in one loop their registers add up and spill)
     if constexpr (TM == 8 && BK == 64) {
-        if (wlive == TM && g.schedule == 3 && LPW == 8 && STAGES == 2) kloop_interleaved();
-        else if (wlive == TM) kloop(body_full256);
+        if (wlive == TM) kloop(body_full256);
         else kloop(body_general);
     } else {
         kloop(body_general);
@@ -784,196 +754,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     } else {
         out_epilogue<EPI, TM, TN, WROWS>(g, tl, acc, wlive, wm, wn, n_base, kg, kc_id, lane);
     }
-}
-
-// ------------------------------------------------------------ ping-pong
-
-// Compiler-level barrier around the workgroup barriers of the ping-pong loop:
-// no memory access moves across it (the s_barrier intrinsic alone does not
-// order memory for the optimiser).
-__device__ __forceinline__ void pp_sync() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// Ping-pong main loop for 256 x 256 tiles over two LDS stages of K = 64.
-// The workgroup's eight waves form two groups: G0 = waves 0-3 (tile rows
-// 0-127), G1 = waves 4-7 (rows 128-255); wave w and wave w + 4 share SIMD w.
-// Each group alternates between a multiply phase (the MFMAs of one unit of
-// PK = 32 or 64 K-steps, operands already in registers) and a memory phase
-// (reading its fragments of the next unit from LDS), half a unit out of step
-// with the other group, so each SIMD's matrix core is kept busy by one wave
-// while the other waits on memory.  Phases end at a workgroup barrier:
-//   phase 2u:     G0 multiplies unit u;   G1 reads unit u
-//   phase 2u + 1: G1 multiplies unit u;   G0 reads unit u + 1, and after the
-//                 last unit of stage k issues the global->LDS loads of
-//                 stage k + 2 into the slot stage k held (read by both)
-// G0 issues every load (16 per wave per stage) and waits for a stage's
-// loads at the end of its multiply phase of the previous stage's last unit,
-// 2 x 64 K-steps of MFMA time after issuing them.  The last phase runs G0's
-// epilogue beside G1's last multiply.  Each output element's MFMA sequence
-// over K is the one gemm_bf16 runs, so results are bitwise the same.
-template <int EPI, int PK>
-__global__ __launch_bounds__(NT, 1) void gemm_bf16_pp(GemmArgs g, int m_tiles, int n_tiles) {
-    constexpr int BM = 256, BNB = 256, BK = 64, TM = 8, TN = 4, WROWS = 128;
-    constexpr int KH = PK / 32;                 // 32-K fragment halves per unit
-    constexpr int UPS = BK / PK;                // units per stage
-    constexpr int STAGE = (BM + BNB) * BK;      // bf16 elements per stage (64 KB)
-    constexpr int RPL = 1024 / (BK * 2);        // rows per 1 KB wave load (8)
-    constexpr int B_LOADS = BNB / RPL;          // 32 B blocks, then 32 A blocks
-    static_assert(PK == 32 || PK == 64, "unit of 32 or 64 K-steps");
-    __shared__ __attribute__((aligned(1024))) bf16_t sm[2 * STAGE];
-
-    const int m_valid = g.tiles ? min(m_tiles, g.tiles[2 * m_tiles]) : m_tiles;
-    int mt, nt;
-    if (!tile_coords(m_valid, n_tiles, g.group_m > 0 ? g.group_m : 4, (int)blockIdx.x, mt, nt,
-                     g.xcd_mode))
-        return;
-    Tile tl;
-    if (!tile_of(g, mt, BM, tl)) return;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;    // wm: the group
-    const int K = g.K, N = g.N;
-    const int out_per_tile = epi_pairs(EPI) ? BNB / 2 : BNB;
-    const int n_base = nt * out_per_tile;
-
-    const int64_t a_rows = g.gather ? g.a_rows : tl.rend;
-    const i32x4 ra = make_rsrc(g.a, (uint32_t)(a_rows * K * 2));
-    const bf16_t* Bp = (g.b_extra && tl.e == g.extra_group)
-                           ? static_cast<const bf16_t*>(g.b_extra)
-                           : static_cast<const bf16_t*>(g.b) + (int64_t)tl.e * g.b_stride;
-    const i32x4 rb = make_rsrc(Bp, (uint32_t)((g.b_tiled ? g.b_stride : (int64_t)g.b_rows * K) * 2));
-    constexpr uint32_t TILE_STAGE = kTileRows * BK * 2;
-    const uint32_t tile_base =
-        (uint32_t)nt * (uint32_t)((K + BK - 1) / BK) * TILE_STAGE;
-
-    // G0 loads: wave w issues blocks w + 4 q, q < 8 of B and of A; lane ->
-    // row lane / 8 of the 8-row block, stored chunk lane % 8 holding the
-    // logical chunk given by the swizzle.  A rows past the group read zeros.
-    const int lrow = lane >> 3;
-    const int lchunk = (lane & 7) ^ swz_chunk<BK>(lrow);
-    uint32_t aoff[8];
-    if (wm == 0) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int64_t r = tl.r0 + RPL * (wave + 4 * q) + lrow;
-            aoff[q] = r < tl.rend
-                          ? (uint32_t)((g.gather ? (int64_t)g.gather[r] : r) * K * 2)
-                          : kOOB;
-        }
-    }
-    auto issue = [&](int kt) {
-        bf16_t* st = sm + (kt & 1) * STAGE;
-        const int kc = kt * BK + lchunk * 8;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int blk = wave + 4 * q;
-            uint32_t off;
-            if (g.b_tiled) {
-                off = tile_base + (uint32_t)kt * TILE_STAGE + (uint32_t)blk * 1024u + lane * 16u;
-            } else {
-                int oc, br;
-                brow_map<EPI>(RPL * blk + lrow, n_base, g.F_split, oc, br);
-                off = (oc < N && kc < K) ? (uint32_t)br * (uint32_t)K * 2u + (uint32_t)kc * 2u
-                                         : kOOB;
-            }
-            llvm_amdgcn_raw_buffer_load_lds(rb, (lds_u32_ptr)(st + BM * BK + blk * 512), 16,
-                                            (int)off, 0, 0, 0);
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int blk = wave + 4 * q;
-            const uint32_t off = kc < K ? aoff[q] + (uint32_t)kc * 2u : kOOB;
-            llvm_amdgcn_raw_buffer_load_lds(ra, (lds_u32_ptr)(st + blk * 512), 16, (int)off, 0,
-                                            0, 0);
-        }
-    };
-
-    floatx4 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int valid_rows = (int)min<int64_t>(tl.rend - tl.r0, (int64_t)BM);
-    const int wlive = min(TM, max(0, (valid_rows - wm * WROWS + 15) / 16));
-    const int fr = lane & 15, fc = lane >> 4;
-    bf16x8 af[KH][TM], bfr[KH][TN];
-    auto read_unit = [&](int u) {
-        const bf16_t* st = sm + ((u / UPS) & 1) * STAGE;
-#pragma unroll
-        for (int h = 0; h < KH; ++h) {
-            const int kk = (u % UPS) * KH + h;
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                bfr[h][j] = *reinterpret_cast<const bf16x8*>(
-                    st + BM * BK + swz<BK>(wn * 64 + 16 * j + fr, kk * 4 + fc));
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                if (i < wlive)
-                    af[h][i] = *reinterpret_cast<const bf16x8*>(
-                        st + swz<BK>(wm * WROWS + 16 * i + fr, kk * 4 + fc));
-        }
-    };
-    auto multiply = [&]() {
-#pragma unroll
-        for (int h = 0; h < KH; ++h)
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                if (i < wlive) {
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[h][j], af[h][i],
-                                                                            acc[i][j], 0, 0, 0);
-                }
-    };
-
-    const int nk = (K + BK - 1) / BK;
-    const int units = nk * UPS;
-    if (wm == 0) {
-        issue(0);
-        if (nk > 1) {
-            issue(1);
-            wait_vmcnt<16>();
-        } else {
-            wait_vmcnt<0>();
-        }
-    }
-    pp_sync();                      // stage 0 landed
-    // Each group runs a loop of its own (one path updates its accumulators,
-    // so they stay in place); s_barrier counts arrivals from any barrier
-    // instruction, and both loops pass the same number of barriers.
-    if (wm == 0) {
-        read_unit(0);
-        pp_sync();
-        for (int u = 0; u + 1 < units; ++u) {
-            const int k = u / UPS;
-            const bool last_of_stage = (u % UPS) == UPS - 1;
-            multiply();                                             // phase 2u
-            if (last_of_stage && k + 1 < nk) wait_vmcnt<0>();       // stage k + 1 landed
-            pp_sync();
-            read_unit(u + 1);                                       // phase 2u + 1
-            if (last_of_stage && k + 2 < nk) issue(k + 2);
-            pp_sync();
-        }
-        multiply();                                                 // the last unit
-        pp_sync();
-    } else {
-        pp_sync();
-        for (int u = 0; u + 1 < units; ++u) {
-            read_unit(u);                                           // phase 2u
-            pp_sync();
-            multiply();                                             // phase 2u + 1
-            pp_sync();
-        }
-        read_unit(units - 1);
-        pp_sync();
-        multiply();        // the last unit, beside G0's epilogue
-    }
-    out_epilogue<EPI, TM, TN, WROWS>(g, tl, acc, wlive, wm, wn, n_base, 0, 0, lane);
 }
 
 // Scalar (wave-uniform) load of p[index] through the constant address
@@ -1074,8 +854,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16(GemmArgs g, int m_tiles, int
         if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
         const bf16_t* st = sm + (kt % STAGES) * STAGE;
         if constexpr (BM == 256 && BNB == 256 && BK == 64) {
-            mfma_stage_full256<BNB, 0>(st, acc, wm, wn, lane,
-                                       [](int) {});   // rows past the end read zeros
+            mfma_stage_full256<BNB, 0>(st, acc, wm, wn, lane);   // rows past the end read zeros
         } else {
 #pragma unroll
             for (int kk = 0; kk < BK / 32; ++kk) {
@@ -1235,16 +1014,6 @@ hipError_t launch_bf16(hipStream_t s, const GemmArgs& g, int64_t m_tiles) {
     return hipGetLastError();
 }
 
-template <int EPI, int PK>
-hipError_t launch_pp(hipStream_t s, const GemmArgs& g, int64_t m_tiles) {
-    const int opt = epi_pairs(EPI) ? 128 : 256;
-    const int n_tiles = (g.N + opt - 1) / opt;
-    const int64_t total = grid_tiles(g, m_tiles, n_tiles);
-    hipLaunchKernelGGL((gemm_bf16_pp<EPI, PK>), dim3((unsigned)total), dim3(NT), 0, s, g,
-                       (int)m_tiles, n_tiles);
-    return hipGetLastError();
-}
-
 template <int EPI>
 hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64_t m_tiles) {
     if (m_tiles <= 0) return hipSuccess;
@@ -1260,18 +1029,7 @@ hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64
             if (g.b_kn) return hipErrorInvalidValue;
         }
         // (256 x 256 with K = 32 stages, 4 or 5 deep, measured slower than 2 x 64)
-        if (bm == 256) {
-            constexpr bool fwd = EPI == EPI_SWIGLU || EPI == EPI_GELU || EPI == EPI_DOWN_SCALED ||
-                                 EPI == EPI_DOWN_F32 || EPI == EPI_SWIGLU_SAVE ||
-                                 EPI == EPI_GELU_SAVE;
-            if constexpr (fwd) {
-                if ((g.schedule == 1 || g.schedule == 2) && g.k_split <= 1 && !g.koff) {
-                    if (g.schedule == 2) return launch_pp<EPI, 32>(s, g, m_tiles);
-                    return launch_pp<EPI, 64>(s, g, m_tiles);
-                }
-            }
-            return launch_bf16<EPI, 256, 256, 2>(s, g, m_tiles);
-        }
+        if (bm == 256) return launch_bf16<EPI, 256, 256, 2>(s, g, m_tiles);
         if (bm == 160) return launch_bf16<EPI, 160, 256, 3>(s, g, m_tiles);
         if (bm == 64) return launch_bf16<EPI, 64, 128, 5>(s, g, m_tiles);
         return launch_bf16<EPI, 128, 256, 3>(s, g, m_tiles);

@@ -35,13 +35,13 @@ def test_descriptor_layout_matches_header(tmp_path):
     prog = tmp_path / "layout.c"
     prog.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
-        'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n",'
+        'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n",'
         ' sizeof(moe_kernel_time), sizeof(moe_desc),'
         ' offsetof(moe_desc,k), offsetof(moe_desc,renorm), offsetof(moe_desc,alpha),'
         ' offsetof(moe_desc,eps), offsetof(moe_desc,weight_layout),'
         ' offsetof(moe_desc,topk_group), offsetof(moe_desc,tile_rows),'
         ' offsetof(moe_desc,tile_order), offsetof(moe_desc,group_m),'
-        ' offsetof(moe_desc,shared_mode), offsetof(moe_desc,schedule)); return 0;}\n')
+        ' offsetof(moe_desc,shared_mode)); return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)],
                    check=True)
@@ -51,7 +51,7 @@ def test_descriptor_layout_matches_header(tmp_path):
     assert got == [ctypes.sizeof(B.moe_kernel_time), ctypes.sizeof(d), d.k.offset,
                    d.renorm.offset, d.alpha.offset, d.eps.offset, d.weight_layout.offset,
                    d.topk_group.offset, d.tile_rows.offset, d.tile_order.offset,
-                   d.group_m.offset, d.shared_mode.offset, d.schedule.offset]
+                   d.group_m.offset, d.shared_mode.offset]
 
 
 def _ws(desc):
@@ -81,7 +81,7 @@ def test_workspace_size_covers_intermediates():
     ("F_shared", 4, B.MOE_ERR_UNSUPPORTED), ("weight_layout", 2, B.MOE_ERR_INVALID),
     ("tile_rows", 96, B.MOE_ERR_INVALID), ("tile_rows", -64, B.MOE_ERR_INVALID),
     ("tile_order", 4, B.MOE_ERR_INVALID), ("group_m", 17, B.MOE_ERR_INVALID),
-    ("shared_mode", 3, B.MOE_ERR_INVALID), ("schedule", 5, B.MOE_ERR_INVALID),
+    ("shared_mode", 3, B.MOE_ERR_INVALID),
 ])
 def test_bad_descriptor_rejected(field, value, status):
     cfg = workloads.shrink(workloads.GLAM_4K, T=16, D=64, F=32).replace(M=8)

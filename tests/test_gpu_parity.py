@@ -281,21 +281,3 @@ def test_small_workspace_rejected_before_launch():
     assert ei.value.status == B.MOE_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert (y.float() == 3.0).all()
-
-
-# The ping-pong main loops of the 256-row tiles: every stage against the
-# oracle, and the layer bitwise equal to the in-step loop (each output
-# element's MFMA sequence over K is the same).
-@pytest.mark.parametrize("sched", ["pingpong64", "pingpong32", "interleaved"])
-@pytest.mark.parametrize("name,tiled", [("glm45_mid", False), ("glm5_rows", False),
-                                        ("glam_mid", False), ("glm45_small", False),
-                                        ("glam_tiles", False), ("glm45_small", True),
-                                        ("glm5_rows", True), ("glm45_t1500", False)])
-def test_schedules(name, tiled, sched):
-    cfg = PARITY[name]
-    Lb, t, y = _stage_parity(cfg, tiled=tiled, tile_rows=256, schedule=sched)
-    L0 = new_layer(cfg, out_dtype="bf16", weight_layout="tiled" if tiled else "rows",
-                   tile_rows=256, schedule="in_step")
-    y0 = forward(L0, t, aux=torch.cuda.Stream())
-    torch.cuda.synchronize()
-    assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
