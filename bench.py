@@ -49,9 +49,8 @@ def log(*a):
 # only for the GEMM source it was measured on (hash of gemm.hip and
 # common.hpp); any change to them reports null until it is measured again.
 TRAFFIC = {
-    ("glam_t4096_d4096_m64_f16384", "ffn_up"): (9403102077, "b20744445ea2158d"),
-    ("glam_t4096_d4096_m64_f16384", "ffn_down"): (9001283677, "b20744445ea2158d"),
-    ("glm45_decode_t64_d5120_m160_f1536", "ffn_up"): (1575484496, "b20744445ea2158d"),
+    ("glm45_t8192_d5120_m160_f1536", "ffn_up"): (9024586379, "aac143997739e717"),
+    ("glm45_t8192_d5120_m160_f1536", "ffn_down"): (4892903764, "aac143997739e717"),
 }
 
 
