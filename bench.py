@@ -318,8 +318,14 @@ def main():
                     help="workgroup order per GEMM (descriptor tuning): one name for all four, "
                          "or up,down,shared_up,shared_down; names auto, xcd_groups, hardware, "
                          "xcd_slices")
+    ap.add_argument("--tile-rows", default=None,
+                    help="rows per tile per GEMM (descriptor tuning): one value for all four, "
+                         "or up,down,shared_up,shared_down; 0 = choose, 64, 128, 160, 256")
     ap.add_argument("--group-m", type=int, default=0,
                     help="m-tiles per group of the tile order (descriptor tuning; 0 = choose)")
+    ap.add_argument("--shared-mode", default="auto", choices=["auto", "separate", "merged"],
+                    help="shared expert launches (descriptor tuning): auto, separate (launches "
+                         "of its own), merged (one more group of the routed GEMMs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
     ap.add_argument("--backward", action="store_true",
@@ -355,8 +361,13 @@ def main():
     if args.tile_order:
         parts = args.tile_order.split(",")
         order = parts * 4 if len(parts) == 1 else parts
+    rows = None
+    if args.tile_rows:
+        parts = [int(v) for v in args.tile_rows.split(",")]
+        rows = parts * 4 if len(parts) == 1 else parts
     L = MoELayer(B.make_desc(cfg, weight_layout=args.weights, tile_order=order,
-                             group_m=args.group_m))
+                             tile_rows=rows, group_m=args.group_m,
+                             shared_mode=args.shared_mode))
     d = L.desc
     tg = dict(t)   # what the GPU reads; t keeps the row-major weights for the oracle
     if args.weights == "tiled":
@@ -449,7 +460,8 @@ def main():
                    "alpha": cfg.alpha, "seed": args.seed, "touched_experts": U,
                    "aux_stream": aux is not None, "weights": args.weights,
                    "tile_order": args.tile_order or "auto",
-                   "group_m": args.group_m},
+                   "tile_rows": args.tile_rows or "auto", "group_m": args.group_m,
+                   "shared_mode": args.shared_mode},
         "active_tflops": round(active_tflops, 2),
         "alg_hbm_gbps": round(alg_gbps, 1),
         "layer_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),
