@@ -12,8 +12,8 @@
 // already bf16, so every partial product is exact and the logits carry fp32
 // accumulation error only, far below the 1e-6 selection-score gap that
 // decides ties.  The GEMM is the expert GEMM kernel in dense mode with
-// split-K (so even 64 tokens fill the GPU); a top-k kernel sums the planes
-// and K chunks in fixed order.  fp32 x (the tiny fp32 layer): one wave per
+// split-K (so even 64 tokens fill the GPU); the top-k kernel sums the
+// planes and K chunks in fixed order.  fp32 x (the tiny fp32 layer): one wave per
 // token with fp64 dot products.  Both paths share one wavefront top-k
 // epilogue.
 #include "common.hpp"
@@ -222,24 +222,6 @@ __global__ __launch_bounds__(256) void router_split(const float* __restrict__ W_
     *reinterpret_cast<bf16x8*>(W3 + 2 * n + i) = lo;
 }
 
-// logit[t][e] = sum over K chunks z (in order) of the hi plane's partial,
-// plus the same sums of the mid and lo planes: P[z][t][p*M + e] is
-// x_t . plane_p[e] over chunk z.  One thread per (token, expert).
-__global__ __launch_bounds__(256) void route_reduce(const float* __restrict__ P, int nK, int T,
-                                                    int M, float* __restrict__ L) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)T * M) return;
-    const int64_t t = i / M, e = i % M, ld = 3 * (int64_t)M;
-    float h = 0.f, m = 0.f, l = 0.f;
-    for (int z = 0; z < nK; ++z) {
-        const float* row = P + ((int64_t)z * T + t) * ld;
-        h += row[e];
-        m += row[M + e];
-        l += row[2 * M + e];
-    }
-    L[i] = h + (m + l);
-}
-
 constexpr int64_t kSmallRouteT = 256;   // bf16 batches up to this many tokens: fp64 dot router
 
 // Small batches (decode): L[t][e] = x_t . W_r[e] accumulated in fp64 (the
@@ -294,6 +276,43 @@ __global__ __launch_bounds__(256) void route_logits_small(const bf16_t* __restri
     }
 }
 
+// One wave per token straight from the GEMM's partial logits: the wave sums
+// its token's P[z][t][p M + e] over the K chunks z in order for each plane
+// p, adds the planes as hi + (mid + lo) (so the logits are bitwise those of
+// a separate reduction pass), stores them in L[t][0..M) (the backward's
+// recomputed routing reads them there), stages them in its own LDS row and
+// runs the top-k epilogue on it.
+__global__ __launch_bounds__(256) void route_topk_partials(
+    const float* __restrict__ P, int nK, float* __restrict__ L, const float* __restrict__ bias,
+    int32_t* __restrict__ idx, float* __restrict__ w, int T, int M, int k, int scorer,
+    int renorm, float alpha, float eps, int n_group, int topk_group) {
+    extern __shared__ float s_logit[];   // [4][M]
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;   // whole wave leaves; no block barrier follows
+    float* lrow = s_logit + wave * M;
+    const int64_t ld = 3 * (int64_t)M;
+    for (int e = lane; e < M; e += 64) {
+        float h = 0.f, m = 0.f, l = 0.f;
+        for (int z = 0; z < nK; ++z) {
+            const float* row = P + ((int64_t)z * T + t) * ld;
+            h += row[e];
+            m += row[M + e];
+            l += row[2 * M + e];
+        }
+        const float v = h + (m + l);
+        lrow[e] = v;
+        L[(int64_t)t * M + e] = v;
+    }
+    // the wave's own LDS row: make the writes visible across lanes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    topk_epilogue(lrow, M, k, scorer, bias, renorm, (double)alpha, (double)eps, n_group,
+                  topk_group, idx + (int64_t)t * k, w + (int64_t)t * k);
+}
+
 // One wave per token: the top-k epilogue on its logits L[t][0..M).
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ L,
                                                   const float* __restrict__ bias,
@@ -343,16 +362,28 @@ __global__ __launch_bounds__(256) void route_simple(
 }  // namespace
 
 int route_ksplit(int64_t T, int64_t D, int64_t M) {
-    // the logits GEMM (T x 3M, K = D) in 128 x 256 tiles: enough K chunks for
-    // a few hundred workgroups, each chunk at least 512 long (256 when the
-    // tile grid is tiny, as at decode)
+    // The logits GEMM (T x 3M, K = D) runs in 128 x 256 tiles, one
+    // workgroup per CU at a time (256 CUs).  K chunks multiply the
+    // workgroups; each chunk is at least 512 long (256 when the tile grid is
+    // tiny).  The count minimises rounds of workgroups x K stages per
+    // workgroup, so that no round runs half empty (GLM-4.5 prefill: 128
+    // tiles x 2 chunks = one full round of 40 stages, against 3 chunks = 1.5
+    // rounds of 27); on a tie, fewer chunks (less partial-logit traffic).
     const int64_t base = ((T + 127) / 128) * ((3 * M + 255) / 256);
     if (base <= 0 || D <= 0) return 1;
-    int64_t nk = (384 + base - 1) / base;
-    const int64_t maxk = D / (base < 32 ? 256 : 512);
-    if (nk > maxk) nk = maxk;
-    if (nk < 1) nk = 1;
-    return (int)nk;
+    constexpr int64_t kCUs = 256;
+    const int64_t stages = (D + 63) / 64;
+    int64_t maxk = D / (base < 32 ? 256 : 512);
+    if (maxk < 1) maxk = 1;
+    int64_t best = 1, best_cost = -1;
+    for (int64_t nk = 1; nk <= maxk; ++nk) {
+        const int64_t cost = ((base * nk + kCUs - 1) / kCUs) * ((stages + nk - 1) / nk);
+        if (best_cost < 0 || cost < best_cost) {
+            best = nk;
+            best_cost = cost;
+        }
+    }
+    return (int)best;
 }
 
 // Workspace: the split router weights W3 [3][M][D] bf16, the partial logits
@@ -407,10 +438,9 @@ hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, con
         g.k_split = nK;
         hipError_t e = launch_gemm(s, 1, 128, EPI_DOWN_F32, g, (T + 127) / 128);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(route_reduce, dim3((unsigned)((T * M + 255) / 256)), dim3(256), 0, s,
-                           P, nK, (int)T, (int)M, L);
-        hipLaunchKernelGGL(route_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, L, b, idx,
-                           w, (int)T, (int)M, k, scorer, renorm, alpha, eps, n_group, topk_group);
+        hipLaunchKernelGGL(route_topk_partials, dim3((unsigned)((T + 3) / 4)), dim3(256),
+                           4 * (size_t)M * sizeof(float), s, P, nK, L, b, idx, w, (int)T,
+                           (int)M, k, scorer, renorm, alpha, eps, n_group, topk_group);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((T + 3) / 4));
