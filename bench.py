@@ -326,6 +326,10 @@ def main():
     ap.add_argument("--shared-mode", default="auto", choices=["auto", "separate", "merged"],
                     help="shared expert launches (descriptor tuning): auto, separate (launches "
                          "of its own), merged (one more group of the routed GEMMs)")
+    ap.add_argument("--rows-format", default="auto", choices=["auto", "fp32", "compact"],
+                    help="precision of the expert rows between the down projection and the "
+                         "combine (auto: compact fp16 with a power-of-two scale per 64 values "
+                         "for bf16 layers)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
     ap.add_argument("--backward", action="store_true",
@@ -367,7 +371,7 @@ def main():
         rows = parts * 4 if len(parts) == 1 else parts
     L = MoELayer(B.make_desc(cfg, weight_layout=args.weights, tile_order=order,
                              tile_rows=rows, group_m=args.group_m,
-                             shared_mode=args.shared_mode))
+                             shared_mode=args.shared_mode, rows_format=args.rows_format))
     d = L.desc
     tg = dict(t)   # what the GPU reads; t keeps the row-major weights for the oracle
     if args.weights == "tiled":
@@ -461,7 +465,7 @@ def main():
                    "aux_stream": aux is not None, "weights": args.weights,
                    "tile_order": args.tile_order or "auto",
                    "tile_rows": args.tile_rows or "auto", "group_m": args.group_m,
-                   "shared_mode": args.shared_mode},
+                   "shared_mode": args.shared_mode, "rows_format": args.rows_format},
         "active_tflops": round(active_tflops, 2),
         "alg_hbm_gbps": round(alg_gbps, 1),
         "layer_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),

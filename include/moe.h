@@ -117,7 +117,23 @@ enum { MOE_WEIGHT_W1 = 0, MOE_WEIGHT_W2 = 1, MOE_WEIGHT_SH_GU = 2, MOE_WEIGHT_SH
  *   shared_mode   0 (choose), 1 the shared expert in launches of its own
  *                 (on aux_stream when given), 2 the shared expert as one
  *                 more group of the routed GEMM launches (needs F_shared ==
- *                 F, SwiGLU, bf16 and T <= 1024; otherwise as 1)        */
+ *                 F, SwiGLU, bf16 and T <= 1024; otherwise as 1)
+ * With rows_format 1 every tuning setting gives bitwise the same output; the
+ * compact rows are used only where the shared expert is not merged, so with
+ * them a merged and a separate shared expert differ by that rounding.
+ *
+ * Precision of one intermediate (a choice of rounding inside the layer's
+ * stated tolerance, not tuning):
+ *   rows_format   the gate-weighted expert rows that moe_forward hands from
+ *                 the down projection to the combine: 0 (choose: compact
+ *                 for bf16 layers), 1 fp32, 2 compact: fp16 values with one
+ *                 power-of-two scale per 64 consecutive values of a row,
+ *                 chosen so that the group's largest finite magnitude lands
+ *                 in [2^14, 2^15) (scaling is exact, one round-to-nearest-
+ *                 even to fp16: relative error <= 2^-11; half the bytes of
+ *                 fp32).  bf16 layers only; a shared expert merged into the
+ *                 routed GEMMs keeps fp32 rows.  The stage entry points
+ *                 (moe_expert_ffn, moe_combine) always exchange fp32 rows. */
 typedef struct moe_desc {
     int64_t T, D, M, F, F_shared;
     int32_t k;
@@ -135,6 +151,7 @@ typedef struct moe_desc {
     int32_t tile_order[4];
     int32_t group_m;
     int32_t shared_mode;
+    int32_t rows_format;
 } moe_desc;
 
 /* Indices of moe_desc.tile_rows / tile_order. */

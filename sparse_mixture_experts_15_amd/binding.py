@@ -43,7 +43,7 @@ class moe_desc(ctypes.Structure):
                 ("weight_layout", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("tile_rows", ctypes.c_int32 * 4),
                 ("tile_order", ctypes.c_int32 * 4), ("group_m", ctypes.c_int32),
-                ("shared_mode", ctypes.c_int32)]
+                ("shared_mode", ctypes.c_int32), ("rows_format", ctypes.c_int32)]
 
 
 class moe_kernel_time(ctypes.Structure):
@@ -120,6 +120,7 @@ def _check(fn: str, rc: int):
 GEMMS = ("up", "down", "shared_up", "shared_down")   # order of tile_rows / tile_order
 ORDER = {"auto": 0, "xcd_groups": 1, "hardware": 2, "xcd_slices": 3}
 SHARED_MODE = {"auto": 0, "separate": 1, "merged": 2}
+ROWS_FORMAT = {"auto": 0, "fp32": 1, "compact": 2}
 
 
 def make_desc(cfg=None, **kw) -> moe_desc:
@@ -129,7 +130,8 @@ def make_desc(cfg=None, **kw) -> moe_desc:
     out_dtype defaults to dtype, weight_layout to "rows".  Launch tuning
     (default: the library's choice): tile_rows and tile_order as dicts keyed
     by GEMMS names or 4-sequences, group_m, shared_mode ("separate",
-    "merged")."""
+    "merged").  rows_format ("auto", "fp32", "compact") picks the precision
+    of the expert rows inside moe_forward."""
     f = {}
     if cfg is not None:
         for n in ("T", "D", "M", "F", "F_shared", "k", "scorer", "act", "dtype", "renorm",
@@ -151,6 +153,7 @@ def make_desc(cfg=None, **kw) -> moe_desc:
         return (ctypes.c_int32 * 4)(*[int(names.get(x, x) if names else x) for x in v])
 
     sm = f.get("shared_mode", 0)
+    rf = f.get("rows_format", 0)
     return moe_desc(T=int(f["T"]), D=int(f["D"]), M=int(f["M"]), F=int(f["F"]),
                     F_shared=int(f.get("F_shared", 0)), k=int(f["k"]),
                     scorer=SCORER.get(sc, sc), act=ACT.get(ac, ac), dtype=DTYPE.get(dt, dt),
@@ -161,7 +164,8 @@ def make_desc(cfg=None, **kw) -> moe_desc:
                     tile_rows=four(f.get("tile_rows")),
                     tile_order=four(f.get("tile_order"), ORDER),
                     group_m=int(f.get("group_m", 0)),
-                    shared_mode=int(SHARED_MODE.get(sm, sm)))
+                    shared_mode=int(SHARED_MODE.get(sm, sm)),
+                    rows_format=int(ROWS_FORMAT.get(rf, rf)))
 
 
 def _ptr(t, name, dtype=None, numel=None):

@@ -43,6 +43,9 @@ struct Plan {
     // M, every token once) of the routed GEMMs; its rows follow the S routed
     // rows, so Hsh and Ysh are the tails of H and O, and Sx = S + T.
     bool merged = false;
+    // compact: moe_forward hands the expert rows from the down projection to
+    // the combine as fp16 values with a scale per 64 (in O's space)
+    bool compact = false;
     int64_t Sx = 0;
     int64_t S = 0, nblk = 0, max_tiles_up = 0, max_tiles_dn = 0;
     int bm_up = 0, bm_dn = 0, bm_sh_up = 0, bm_sh_dn = 0;
@@ -66,6 +69,7 @@ Plan make_plan(const moe_desc* d, bool allow_merge = true) {
                            d->act == MOE_ACT_SWIGLU && d->dtype == MOE_DTYPE_BF16 &&
                            d->T <= kSmallT && d->M + 1 <= 1024;
     p.merged = allow_merge && can_merge && d->shared_mode != 1;
+    p.compact = !p.merged && d->dtype == MOE_DTYPE_BF16 && d->rows_format != 1;
     const int64_t groups = d->M + (p.merged ? 1 : 0);
     p.Sx = p.S + (p.merged ? d->T : 0);
     p.bm_up = gemm_block_m(d->dtype, p.Sx, groups, false, G * d->F, d->tile_rows[MOE_GEMM_UP]);
@@ -101,7 +105,10 @@ Plan make_plan(const moe_desc* d, bool allow_merge = true) {
         p.Ysh = p.O + (size_t)p.S * d->D * 4;
     } else {
         p.H = take((size_t)p.S * d->F * p.esz);
-        p.O = take((size_t)p.S * d->D * 4);
+        // fp32 rows, or the compact rows (smaller except at tiny sizes,
+        // where the exponents' 256-byte alignment dominates)
+        p.O = take(std::max((size_t)p.S * d->D * 4,
+                            (size_t)compact_row_bytes(p.S, d->D)));
         p.Hsh = take((size_t)d->T * d->F_shared * p.esz);
         p.Ysh = take(d->F_shared > 0 ? (size_t)d->T * d->D * 4 : 0);
     }
@@ -149,6 +156,10 @@ int validate(const moe_desc* d) {
         return fail(MOE_ERR_INVALID, "group_m=%d is not in [0, 16]", d->group_m);
     if (d->shared_mode < 0 || d->shared_mode > 2)
         return fail(MOE_ERR_INVALID, "shared_mode=%d is not in [0, 2]", d->shared_mode);
+    if (d->rows_format < 0 || d->rows_format > 2)
+        return fail(MOE_ERR_INVALID, "rows_format=%d is not in [0, 2]", d->rows_format);
+    if (d->rows_format == 2 && d->dtype != MOE_DTYPE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "compact expert rows need a bf16 layer");
     if (d->weight_layout != MOE_LAYOUT_ROWS && d->weight_layout != MOE_LAYOUT_TILED)
         return fail(MOE_ERR_INVALID, "unknown weight_layout %d", d->weight_layout);
     if (d->weight_layout == MOE_LAYOUT_TILED && d->dtype != MOE_DTYPE_BF16)
@@ -336,7 +347,7 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
                   int32_t* sorted_token, const int32_t* sorted_slot, int32_t* offsets,
                   const float* w, const void* W1, const void* b1, const void* W2, const void* b2,
                   float* O, void* ws, hipStream_t s, const void* Wsh_gu = nullptr,
-                  const void* Wsh_dn = nullptr) {
+                  const void* Wsh_dn = nullptr, bool compact = false) {
     const bool merged = Wsh_gu != nullptr;
     const int64_t rows = merged ? p.Sx : p.S;
     int32_t* tiles_up = at<int32_t>(ws, p.tiles_up);
@@ -388,6 +399,10 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
     dn.row_w = row_scale;
     dn.dense_rows = rows;
     dn.c = O;
+    if (compact) {   // O's space holds the compact rows instead
+        dn.c16 = O;
+        dn.cexp = reinterpret_cast<int8_t*>(O) + compact_exp_offset(rows, d->D);
+    }
     dn.tiles = tiles_dn;
     dn.group_m = gemm_group_m(rows, d->M, p.bm_dn, d->group_m);
     if (merged) {
@@ -442,8 +457,13 @@ int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, co
 }
 
 int do_combine(moe_handle* h, const moe_desc* d, const float* O, const int32_t* slot_row,
-               const float* Ysh, void* y, hipStream_t s) {
+               const float* Ysh, void* y, hipStream_t s, bool compact = false) {
     return run(h, s, L_COMBINE, [&] {
+        if (compact)
+            return launch_combine_compact(
+                s, d->out_dtype, O,
+                reinterpret_cast<const int8_t*>(O) + compact_exp_offset(d->T * d->k, d->D),
+                slot_row, Ysh, y, d->T, d->k, d->D);
         return launch_combine(s, d->out_dtype, O, slot_row, Ysh, y, d->T, d->k, d->D);
     });
 }
@@ -856,12 +876,13 @@ int forward_impl(moe_handle* h, const moe_desc* d, const void* x, const float* W
     }
     TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
     TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
-    TRY(do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O, ws, s));
+    TRY(do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O, ws, s,
+                      nullptr, nullptr, p.compact));
     if (fork) {
         const hipError_t e = hipStreamWaitEvent(s, h->ev_join, 0);
         if (e != hipSuccess) return fail(MOE_ERR_HIP, "stream join: %s", hipGetErrorString(e));
     }
-    return do_combine(h, d, O, slot_row, Ysh, y, s);
+    return do_combine(h, d, O, slot_row, Ysh, y, s, p.compact);
 }
 
 }  // namespace

@@ -151,7 +151,24 @@ struct GemmArgs {
     const int32_t* koff;
     int kgroups;
     int64_t c_group_stride;
+    // EPI_DOWN_SCALED, compact rows (c16 non-null, c unused): c16[r, n] fp16
+    // values with one scale exponent cexp[r, n / kRowGroup] per kRowGroup
+    // columns, the value being c16 * 2^cexp
+    void* c16;
+    int8_t* cexp;
 };
+
+// Compact expert rows: fp16 values with one power-of-two scale per
+// kRowGroup consecutive values of a row (the 64 columns one wave of the
+// down projection holds of a row); [rows, N] fp16, then the exponents
+// [rows, ceil(N / kRowGroup)] int8 at a 256-byte aligned offset.
+constexpr int kRowGroup = 64;
+inline int64_t compact_exp_offset(int64_t rows, int64_t N) {
+    return ((rows * N * 2) + 255) & ~int64_t(255);
+}
+inline int64_t compact_row_bytes(int64_t rows, int64_t N) {
+    return compact_exp_offset(rows, N) + rows * ((N + kRowGroup - 1) / kRowGroup);
+}
 
 // Weight tiles of the bf16 GEMM: 256 weight rows by K stages of 64.
 constexpr int kTileRows = 256;
@@ -225,6 +242,12 @@ hipError_t launch_gemm(hipStream_t s, int dtype, int bm, int epi, const GemmArgs
                        int64_t m_tiles);
 hipError_t launch_combine(hipStream_t s, int out_dtype, const float* O, const int32_t* slot_row,
                           const float* Ysh, void* y, int64_t T, int k, int64_t D);
+// The combine over compact rows (fp16 values O16 with exponents Oexp, as the
+// compact EPI_DOWN_SCALED epilogue writes them); same order and rounding of
+// the fp32 sum as launch_combine.
+hipError_t launch_combine_compact(hipStream_t s, int out_dtype, const void* O16,
+                                  const int8_t* Oexp, const int32_t* slot_row, const float* Ysh,
+                                  void* y, int64_t T, int k, int64_t D);
 
 // Backward (backward.hip).
 hipError_t launch_transpose(hipStream_t s, const void* src, int64_t ld_src, int64_t src_rows,

@@ -317,6 +317,56 @@ __device__ __forceinline__ void out_epilogue(const GemmArgs& g, const Tile& tl,
         if (r >= tl.rend) continue;
         float wr = 1.f;
         if (EPI == EPI_DOWN_SCALED) wr = g.row_w[r];
+        if constexpr (EPI == EPI_DOWN_SCALED) {
+            if (g.c16) {
+                // compact rows: the four lanes holding this row's 64 columns
+                // agree on a power-of-two scale that puts the group's largest
+                // finite magnitude in [2^14, 2^15) (exponent read from its
+                // bits), then each stores its values scaled (exactly) and
+                // rounded once to fp16
+                static_assert(OUT_W == kRowGroup, "one scale per wave row segment");
+                const int G = (N + kRowGroup - 1) / kRowGroup;
+                float v[OUT_FR][4];
+                float m = 0.f;
+#pragma unroll
+                for (int j = 0; j < OUT_FR; ++j) {
+                    const int n = n_base + OUT_W * wn + 16 * j + lc;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        v[j][q] = n + q < N ? wr * (acc[i][j][q] + bv[j][q]) : 0.f;
+                        const float a = fabsf(v[j][q]);
+                        if (a <= 3.402823466e38f) m = fmaxf(m, a);   // finite values only
+                    }
+                }
+                m = fmaxf(m, __shfl_xor(m, 16));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                const int be = (int)((__float_as_uint(m) >> 23) & 0xffu);   // biased exponent
+                const int e = min(max(be - 127 - 14, -128), 113);
+#pragma unroll
+                for (int j = 0; j < OUT_FR; ++j) {
+                    const int n = n_base + OUT_W * wn + 16 * j + lc;
+                    if (n >= N) continue;
+                    uint16_t hv[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        hv[q] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(v[j][q], -e));
+                    uint16_t* dst = static_cast<uint16_t*>(g.c16) + r * N + n;
+                    if (vec && n + 4 <= N) {
+                        uint2 pk;
+                        pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+                        pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+                        *reinterpret_cast<uint2*>(dst) = pk;
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (n + q < N) dst[q] = hv[q];
+                    }
+                }
+                const int n0 = n_base + OUT_W * wn;
+                if (lc == 0 && n0 < N) g.cexp[r * G + n0 / kRowGroup] = (int8_t)e;
+                continue;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < OUT_FR; ++j) {
             const int n = n_base + OUT_W * wn + 16 * j + lc;

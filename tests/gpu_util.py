@@ -103,6 +103,22 @@ def y_plain(cfg) -> bool:
     return cfg.F >= Y_PLAIN_MIN_WIDTH and (cfg.F_shared == 0 or
                                             cfg.F_shared >= Y_PLAIN_MIN_WIDTH)
 SLACK = 1e-3             # fp32 accumulation and activation error, as a fraction of RMS
+# Largest relative error of the compact expert rows (fp16 with an exact
+# power-of-two scale, one round-to-nearest-even) that moe_forward uses
+# between the down projection and the combine of a bf16 layer.
+COMPACT_REL = 2.0 ** -11
+
+
+def uses_compact_rows(cfg, shared_mode="auto", rows_format="auto") -> bool:
+    """Whether moe_forward of cfg hands compact expert rows to the combine:
+    bf16 layers unless fp32 rows are asked for or the shared expert is
+    merged into the routed GEMMs (decode-sized batch, a shared expert of one
+    routed expert's SwiGLU shape), whose rows stay fp32."""
+    if cfg.dtype != "bf16" or rows_format == "fp32":
+        return False
+    merged = (cfg.F_shared > 0 and cfg.F_shared == cfg.F and cfg.act == "swiglu"
+              and cfg.T <= 1024 and cfg.M + 1 <= 1024 and shared_mode != "separate")
+    return not merged
 
 
 def _act(cfg, Z, b1=None):
@@ -115,14 +131,15 @@ def _act(cfg, Z, b1=None):
     return 0.5 * Z * (1.0 + special.erf(Z / np.sqrt(2.0)))
 
 
-def rounding_bounds(cfg, h, idx, w):
+def rounding_bounds(cfg, h, idx, w, compact=False):
     """Forward-error bound of the bf16 path's one unavoidable rounding: the
     hidden activation H is rounded to bf16 (relative error <= 2^-8) before
     the bf16 down projection, so an output element O_i = w sum_f H_f W2_if
-    can be off by up to 2^-8 w sum_f |H_f| |W2_if|.  Returns that bound per
-    (token, slot) row [T, k, D] and for the shared expert [T, D] (or None).
-    Computed with numpy from the same inputs; it is an error allowance, never
-    an expected value."""
+    can be off by up to 2^-8 w sum_f |H_f| |W2_if|.  With `compact` (the
+    forward's compact expert rows) each row element also carries up to
+    2^-11 |O_i|.  Returns that bound per (token, slot) row [T, k, D] and for
+    the shared expert [T, D] (or None).  Computed with numpy from the same
+    inputs; it is an error allowance, never an expected value."""
     X = widen(h["x"])
     W1, W2 = widen(h["W1"]), widen(h["W2"])
     b1 = widen(h["b1"]) if h.get("b1") is not None else None
@@ -132,8 +149,13 @@ def rounding_bounds(cfg, h, idx, w):
         if e < 0 or e >= cfg.M:
             continue
         tt, jj = np.nonzero(idx == e)
-        Hm = np.abs(_act(cfg, X[tt] @ W1[e].T, None if b1 is None else b1[e]))
-        bnd[tt, jj] = BF16_REL * np.abs(w[tt, jj])[:, None] * (Hm @ np.abs(W2[e]).T)
+        Hs = _act(cfg, X[tt] @ W1[e].T, None if b1 is None else b1[e])
+        bnd[tt, jj] = BF16_REL * np.abs(w[tt, jj])[:, None] * (np.abs(Hs) @ np.abs(W2[e]).T)
+        if compact:
+            Oe = Hs @ W2[e].T
+            if h.get("b2") is not None:
+                Oe = Oe + widen(h["b2"])[e]
+            bnd[tt, jj] += COMPACT_REL * np.abs(w[tt, jj])[:, None] * np.abs(Oe)
     bsh = None
     if cfg.F_shared:
         gu, dn = widen(h["Wsh_gu"]), widen(h["Wsh_dn"])
@@ -150,12 +172,12 @@ def _widen32(a):
     return a.astype(np.float32)
 
 
-def rounding_bounds_tokens(cfg, h, idx, w, tokens):
+def rounding_bounds_tokens(cfg, h, idx, w, tokens, compact=False):
     """rounding_bounds' bound on the layer output y for the listed tokens
     only, [len(tokens), D]: per routed slot 2^-8 |w| sum_f |H_f| |W2_if|, plus
     the shared expert's 2^-8 sum_f |Hsh_f| |Wsh_dn_if|.  Only the experts those
     tokens reach are widened (fp32 suffices for an allowance), so it runs at
-    full layer sizes."""
+    full layer sizes.  `compact` adds the compact rows' 2^-11 |O| per slot."""
     from scipy import special
     X = _widen32(h["x"][tokens])
     out = np.zeros((len(tokens), cfg.D), np.float64)
@@ -166,9 +188,14 @@ def rounding_bounds_tokens(cfg, h, idx, w, tokens):
         rr, jj = np.nonzero(sub_idx == e)
         W1 = _widen32(h["W1"][e])
         b1 = _widen32(h["b1"][e]) if h.get("b1") is not None else None
-        Hm = np.abs(_act(cfg, (X[rr] @ W1.T).astype(np.float64), b1))
-        W2 = np.abs(_widen32(h["W2"][e]))
-        np.add.at(out, rr, BF16_REL * np.abs(sub_w[rr, jj])[:, None] * (Hm @ W2.T.astype(np.float64)))
+        Hs = _act(cfg, (X[rr] @ W1.T).astype(np.float64), b1)
+        W2s = _widen32(h["W2"][e]).astype(np.float64)
+        np.add.at(out, rr, BF16_REL * np.abs(sub_w[rr, jj])[:, None] * (np.abs(Hs) @ np.abs(W2s).T))
+        if compact:
+            Oe = Hs @ W2s.T
+            if h.get("b2") is not None:
+                Oe = Oe + _widen32(h["b2"][e]).astype(np.float64)
+            np.add.at(out, rr, COMPACT_REL * np.abs(sub_w[rr, jj])[:, None] * np.abs(Oe))
     if cfg.F_shared:
         Z = (X @ _widen32(h["Wsh_gu"]).T).astype(np.float64)
         g, u = Z[:, :cfg.F_shared], Z[:, cfg.F_shared:]

@@ -35,13 +35,13 @@ def test_descriptor_layout_matches_header(tmp_path):
     prog = tmp_path / "layout.c"
     prog.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
-        'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n",'
+        'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n",'
         ' sizeof(moe_kernel_time), sizeof(moe_desc),'
         ' offsetof(moe_desc,k), offsetof(moe_desc,renorm), offsetof(moe_desc,alpha),'
         ' offsetof(moe_desc,eps), offsetof(moe_desc,weight_layout),'
         ' offsetof(moe_desc,topk_group), offsetof(moe_desc,tile_rows),'
         ' offsetof(moe_desc,tile_order), offsetof(moe_desc,group_m),'
-        ' offsetof(moe_desc,shared_mode)); return 0;}\n')
+        ' offsetof(moe_desc,shared_mode), offsetof(moe_desc,rows_format)); return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)],
                    check=True)
@@ -51,7 +51,7 @@ def test_descriptor_layout_matches_header(tmp_path):
     assert got == [ctypes.sizeof(B.moe_kernel_time), ctypes.sizeof(d), d.k.offset,
                    d.renorm.offset, d.alpha.offset, d.eps.offset, d.weight_layout.offset,
                    d.topk_group.offset, d.tile_rows.offset, d.tile_order.offset,
-                   d.group_m.offset, d.shared_mode.offset]
+                   d.group_m.offset, d.shared_mode.offset, d.rows_format.offset]
 
 
 def _ws(desc):
@@ -81,7 +81,7 @@ def test_workspace_size_covers_intermediates():
     ("F_shared", 4, B.MOE_ERR_UNSUPPORTED), ("weight_layout", 2, B.MOE_ERR_INVALID),
     ("tile_rows", 96, B.MOE_ERR_INVALID), ("tile_rows", -64, B.MOE_ERR_INVALID),
     ("tile_order", 4, B.MOE_ERR_INVALID), ("group_m", 17, B.MOE_ERR_INVALID),
-    ("shared_mode", 3, B.MOE_ERR_INVALID),
+    ("shared_mode", 3, B.MOE_ERR_INVALID), ("rows_format", 3, B.MOE_ERR_INVALID),
 ])
 def test_bad_descriptor_rejected(field, value, status):
     cfg = workloads.shrink(workloads.GLAM_4K, T=16, D=64, F=32).replace(M=8)
@@ -231,3 +231,14 @@ def test_tuning_fields_select_the_plan_not_the_result_shape():
     out = subprocess.run(["nm", "-D", "--undefined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     assert not re.search(r"\bgetenv\b", out), "the library reads the environment"
+
+
+def test_compact_rows_need_a_bf16_layer():
+    cfg = workloads.shrink(workloads.GLM45_PREFILL, T=16, D=64, F=32).replace(dtype="f32")
+    d = B.make_desc(cfg, rows_format="compact")
+    n = ctypes.c_size_t()
+    rc = B.load_library().moe_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    assert rc == B.MOE_ERR_UNSUPPORTED, B.last_error_detail()
+    # fp32 rows, or the choice, are accepted for it
+    for rf in ("auto", "fp32"):
+        assert B.moe_workspace_size(B.make_desc(cfg, rows_format=rf)) > 0

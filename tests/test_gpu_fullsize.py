@@ -20,7 +20,7 @@ import oracle
 import workloads
 from tests.gpu_util import (assert_rounded_from, check_float, check_dispatch_props, check_route,
                             forward, gpu_permute, new_layer, rounding_bounds_tokens, run_route,
-                            tiled_weights, to_np)
+                            tiled_weights, to_np, uses_compact_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -107,7 +107,7 @@ def test_full_size_forward(name, layout):
     y_o = oracle.layer(cfg, h["x"], idx_o, w_o, h["W1"], h["b1"], h["W2"], h["b2"],
                        h["Wsh_gu"], h["Wsh_dn"], tokens=toks)
     if name in GATE_SCALED:
-        bound = rounding_bounds_tokens(cfg, h, idx_o, w_o, toks)
+        bound = rounding_bounds_tokens(cfg, h, idx_o, w_o, toks, compact=uses_compact_rows(cfg))
         err, scale = check_float(cfg, y32h[toks], y_o, f"{cfg.name} fp32 y on {len(toks)} "
                                  "tokens", bound=bound, plain=False)
     else:

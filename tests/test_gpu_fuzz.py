@@ -25,7 +25,7 @@ import oracle
 import workloads
 from tests.gpu_util import (assert_rounded_from, check_dispatch_props, check_float, check_route,
                             forward, gpu_permute, new_layer, rounding_bounds, run_route,
-                            tiled_weights, to_np, y_plain)
+                            tiled_weights, to_np, uses_compact_rows, y_plain)
 
 pytestmark = pytest.mark.gpu
 
@@ -130,7 +130,7 @@ def test_fuzz_case(case):
     wide = y_plain(cfg)
     bound = None
     if bf and not wide:
-        bnd, bsh = rounding_bounds(cfg, h, idx_o, w_o)
+        bnd, bsh = rounding_bounds(cfg, h, idx_o, w_o, compact=uses_compact_rows(cfg))
         bound = (bnd.sum(axis=1) + (bsh if bsh is not None else 0.0))[keep]
     check_float(cfg, got, y_o[keep], "forward y", bound=bound, plain=wide or not bf)
     if bf:

@@ -14,9 +14,10 @@ import torch
 import oracle
 import workloads
 from sparse_mixture_experts_15_amd import binding as B
-from tests.gpu_util import (PLAIN_MIN_WIDTH, assert_rounded_from, check_dispatch_props,
-                            check_float, check_route, dev_i32, forward, gpu_permute, new_layer,
-                            rounding_bounds, run_route, tiled_weights, to_np, y_plain)
+from tests.gpu_util import (COMPACT_REL, PLAIN_MIN_WIDTH, assert_rounded_from,
+                            check_dispatch_props, check_float, check_route, dev_i32, forward,
+                            gpu_permute, new_layer, rounding_bounds, run_route, tiled_weights,
+                            to_np, uses_compact_rows, y_plain)
 
 pytestmark = pytest.mark.gpu
 
@@ -113,12 +114,16 @@ def _stage_parity(cfg, seed=0, tiled=False, **tuning):
     wide = y_plain(cfg)
     check_float(cfg, to_np(y).reshape(T, D), y_o, "combine y", bound=ybnd, plain=wide)
 
-    # whole layer, shared expert on a second stream, fp32 output
+    # whole layer, shared expert on a second stream, fp32 output (its expert
+    # rows compact for bf16 layers: up to 2^-11 |O| more per slot)
     aux = torch.cuda.Stream()
     y_f = forward(L, t, aux=aux)
     torch.cuda.synchronize()
     keep = ~mism
-    check_float(cfg, to_np(y_f).reshape(T, D)[keep], y_o[keep], "forward y", bound=ybnd[keep],
+    fbnd = ybnd
+    if uses_compact_rows(cfg):
+        fbnd = ybnd + COMPACT_REL * np.abs(slots_o).sum(axis=1)
+    check_float(cfg, to_np(y_f).reshape(T, D)[keep], y_o[keep], "forward y", bound=fbnd[keep],
                 plain=wide)
     if not bf:
         return L, t, y_f
@@ -159,7 +164,10 @@ def test_forward_deterministic_and_stream_invariant(name):
     assert torch.equal(y1.view(torch.int16) if y1.dtype == torch.bfloat16 else y1,
                        y2.view(torch.int16) if y2.dtype == torch.bfloat16 else y2)
     assert torch.equal(y1, y3)
-    # the stage calls chained on the GPU's own outputs reproduce forward bitwise
+    # the stage calls chained on the GPU's own outputs (fp32 expert rows)
+    # reproduce the forward with fp32 rows bitwise
+    L = new_layer(cfg, rows_format="fp32")
+    y1 = forward(L, t, aux=aux)
     d = L.desc
     idx, w = run_route(L, d, t)
     p = gpu_permute(L, d, idx)
@@ -174,6 +182,51 @@ def test_forward_deterministic_and_stream_invariant(name):
     B.moe_combine(L.handle, d, O, p["slot_row"], Ysh, y4)
     torch.cuda.synchronize()
     assert torch.equal(y1, y4)
+
+
+@pytest.mark.parametrize("name", ["glm45_small", "glam_tiles", "glm45_mid", "glam_mid",
+                                  "glm5_rows", "glm5_small"])
+def test_compact_rows_within_fp16_rounding(name):
+    """The forward with compact expert rows against the same forward with
+    fp32 rows: per output element the difference stays within the compact
+    format's rounding of every routed row it sums, 2^-11 |O_j| (relative
+    error of one fp16 rounding after an exact power-of-two scale), plus the
+    two fp32 sums' own rounding and fp16 underflow of values far below
+    their group's largest."""
+    cfg = PARITY[name]
+    t = workloads.generate(cfg, seed=3, device="cuda")
+    aux = torch.cuda.Stream()
+    # a separate shared expert: a merged one keeps fp32 rows
+    L32 = new_layer(cfg, out_dtype="f32", rows_format="fp32", shared_mode="separate")
+    Lc = new_layer(cfg, out_dtype="f32", rows_format="compact", shared_mode="separate")
+    y32 = forward(L32, t, aux=aux)
+    yc = forward(Lc, t, aux=aux)
+    d = L32.desc
+    idx, w = run_route(L32, d, t)
+    p = gpu_permute(L32, d, idx)
+    S = cfg.T * cfg.k
+    O = torch.zeros(S * cfg.D, dtype=torch.float32, device="cuda")
+    B.moe_expert_ffn(L32.handle, d, t["x"], p["sorted_token"], p["sorted_slot"], p["offsets"],
+                     w, t["W1"], t["b1"], t["W2"], t["b2"], O, L32.ws)
+    torch.cuda.synchronize()
+    On = np.abs(to_np(O).reshape(S, cfg.D).astype(np.float64))
+    sr = to_np(p["slot_row"]).reshape(cfg.T, cfg.k)
+    tot = np.zeros((cfg.T, cfg.D))
+    rowmax = np.zeros(cfg.T)
+    for j in range(cfg.k):
+        ok = sr[:, j] >= 0
+        tot[ok] += On[sr[ok, j]]
+        rowmax[ok] += On[sr[ok, j]].max(axis=1)
+    a32 = to_np(y32).reshape(cfg.T, cfg.D).astype(np.float64)
+    ac = to_np(yc).reshape(cfg.T, cfg.D).astype(np.float64)
+    allow = (COMPACT_REL * tot + 2 * (cfg.k + 1) * 2.0 ** -24 * (tot + np.abs(a32))
+             + 2.0 ** -38 * rowmax[:, None])
+    err = np.abs(ac - a32)
+    assert np.isfinite(ac).all()
+    worst = float((err - allow).max())
+    assert worst <= 0.0, f"compact rows differ beyond their rounding by {worst:.3e}"
+    # and they are not simply fp32: some element moved
+    assert (err > 0).any()
 
 
 # ------------------------------------------------------------------ edges
