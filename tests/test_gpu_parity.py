@@ -229,6 +229,50 @@ def test_compact_rows_within_fp16_rounding(name):
     assert (err > 0).any()
 
 
+def test_compact_rows_extreme_magnitudes():
+    """Compact rows across the exponent range: experts whose down weights
+    are scaled by 2^40 or 2^-40 (exact in bf16) or zeroed give expert rows
+    from ~1e11 to ~1e-13 and all-zero scale groups in one layer; the
+    compact forward stays within its rounding of the fp32-rows forward."""
+    cfg = PARITY["glm45_small"]
+    t = workloads.generate(cfg, seed=5, device="cuda")
+    W2 = t["W2"].clone().view(cfg.M, cfg.D, cfg.F)
+    e = torch.arange(cfg.M, device="cuda")
+    scale = torch.where(e % 3 == 0, 2.0 ** 40, torch.where(e % 3 == 1, 2.0 ** -40, 1.0))
+    scale = torch.where(e % 7 == 0, 0.0, scale)
+    t["W2"] = (W2.float() * scale[:, None, None]).to(torch.bfloat16).reshape(-1).contiguous()
+    aux = torch.cuda.Stream()
+    outs = {}
+    for rf in ("fp32", "compact"):
+        L = new_layer(cfg, out_dtype="f32", rows_format=rf, shared_mode="separate")
+        outs[rf] = (L, forward(L, t, aux=aux))
+    L32 = outs["fp32"][0]
+    d = L32.desc
+    idx, w = run_route(L32, d, t)
+    p = gpu_permute(L32, d, idx)
+    S = cfg.T * cfg.k
+    O = torch.zeros(S * cfg.D, dtype=torch.float32, device="cuda")
+    B.moe_expert_ffn(L32.handle, d, t["x"], p["sorted_token"], p["sorted_slot"], p["offsets"],
+                     w, t["W1"], t["b1"], t["W2"], t["b2"], O, L32.ws)
+    torch.cuda.synchronize()
+    On = np.abs(to_np(O).reshape(S, cfg.D).astype(np.float64))
+    assert On.max() > 1e9 and On[On > 0].min() < 1e-9, "the layer does not span the range"
+    sr = to_np(p["slot_row"]).reshape(cfg.T, cfg.k)
+    tot = np.zeros((cfg.T, cfg.D))
+    rowmax = np.zeros(cfg.T)
+    for j in range(cfg.k):
+        ok = sr[:, j] >= 0
+        tot[ok] += On[sr[ok, j]]
+        rowmax[ok] += On[sr[ok, j]].max(axis=1)
+    a32 = to_np(outs["fp32"][1]).reshape(cfg.T, cfg.D).astype(np.float64)
+    ac = to_np(outs["compact"][1]).reshape(cfg.T, cfg.D).astype(np.float64)
+    assert np.isfinite(ac).all()
+    allow = (COMPACT_REL * tot + 2 * (cfg.k + 1) * 2.0 ** -24 * (tot + np.abs(a32))
+             + 2.0 ** -38 * rowmax[:, None])
+    worst = float((np.abs(ac - a32) - allow).max())
+    assert worst <= 0.0, f"compact rows differ beyond their rounding by {worst:.3e}"
+
+
 # ------------------------------------------------------------------ edges
 
 # Every bf16 tile height on every GEMM (the library picks one per shape; the
