@@ -58,6 +58,61 @@ def check_route(cfg, idx_g, w_g, idx_o, w_o, gap_o, sel_o):
     return mism
 
 
+def weights_for(cfg, logits, idx):
+    """Gate weights [n, k] of a given expert set idx[n, k] per token from the
+    oracle's fp64 logits[n, M]: the selected gate values (softmax
+    probabilities over all M, GLaM note "Sparse MoE Layer"; sigmoid scores,
+    "Shared Expert" note "How it works") renormalised by their sum plus eps
+    when renorm, times alpha.  Used for tie-exempt tokens, where the GPU may
+    pick another valid set than the oracle."""
+    l = np.asarray(logits, np.float64)
+    if cfg.scorer == "softmax":
+        e = np.exp(l - l.max(axis=1, keepdims=True))
+        g = e / e.sum(axis=1, keepdims=True)
+    else:
+        g = 1.0 / (1.0 + np.exp(-l))
+    gs = np.take_along_axis(g, np.asarray(idx, np.int64), axis=1)
+    if cfg.renorm:
+        return cfg.alpha * gs / (gs.sum(axis=1, keepdims=True) + cfg.eps)
+    return cfg.alpha * gs
+
+
+def check_tie_exempt(cfg, h, mism, idx_g, w_g, y_g, logits_o, idx_o, w_o, scale, what,
+                     plain=True, compact=False):
+    """Tokens whose GPU top-k differs from the oracle's (tie-exempt, gap
+    below TIE_GAP): the oracle's layer on the GPU's own selection, with the
+    gate weights of that selection, must match the GPU's weights within
+    1e-5 * alpha and its output y within the layer's bar (tol * `scale`, the
+    RMS of the whole oracle output), or, with plain=False, per element within
+    the rounding bound of that selection (rounding_bounds) plus SLACK *
+    scale.  Returns the number of tokens checked."""
+    mt = np.nonzero(mism)[0]
+    if mt.size == 0:
+        return 0
+    idx_g = np.asarray(idx_g).reshape(cfg.T, cfg.k)
+    w_g = np.asarray(w_g).reshape(cfg.T, cfg.k)
+    wt = weights_for(cfg, logits_o[mt], idx_g[mt])
+    dw = float(np.abs(w_g[mt].astype(np.float64) - wt).max())
+    assert dw <= 1e-5 * max(cfg.alpha, 1e-30), f"{what}: tie-exempt weights differ by {dw}"
+    idx_a = idx_o.copy()
+    w_a = w_o.copy()
+    idx_a[mt] = idx_g[mt]
+    w_a[mt] = wt
+    y_a = oracle.layer(cfg, h["x"], idx_a, w_a, h["W1"], h["b1"], h["W2"], h["b2"],
+                       h["Wsh_gu"], h["Wsh_dn"], tokens=mt)
+    diff = np.abs(np.asarray(y_g, np.float64)[mt] - y_a)
+    if plain or cfg.dtype != "bf16":
+        err = float(diff.max())
+        assert err <= tol(cfg) * scale, (f"{what}: tie-exempt tokens {mt[:8]} max|err| "
+                                         f"{err:.3e} > {tol(cfg)} * RMS {scale:.3e}")
+    else:
+        bnd, bsh = rounding_bounds(cfg, h, idx_a, w_a, compact=compact)
+        allow = (bnd.sum(axis=1) + (bsh if bsh is not None else 0.0))[mt] + SLACK * scale
+        worst = float((diff - allow).max())
+        assert worst <= 0.0, f"{what}: tie-exempt tokens {mt[:8]} beyond their bound by {worst:.3e}"
+    return int(mt.size)
+
+
 def check_dispatch_props(cfg, idx_g, d):
     """GPU dispatch arrays against numpy's stable argsort of the GPU's own
     indices (a library routine, independent of both implementations)."""

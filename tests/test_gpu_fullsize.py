@@ -19,8 +19,9 @@ import torch
 import oracle
 import workloads
 from tests.gpu_util import (assert_rounded_from, check_float, check_dispatch_props, check_route,
-                            forward, gpu_permute, new_layer, rounding_bounds_tokens, run_route,
-                            tiled_weights, to_np, uses_compact_rows)
+                            check_tie_exempt, forward, gpu_permute, new_layer,
+                            rounding_bounds_tokens, run_route, tiled_weights, to_np,
+                            uses_compact_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -91,7 +92,8 @@ def test_full_size_forward(name, layout):
     gc.collect()
     torch.cuda.empty_cache()
 
-    idx_o, w_o, gap_o, sel_o = oracle.route(cfg, h["x"], h["W_r"], h["bias"], want_sel=True)
+    idx_o, w_o, gap_o, logits_o, sel_o = oracle.route(cfg, h["x"], h["W_r"], h["bias"],
+                                                      want_logits=True, want_sel=True)
     mism = check_route(cfg, idx_gh, w_gh, idx_o, w_o, gap_o, sel_o)
     check_dispatch_props(cfg, idx_gh, pg)
     disp_o = oracle.dispatch(cfg.T, cfg.k, cfg.M, idx_o)
@@ -115,6 +117,12 @@ def test_full_size_forward(name, layout):
                                  "tokens")
     print(f"  fp32 y max|err| {err:.3e}  RMS {scale:.3e}  ratio {err / scale:.2e} on "
           f"{len(toks)} tokens", flush=True)
+    # tie-exempt tokens: the oracle on the GPU's own selection
+    n_tie = check_tie_exempt(cfg, h, mism, idx_gh, w_gh, y32h, logits_o, idx_o, w_o, scale,
+                             f"{cfg.name} fp32 y", plain=name not in GATE_SCALED,
+                             compact=uses_compact_rows(cfg))
+    if n_tie:
+        print(f"  {n_tie} tie-exempt tokens checked on the GPU's selection", flush=True)
     if bf and name in STATED:
         err, scale = check_float(cfg, ybh[toks], y_o, f"{cfg.name} bf16 y on {len(toks)} tokens")
         print(f"  bf16 y max|err| {err:.3e}  ratio {err / scale:.2e}", flush=True)

@@ -24,7 +24,8 @@ import torch
 import oracle
 import workloads
 from tests.gpu_util import (assert_rounded_from, check_dispatch_props, check_float, check_route,
-                            forward, gpu_permute, new_layer, rounding_bounds, run_route,
+                            check_tie_exempt, forward, gpu_permute, new_layer, rounding_bounds,
+                            run_route,
                             tiled_weights, to_np, uses_compact_rows, y_plain)
 
 pytestmark = pytest.mark.gpu
@@ -91,9 +92,11 @@ def test_fuzz_case(case):
         t = tiled_weights(L, t)
 
     idx_g, w_g = run_route(L, L.desc, t)
-    idx_o, w_o, gap_o, sel_o = oracle.route(cfg, h["x"], h["W_r"], h["bias"], want_sel=True)
+    idx_o, w_o, gap_o, logits_o, sel_o = oracle.route(cfg, h["x"], h["W_r"], h["bias"],
+                                                      want_logits=True, want_sel=True)
     idx_gh = to_np(idx_g).reshape(cfg.T, cfg.k)
-    mism = check_route(cfg, idx_gh, to_np(w_g), idx_o, w_o, gap_o, sel_o)
+    w_gh = to_np(w_g)
+    mism = check_route(cfg, idx_gh, w_gh, idx_o, w_o, gap_o, sel_o)
 
     # dispatch with dropped slots, and the combine skipping them
     rng = np.random.default_rng(seed)
@@ -133,6 +136,9 @@ def test_fuzz_case(case):
         bnd, bsh = rounding_bounds(cfg, h, idx_o, w_o, compact=uses_compact_rows(cfg))
         bound = (bnd.sum(axis=1) + (bsh if bsh is not None else 0.0))[keep]
     check_float(cfg, got, y_o[keep], "forward y", bound=bound, plain=wide or not bf)
+    check_tie_exempt(cfg, h, mism, idx_gh, w_gh, to_np(y_f).reshape(cfg.T, cfg.D), logits_o,
+                     idx_o, w_o, float(np.sqrt(np.mean(y_o * y_o))) if y_o.size else 0.0,
+                     "forward y", plain=wide or not bf, compact=uses_compact_rows(cfg))
     if bf:
         Lb = new_layer(cfg, out_dtype="bf16", weight_layout=layout)
         y_b = forward(Lb, t, aux=aux)

@@ -15,7 +15,8 @@ import oracle
 import workloads
 from sparse_mixture_experts_15_amd import binding as B
 from tests.gpu_util import (COMPACT_REL, PLAIN_MIN_WIDTH, assert_rounded_from,
-                            check_dispatch_props, check_float, check_route, dev_i32, forward,
+                            check_dispatch_props, check_float, check_route, check_tie_exempt,
+                            dev_i32, forward,
                             gpu_permute, new_layer, rounding_bounds, run_route, tiled_weights,
                             to_np, uses_compact_rows, y_plain)
 
@@ -70,9 +71,11 @@ def _stage_parity(cfg, seed=0, tiled=False, **tuning):
 
     # router
     idx_g, w_g = run_route(L, d, t)
-    idx_o, w_o, gap_o, sel_o = oracle.route(cfg, h["x"], h["W_r"], h["bias"], want_sel=True)
+    idx_o, w_o, gap_o, logits_o, sel_o = oracle.route(cfg, h["x"], h["W_r"], h["bias"],
+                                                      want_logits=True, want_sel=True)
     idx_gh = to_np(idx_g).reshape(T, k)
-    mism = check_route(cfg, idx_gh, to_np(w_g), idx_o, w_o, gap_o, sel_o)
+    w_gh = to_np(w_g)
+    mism = check_route(cfg, idx_gh, w_gh, idx_o, w_o, gap_o, sel_o)
 
     # dispatch of the GPU's own indices
     pg = {kk: to_np(v) for kk, v in gpu_permute(L, d, idx_g).items()}
@@ -125,6 +128,10 @@ def _stage_parity(cfg, seed=0, tiled=False, **tuning):
         fbnd = ybnd + COMPACT_REL * np.abs(slots_o).sum(axis=1)
     check_float(cfg, to_np(y_f).reshape(T, D)[keep], y_o[keep], "forward y", bound=fbnd[keep],
                 plain=wide)
+    # tie-exempt tokens: the oracle on the GPU's own selection
+    check_tie_exempt(cfg, h, mism, idx_gh, w_gh, to_np(y_f).reshape(T, D), logits_o, idx_o, w_o,
+                     float(np.sqrt(np.mean(y_o * y_o))), "forward y", plain=wide,
+                     compact=uses_compact_rows(cfg))
     if not bf:
         return L, t, y_f
 

@@ -72,3 +72,50 @@ def test_w2_allowance_covers_bf16_roundings(act):
     assert (err <= allow + 1e-3 * rms).all()
     # cancellation across tokens: a bound relative to |dW2| alone fails
     assert (err > 2.0 ** -7 * np.abs(exact) + 1e-3 * rms).any()
+
+
+@pytest.mark.parametrize("scorer,renorm,alpha", [("softmax", True, 1.0), ("sigmoid", True, 2.5),
+                                                 ("sigmoid", False, 1.5),
+                                                 ("softmax", False, 0.7)])
+def test_tie_weights_helper_matches_the_oracle(scorer, renorm, alpha):
+    """The helper that weights a tie-exempt token's alternative expert set
+    reproduces the oracle's own weights on the oracle's own selection."""
+    import oracle
+    import workloads
+    from tests.gpu_util import weights_for
+    cfg = workloads.shrink(workloads.GLM45_PREFILL, T=40, D=64, F=16, F_shared=0).replace(
+        scorer=scorer, renorm=renorm, alpha=alpha, M=24, k=4)
+    h = workloads.host_inputs(workloads.generate(cfg, seed=7, device="cpu"))
+    idx, w, _, logits = oracle.route(cfg, h["x"], h["W_r"], h["bias"], want_logits=True)
+    got = weights_for(cfg, logits, idx)
+    assert np.allclose(got, w, rtol=1e-12, atol=1e-15 * alpha)
+
+
+def test_tie_exempt_check_accepts_the_alternative_and_catches_errors():
+    """check_tie_exempt on a planted alternative selection: one token's k-th
+    expert swapped for its (k+1)-th, the output computed by the oracle on
+    that selection, passes; the same with a 5% error in that token fails."""
+    import oracle
+    import workloads
+    from tests.gpu_util import check_tie_exempt, weights_for
+    cfg = workloads.shrink(workloads.GLM45_PREFILL, T=24, D=64, F=32, F_shared=32).replace(
+        M=16, k=4)
+    h = workloads.host_inputs(workloads.generate(cfg, seed=3, device="cpu"))
+    idx_o, w_o, _, logits, sel = oracle.route(cfg, h["x"], h["W_r"], h["bias"],
+                                              want_logits=True, want_sel=True)
+    t0 = 5
+    order = np.lexsort((np.arange(cfg.M), -sel[t0]))   # best first, lower index on ties
+    alt = np.sort(np.concatenate([order[:cfg.k - 1], order[cfg.k:cfg.k + 1]]))
+    idx_g = idx_o.copy()
+    idx_g[t0] = alt
+    w_g = weights_for(cfg, logits, idx_g).astype(np.float32)
+    y_g = oracle.layer(cfg, h["x"], idx_g, w_g.astype(np.float64), h["W1"], h["b1"], h["W2"],
+                       h["b2"], h["Wsh_gu"], h["Wsh_dn"])
+    mism = np.zeros(cfg.T, bool)
+    mism[t0] = True
+    scale = float(np.sqrt(np.mean(y_g ** 2)))
+    assert check_tie_exempt(cfg, h, mism, idx_g, w_g, y_g, logits, idx_o, w_o, scale, "t") == 1
+    bad = y_g.copy()
+    bad[t0, 3] += 0.05 * scale
+    with pytest.raises(AssertionError):
+        check_tie_exempt(cfg, h, mism, idx_g, w_g, bad, logits, idx_o, w_o, scale, "t")
