@@ -291,7 +291,8 @@ __device__ __forceinline__ void dh_epilogue(const GemmArgs& g, const Tile& tl,
 template <int EPI, int TM, int TN, int WROWS>
 __device__ __forceinline__ void out_epilogue(const GemmArgs& g, const Tile& tl,
                                              const floatx4 (&acc)[TM][TN], int wlive, int wm,
-                                             int wn, int n_base, int kg, int kc_id, int lane) {
+                                             int wn, int n_base, int kg, int kc_id, int lane,
+                                             const float (&wpre)[TM]) {
     const int N = g.N;
     const int lr = lane & 15, lc = 4 * (lane >> 4);
     const bf16_t* bias = static_cast<const bf16_t*>(g.bias);
@@ -301,6 +302,7 @@ __device__ __forceinline__ void out_epilogue(const GemmArgs& g, const Tile& tl,
     constexpr int OUT_FR = epi_pairs(EPI) ? TN / 2 : TN;   // output fragments per row
     constexpr int OUT_W = epi_pairs(EPI) ? 32 : 64;        // output columns per wave
     const bool vec = (N % 4) == 0;                              // aligned 4-column groups
+    const bool HAS_BIAS_RT = HAS_BIAS && bias != nullptr;
     float bv[OUT_FR][4];
 #pragma unroll
     for (int j = 0; j < OUT_FR; ++j) {
@@ -316,7 +318,7 @@ __device__ __forceinline__ void out_epilogue(const GemmArgs& g, const Tile& tl,
         const int64_t r = tl.r0 + wm * WROWS + 16 * i + lr;
         if (r >= tl.rend) continue;
         float wr = 1.f;
-        if (EPI == EPI_DOWN_SCALED) wr = g.row_w[r];
+        if (EPI == EPI_DOWN_SCALED) wr = wpre[i];
         if constexpr (EPI == EPI_DOWN_SCALED) {
             if (g.c16) {
                 // compact rows: the four lanes holding this row's 64 columns
@@ -326,32 +328,94 @@ __device__ __forceinline__ void out_epilogue(const GemmArgs& g, const Tile& tl,
                 // rounded once to fp16
                 static_assert(OUT_W == kRowGroup, "one scale per wave row segment");
                 const int G = (N + kRowGroup - 1) / kRowGroup;
-                float v[OUT_FR][4];
-                float m = 0.f;
+                const int n0 = n_base + OUT_W * wn;
+                // every column of this wave's segment exists (wave-uniform)
+                const bool full = vec && n0 + OUT_W <= N;
+                if (full && !HAS_BIAS_RT) {
+                    // Whole segment, no bias: the largest |wr a| is |wr| times
+                    // the largest |a| (rounding is monotonic), and wr a 2^-e
+                    // rounds to (wr 2^-e) a exactly while wr 2^-e stays a
+                    // normal float, so one scaled weight serves the segment
+                    // with the general path's bits (except products below
+                    // the fp32 normal range, rounded once here, twice there).
+                    float ma = 0.f;
 #pragma unroll
-                for (int j = 0; j < OUT_FR; ++j) {
-                    const int n = n_base + OUT_W * wn + 16 * j + lc;
+                    for (int j = 0; j < OUT_FR; ++j)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        v[j][q] = n + q < N ? wr * (acc[i][j][q] + bv[j][q]) : 0.f;
-                        const float a = fabsf(v[j][q]);
-                        if (a <= 3.402823466e38f) m = fmaxf(m, a);   // finite values only
+                        for (int q = 0; q < 4; ++q) ma = fmaxf(ma, fabsf(acc[i][j][q]));
+                    ma = fmaxf(ma, __shfl_xor(ma, 16));
+                    ma = fmaxf(ma, __shfl_xor(ma, 32));
+                    const float mw = fabsf(wr) * ma;
+                    const int bw = (int)((__float_as_uint(mw) >> 23) & 0xffu);
+                    const int ew = min(max(bw - 127 - 14, -128), 113);
+                    const float sw = ldexpf(wr, -ew);
+                    const float asw = fabsf(sw);
+                    // uniform over the four lanes: same row, same maximum
+                    if (mw <= 3.402823466e38f &&
+                        (sw == 0.f || (asw >= 1.175494351e-38f && asw <= 3.402823466e38f))) {
+#pragma unroll
+                        for (int j = 0; j < OUT_FR; ++j) {
+                            const int n = n0 + 16 * j + lc;
+                            uint2 pk;
+                            pk.x = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sw * acc[i][j][0])) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sw * acc[i][j][1])) << 16);
+                            pk.y = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sw * acc[i][j][2])) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sw * acc[i][j][3])) << 16);
+                            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.c16) + r * N + n) = pk;
+                        }
+                        if (lc == 0) g.cexp[r * G + n0 / kRowGroup] = (int8_t)ew;
+                        continue;
                     }
                 }
+                float v[OUT_FR][4];
+                float m = 0.f;
+                if (full && !HAS_BIAS_RT) {
+#pragma unroll
+                    for (int j = 0; j < OUT_FR; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            v[j][q] = wr * acc[i][j][q];
+                            m = fmaxf(m, fabsf(v[j][q]));
+                        }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < OUT_FR; ++j) {
+                        const int n = n0 + 16 * j + lc;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            v[j][q] = n + q < N ? wr * (acc[i][j][q] + bv[j][q]) : 0.f;
+                            m = fmaxf(m, fabsf(v[j][q]));
+                        }
+                    }
+                }
+                // fmaxf skips NaNs; an infinity would set the scale, so then
+                // the maximum is taken again over the finite values only
                 m = fmaxf(m, __shfl_xor(m, 16));
                 m = fmaxf(m, __shfl_xor(m, 32));
+                if (!(m <= 3.402823466e38f)) {   // uniform over the four lanes
+                    m = 0.f;
+#pragma unroll
+                    for (int j = 0; j < OUT_FR; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float a = fabsf(v[j][q]);
+                            if (a <= 3.402823466e38f) m = fmaxf(m, a);
+                        }
+                    m = fmaxf(m, __shfl_xor(m, 16));
+                    m = fmaxf(m, __shfl_xor(m, 32));
+                }
                 const int be = (int)((__float_as_uint(m) >> 23) & 0xffu);   // biased exponent
                 const int e = min(max(be - 127 - 14, -128), 113);
 #pragma unroll
                 for (int j = 0; j < OUT_FR; ++j) {
-                    const int n = n_base + OUT_W * wn + 16 * j + lc;
-                    if (n >= N) continue;
+                    const int n = n0 + 16 * j + lc;
+                    if (!full && n >= N) continue;
                     uint16_t hv[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
                         hv[q] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(v[j][q], -e));
                     uint16_t* dst = static_cast<uint16_t*>(g.c16) + r * N + n;
-                    if (vec && n + 4 <= N) {
+                    if (full || (vec && n + 4 <= N)) {
                         uint2 pk;
                         pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
                         pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
@@ -362,7 +426,6 @@ __device__ __forceinline__ void out_epilogue(const GemmArgs& g, const Tile& tl,
                             if (n + q < N) dst[q] = hv[q];
                     }
                 }
-                const int n0 = n_base + OUT_W * wn;
                 if (lc == 0 && n0 < N) g.cexp[r * G + n0 / kRowGroup] = (int8_t)e;
                 continue;
             }
@@ -695,6 +758,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     // MFMAs (wave-uniform branches).
     const int valid_rows = (int)min<int64_t>(tl.rend - tl.r0, (int64_t)BM);
     const int wlive = min(TM, max(0, (valid_rows - wm * WROWS + 15) / 16));
+    // the down projection's row weights, loaded before the K loop so that
+    // their latency hides behind the first stage's
+    float wpre[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int64_t r = tl.r0 + wm * WROWS + 16 * i + (lane & 15);
+        wpre[i] = (EPI == EPI_DOWN_SCALED && i < wlive && r < tl.rend) ? g.row_w[r] : 1.f;
+    }
 
     // STAGES-deep ring: stages kt+1 .. kt+STAGES-1 load while stage kt is
     // multiplied.  With split-K this workgroup runs stages [k_first, k_last).
@@ -802,7 +873,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
     if constexpr (EPI == EPI_DH_SWIGLU || EPI == EPI_DH_GELU) {
         dh_epilogue<EPI, TM, TN, WROWS, WN>(g, tl, acc, wlive, wm, wn, n_base, nt, lane);
     } else {
-        out_epilogue<EPI, TM, TN, WROWS>(g, tl, acc, wlive, wm, wn, n_base, kg, kc_id, lane);
+        out_epilogue<EPI, TM, TN, WROWS>(g, tl, acc, wlive, wm, wn, n_base, kg, kc_id, lane,
+                                          wpre);
     }
 }
 
