@@ -103,6 +103,18 @@ def calib_copy():
                       "gemm_source_hash": gemm_source_hash()}), flush=True)
 
 
+def routing_stats(counts):
+    """Rows per reached expert of the realised routing: how many experts were
+    reached, and the min / median / max and coefficient of variation of their
+    row counts (the skew that sets the grouped GEMMs' partial tiles)."""
+    import numpy as np
+    c = np.asarray([x for x in counts if x > 0], dtype=np.float64)
+    if c.size == 0:
+        return {"reached": 0}
+    return {"reached": int(c.size), "rows_min": int(c.min()), "rows_median": float(np.median(c)),
+            "rows_max": int(c.max()), "rows_cv": round(float(c.std() / c.mean()), 4)}
+
+
 def kernel_work(cfg, counts):
     """Algorithmic FLOPs and HBM bytes per launch of each kernel, from the
     layer shape and the realised per-expert counts.  Bytes are the layer's
@@ -477,6 +489,9 @@ def main():
         "kernel_ms_per_step": {k: round(v, 4) for k, v in split.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "routing": routing_stats(counts),
+        "env": {"device": torch.cuda.get_device_name(0), "torch": torch.__version__,
+                "hip": torch.version.hip, "gemm_source_hash": gemm_source_hash()},
     }
     print(json.dumps(out), flush=True)
 

@@ -81,3 +81,11 @@ def test_default_workload_is_the_glm45_prefill_layer():
     src = open(os.path.join(ROOT, "bench.py")).read()
     assert 'ap.add_argument("--config", default="glm45")' in src
     assert workloads.get("glm45").name == "glm45_t8192_d5120_m160_f1536"
+
+
+def test_routing_stats_of_reached_experts():
+    s = bench.routing_stats([0, 4, 0, 2, 6])
+    assert s["reached"] == 3 and s["rows_min"] == 2 and s["rows_max"] == 6
+    assert s["rows_median"] == 4.0
+    assert s["rows_cv"] == pytest.approx(1.632993 / 4, abs=1e-4)   # population std / mean
+    assert bench.routing_stats([0, 0]) == {"reached": 0}
