@@ -281,6 +281,37 @@ __device__ __forceinline__ void dh_epilogue(const GemmArgs& g, const Tile& tl,
     }
 }
 
+// Packed halves of two output fragments (f0, f1) of a wave row -> one
+// 16-byte piece per lane.  Lane l holds columns 4 c .. 4 c + 3 (c = l / 16)
+// of each fragment; v_permlane16_swap trades the odd 16-lane rows of its
+// first operand for the even rows of its second, so a lane with c even keeps
+// its own f0 columns and receives the next four from lane l + 16, and a lane
+// with c odd keeps its own f1 columns and receives the four before them from
+// lane l - 16.  The piece starts at column 4 c (c even) or 16 + 4 (c - 1) (c
+// odd) of the pair, so the four lanes of a row cover its 32 columns with
+// 64 contiguous bytes (fp16 / bf16), half the store instructions.
+__device__ __forceinline__ uint4 pair_to_piece(uint32_t x0, uint32_t y0, uint32_t x1,
+                                               uint32_t y1) {
+    const auto sx = __builtin_amdgcn_permlane16_swap(x0, x1, false, false);
+    const auto sy = __builtin_amdgcn_permlane16_swap(y0, y1, false, false);
+    return uint4{sx[0], sy[0], sx[1], sy[1]};
+}
+__device__ __forceinline__ int piece_col(int lane) {
+    return 4 * (lane >> 4) + 12 * ((lane >> 4) & 1);
+}
+
+// Largest value over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes
+// holding one fragment row).  Each swap hands every lane its partner's value
+// beside its own, in VALU instructions rather than LDS-routed permutes.
+__device__ __forceinline__ float row_max4(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Epilogue of the forward and save epilogues, straight from registers.  The
 // MFMAs take the B fragment as their first operand, so for fragment (i, j)
 // lane l holds tile row 16 i + l % 16 of its wave and the four consecutive
@@ -343,8 +374,7 @@ __device__ __forceinline__ void out_epilogue(const GemmArgs& g, const Tile& tl,
                     for (int j = 0; j < OUT_FR; ++j)
 #pragma unroll
                         for (int q = 0; q < 4; ++q) ma = fmaxf(ma, fabsf(acc[i][j][q]));
-                    ma = fmaxf(ma, __shfl_xor(ma, 16));
-                    ma = fmaxf(ma, __shfl_xor(ma, 32));
+                    ma = row_max4(ma);
                     const float mw = fabsf(wr) * ma;
                     const int bw = (int)((__float_as_uint(mw) >> 23) & 0xffu);
                     const int ew = min(max(bw - 127 - 14, -128), 113);
@@ -353,6 +383,24 @@ __device__ __forceinline__ void out_epilogue(const GemmArgs& g, const Tile& tl,
                     // uniform over the four lanes: same row, same maximum
                     if (mw <= 3.402823466e38f &&
                         (sw == 0.f || (asw >= 1.175494351e-38f && asw <= 3.402823466e38f))) {
+                        if ((N % 8) == 0) {   // 16-byte aligned rows: paired pieces
+                            uint32_t px[OUT_FR], py[OUT_FR];
+#pragma unroll
+                            for (int j = 0; j < OUT_FR; ++j) {
+                                px[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sw * acc[i][j][0])) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sw * acc[i][j][1])) << 16);
+                                py[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sw * acc[i][j][2])) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sw * acc[i][j][3])) << 16);
+                            }
+                            const int pc = piece_col(lane);
+#pragma unroll
+                            for (int h = 0; h < OUT_FR / 2; ++h)
+                                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.c16) + r * N + n0 +
+                                                          32 * h + pc) =
+                                    pair_to_piece(px[2 * h], py[2 * h], px[2 * h + 1], py[2 * h + 1]);
+                            if (lc == 0) g.cexp[r * G + n0 / kRowGroup] = (int8_t)ew;
+                            continue;
+                        }
 #pragma unroll
                         for (int j = 0; j < OUT_FR; ++j) {
                             const int n = n0 + 16 * j + lc;
@@ -390,8 +438,7 @@ __device__ __forceinline__ void out_epilogue(const GemmArgs& g, const Tile& tl,
                 }
                 // fmaxf skips NaNs; an infinity would set the scale, so then
                 // the maximum is taken again over the finite values only
-                m = fmaxf(m, __shfl_xor(m, 16));
-                m = fmaxf(m, __shfl_xor(m, 32));
+                m = row_max4(m);
                 if (!(m <= 3.402823466e38f)) {   // uniform over the four lanes
                     m = 0.f;
 #pragma unroll
@@ -401,8 +448,7 @@ __device__ __forceinline__ void out_epilogue(const GemmArgs& g, const Tile& tl,
                             const float a = fabsf(v[j][q]);
                             if (a <= 3.402823466e38f) m = fmaxf(m, a);
                         }
-                    m = fmaxf(m, __shfl_xor(m, 16));
-                    m = fmaxf(m, __shfl_xor(m, 32));
+                    m = row_max4(m);
                 }
                 const int be = (int)((__float_as_uint(m) >> 23) & 0xffu);   // biased exponent
                 const int e = min(max(be - 127 - 14, -128), 113);
@@ -427,6 +473,32 @@ __device__ __forceinline__ void out_epilogue(const GemmArgs& g, const Tile& tl,
                     }
                 }
                 if (lc == 0 && n0 < N) g.cexp[r * G + n0 / kRowGroup] = (int8_t)e;
+                continue;
+            }
+        }
+        if constexpr (OUT_BF16 && !SAVE) {
+            // whole bf16 segment on 16-byte aligned rows: paired pieces
+            const int nw = n_base + OUT_W * wn;
+            if ((N % 8) == 0 && nw + OUT_W <= N) {
+                uint32_t px[OUT_FR], py[OUT_FR];
+#pragma unroll
+                for (int j = 0; j < OUT_FR; ++j) {
+                    float v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if constexpr (EPI == EPI_SWIGLU)
+                            v[q] = silu_f32(acc[i][j][q]) * acc[i][j + 2][q];
+                        else
+                            v[q] = gelu_erf_f32(acc[i][j][q] + bv[j][q]);
+                    }
+                    px[j] = pack_bf16x2(v[0], v[1]);
+                    py[j] = pack_bf16x2(v[2], v[3]);
+                }
+                const int pc = piece_col(lane);
+#pragma unroll
+                for (int h = 0; h < OUT_FR / 2; ++h)
+                    *reinterpret_cast<uint4*>(static_cast<bf16_t*>(g.c) + r * N + nw + 32 * h + pc) =
+                        pair_to_piece(px[2 * h], py[2 * h], px[2 * h + 1], py[2 * h + 1]);
                 continue;
             }
         }
@@ -869,7 +941,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
         kloop(body_general);
     }
 
-    // Epilogue straight from registers (out_epilogue / dh_epilogue).
+    // Epilogue straight from registers (out_epilogue / dh_epilogue).  Every
+    // load has landed by now, so this wait costs nothing; without it the
+    // compiler cannot prove that the row weights loaded before the K loop
+    // have arrived and waits for all memory operations at each one's first
+    // use, which also drains the stores of the previous fragment rows.
+    wait_vmcnt<0>();
     if constexpr (EPI == EPI_DH_SWIGLU || EPI == EPI_DH_GELU) {
         dh_epilogue<EPI, TM, TN, WROWS, WN>(g, tl, acc, wlive, wm, wn, n_base, nt, lane);
     } else {
