@@ -68,6 +68,14 @@ __device__ __forceinline__ void topk_epilogue_nj(const float* lrow, int M, int k
     const int lane = threadIdx.x & 63;
     double sel[NJ];
     double mx = -INFINITY;
+    // the bias loads all go out before the first score is formed
+    float bj[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bj[j] = 0.f;
+    if (scorer != 0 && bias) {   // uniform; lanes past M re-read a valid entry
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bj[j] = bias[min(lane + 64 * j, M - 1)];
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int e = lane + 64 * j;
@@ -79,7 +87,7 @@ __device__ __forceinline__ void topk_epilogue_nj(const float* lrow, int M, int k
                 mx = fmax(mx, l);
             } else {
                 const double s = 1.0 / (1.0 + exp(-l));
-                sel[j] = s + (bias ? (double)bias[e] : 0.0);
+                sel[j] = s + (double)bj[j];
             }
             // a NaN score ranks last, so k valid experts are always chosen
             if (sel[j] != sel[j]) sel[j] = -INFINITY;
@@ -293,17 +301,43 @@ __global__ __launch_bounds__(256) void route_topk_partials(
     if (t >= T) return;   // whole wave leaves; no block barrier follows
     float* lrow = s_logit + wave * M;
     const int64_t ld = 3 * (int64_t)M;
-    for (int e = lane; e < M; e += 64) {
-        float h = 0.f, m = 0.f, l = 0.f;
-        for (int z = 0; z < nK; ++z) {
-            const float* row = P + ((int64_t)z * T + t) * ld;
-            h += row[e];
-            m += row[M + e];
-            l += row[2 * M + e];
+    // Two experts per lane and two K chunks per round have all their loads
+    // in flight before the first sum; each plane still sums its chunks in
+    // chunk order, then the planes as h + (m + l).
+    for (int e0 = lane; e0 < M; e0 += 128) {
+        float h[2] = {0.f, 0.f}, m[2] = {0.f, 0.f}, l[2] = {0.f, 0.f};
+        for (int z0 = 0; z0 < nK; z0 += 2) {
+            float hv[2][2], mv[2][2], lv[2][2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const float* row = P + ((int64_t)min(z0 + q, nK - 1) * T + t) * ld;
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int e = min(e0 + 64 * u, M - 1);
+                    hv[q][u] = row[e];
+                    mv[q][u] = row[M + e];
+                    lv[q][u] = row[2 * M + e];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                if (z0 + q >= nK) continue;
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    h[u] += hv[q][u];
+                    m[u] += mv[q][u];
+                    l[u] += lv[q][u];
+                }
+            }
         }
-        const float v = h + (m + l);
-        lrow[e] = v;
-        L[(int64_t)t * M + e] = v;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = e0 + 64 * u;
+            if (e >= M) continue;
+            const float v = h[u] + (m[u] + l[u]);
+            lrow[e] = v;
+            L[(int64_t)t * M + e] = v;
+        }
     }
     // the wave's own LDS row: make the writes visible across lanes
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
