@@ -27,8 +27,15 @@ __global__ __launch_bounds__(kPermBlock) void perm_count(const int32_t* __restri
     __syncthreads();
     const int t = blockIdx.x * kPermBlock + threadIdx.x;
     if (t < T) {
-        for (int j = 0; j < k; ++j) {
-            const int e = idx[(int64_t)t * k + j];
+        // all of the token's indices are loaded before the first atomic
+        int ev[kMaxK];
+        const int32_t* it = idx + (int64_t)t * k;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) ev[j] = j < k ? it[j] : -1;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j >= k) break;
+            const int e = ev[j];
             if (e >= 0 && e < M) atomicAdd(&s_cnt[e], 1);
         }
     }
@@ -51,11 +58,18 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan(int32_t* __restrict__ 
     // per expert: exclusive running sum over blocks, in block order
     for (int e = tid; e < M; e += kScanThreads) {
         int32_t run = 0;
-        for (int b = 0; b < nblk; ++b) {
-            int32_t* p = hist + (int64_t)b * M + e;
-            const int32_t v = *p;
-            *p = run;
-            run += v;
+        // eight blocks' counts are loaded before any is overwritten (the
+        // clamped index re-reads the last block, not yet overwritten)
+        for (int b0 = 0; b0 < nblk; b0 += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = hist[(int64_t)min(b0 + q, nblk - 1) * M + e];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if (b0 + q >= nblk) break;
+                hist[(int64_t)(b0 + q) * M + e] = run;
+                run += v[q];
+            }
         }
         counts[e] = run;
         s_tot[e] = run;
@@ -101,14 +115,18 @@ __global__ __launch_bounds__(kPermBlock) void perm_scatter(
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) e_of[j] = -1;
     if (t < T) {
+        // all of the token's indices are loaded before the first atomic
+        int ev[kMaxK];
+        const int32_t* it = idx + (int64_t)t * k;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) ev[j] = j < k ? it[j] : -1;
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j) {
-            if (j < k) {
-                const int e = idx[(int64_t)t * k + j];
-                if (e >= 0 && e < M) {
-                    e_of[j] = e;
-                    atomicOr(&s_mask[wv * M + e], 1ull << lane);
-                }
+            if (j >= k) break;
+            const int e = ev[j];
+            if (e >= 0 && e < M) {
+                e_of[j] = e;
+                atomicOr(&s_mask[wv * M + e], 1ull << lane);
             }
         }
     }
@@ -157,14 +175,18 @@ __global__ __launch_bounds__(kScanThreads) void perm_small(const int32_t* __rest
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) e_of[j] = -1;
     if (t < T) {
+        // all of the token's indices are loaded before the first atomic
+        int ev[kMaxK];
+        const int32_t* it = idx + (int64_t)t * k;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) ev[j] = j < k ? it[j] : -1;
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j) {
-            if (j < k) {
-                const int e = idx[(int64_t)t * k + j];
-                if (e >= 0 && e < M) {
-                    e_of[j] = e;
-                    atomicOr(&s_mask[wv * M + e], 1ull << lane);
-                }
+            if (j >= k) break;
+            const int e = ev[j];
+            if (e >= 0 && e < M) {
+                e_of[j] = e;
+                atomicOr(&s_mask[wv * M + e], 1ull << lane);
             }
         }
     }
