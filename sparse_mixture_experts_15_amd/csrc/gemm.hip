@@ -198,6 +198,48 @@ __device__ __forceinline__ bool tile_coords(int m_tiles, int n_tiles, int group_
     return true;
 }
 
+// Packed halves of two output fragments (f0, f1) of a wave row -> one
+// 16-byte piece per lane.  Lane l holds columns 4 c .. 4 c + 3 (c = l / 16)
+// of each fragment; v_permlane16_swap trades the odd 16-lane rows of its
+// first operand for the even rows of its second, so a lane with c even keeps
+// its own f0 columns and receives the next four from lane l + 16, and a lane
+// with c odd keeps its own f1 columns and receives the four before them from
+// lane l - 16.  The piece starts at column 4 c (c even) or 16 + 4 (c - 1) (c
+// odd) of the pair, so the four lanes of a row cover its 32 columns with
+// 64 contiguous bytes (fp16 / bf16), half the store instructions.
+__device__ __forceinline__ uint4 pair_to_piece(uint32_t x0, uint32_t y0, uint32_t x1,
+                                               uint32_t y1) {
+    const auto sx = __builtin_amdgcn_permlane16_swap(x0, x1, false, false);
+    const auto sy = __builtin_amdgcn_permlane16_swap(y0, y1, false, false);
+    return uint4{sx[0], sy[0], sx[1], sy[1]};
+}
+__device__ __forceinline__ int piece_col(int lane) {
+    return 4 * (lane >> 4) + 12 * ((lane >> 4) & 1);
+}
+
+// Largest value over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes
+// holding one fragment row).  Each swap hands every lane its partner's value
+// beside its own, in VALU instructions rather than LDS-routed permutes.
+__device__ __forceinline__ float row_max4(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Sum over the same four lanes, each pair added as x + (partner's x): the
+// values and rounding of the two __shfl_xor steps it replaces.
+__device__ __forceinline__ float row_sum4(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t w = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Backward epilogue of the down projection's input gradient (EPI_DH_*): the
 // accumulator is dH_raw = dy . W2[e] for sorted row r and output column n
 // (an expert-width column).  With the row's gate weight w (row_w, or 1 for
@@ -217,6 +259,87 @@ __device__ __forceinline__ void dh_epilogue(const GemmArgs& g, const Tile& tl,
     const bf16_t* hp = static_cast<const bf16_t*>(g.aux);
     bf16_t* out = static_cast<bf16_t*>(g.c);
     const bool vec = (N % 4) == 0;   // 8-byte aligned 4-column groups
+    const int nw = n_base + 64 * wn;
+    if (TN == 4 && (N % 8) == 0 && nw + 64 <= N) {
+        // The wave's whole 64-column segment on 16-byte aligned rows.  Each
+        // row's weight, pre-activations and H are loaded before the previous
+        // row's outputs are stored (its inputs are spent by then), so a load
+        // never waits behind those stores (memory operations retire in
+        // order); outputs go out as paired 16-byte pieces.  Same arithmetic
+        // as the general path below.
+        constexpr bool SW = EPI == EPI_DH_SWIGLU;
+        const int64_t ldz = SW ? 2 * (int64_t)N : (int64_t)N;
+        const int64_t rlast = (int64_t)tl.rend - 1;
+        uint2 zg[TN], zu[TN], hh[TN];
+        float wnext = 1.f;
+        auto load_row = [&](int i) {   // rows past the tile re-read its last row
+            const int64_t r = min(tl.r0 + wm * WROWS + 16 * i + lr, rlast);
+            wnext = g.row_w ? g.row_w[r] : 1.f;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int n = nw + 16 * j + lc;
+                zg[j] = *reinterpret_cast<const uint2*>(zp + r * ldz + n);
+                if constexpr (SW) zu[j] = *reinterpret_cast<const uint2*>(zp + r * ldz + N + n);
+                hh[j] = hp ? *reinterpret_cast<const uint2*>(hp + r * N + n) : uint2{0u, 0u};
+            }
+        };
+        if (wlive > 0) load_row(0);
+        const int pc = piece_col(lane);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            if (i >= wlive) continue;   // wave-uniform
+            const int64_t r = tl.r0 + wm * WROWS + 16 * i + lr;
+            const bool rv = r < tl.rend;
+            const float wr = wnext;
+            float pw = 0.f;
+            uint32_t ox[2][TN], oy[2][TN];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const float hv[4] = {__uint_as_float(hh[j].x << 16),
+                                     __uint_as_float(hh[j].x & 0xffff0000u),
+                                     __uint_as_float(hh[j].y << 16),
+                                     __uint_as_float(hh[j].y & 0xffff0000u)};
+                const float z0[4] = {__uint_as_float(zg[j].x << 16),
+                                     __uint_as_float(zg[j].x & 0xffff0000u),
+                                     __uint_as_float(zg[j].y << 16),
+                                     __uint_as_float(zg[j].y & 0xffff0000u)};
+                float o[2][4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float a = acc[i][j][q];
+                    if (hp) pw += hv[q] * a;
+                    if constexpr (SW) {
+                        const float dh = wr * a;
+                        const uint32_t uw = (q < 2) ? zu[j].x : zu[j].y;
+                        const float up = __uint_as_float((q & 1) ? (uw & 0xffff0000u) : (uw << 16));
+                        o[0][q] = dh * up * silu_grad_f32(z0[q]);
+                        o[1][q] = dh * silu_f32(z0[q]);
+                    } else {
+                        o[0][q] = wr * a * gelu_grad_f32(z0[q]);
+                    }
+                }
+#pragma unroll
+                for (int h = 0; h < (SW ? 2 : 1); ++h) {
+                    ox[h][j] = pack_bf16x2(o[h][0], o[h][1]);
+                    oy[h][j] = pack_bf16x2(o[h][2], o[h][3]);
+                }
+            }
+            if (i + 1 < wlive) load_row(i + 1);
+#pragma unroll
+            for (int h = 0; h < (SW ? 2 : 1); ++h) {
+#pragma unroll
+                for (int pp = 0; pp < TN / 2; ++pp) {
+                    const uint4 piece = pair_to_piece(ox[h][2 * pp], oy[h][2 * pp],
+                                                      ox[h][2 * pp + 1], oy[h][2 * pp + 1]);
+                    if (rv)
+                        *reinterpret_cast<uint4*>(out + r * ldz + h * N + nw + 32 * pp + pc) = piece;
+                }
+            }
+            pw = row_sum4(pw);
+            if (rv && g.part && lane < 16) g.part[r * g.part_ld + nt * WN + wn] = pw;
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         if (i >= wlive) continue;   // wave-uniform
@@ -279,37 +402,6 @@ __device__ __forceinline__ void dh_epilogue(const GemmArgs& g, const Tile& tl,
         pw += __shfl_xor(pw, 32);
         if (rv && g.part && lane < 16) g.part[r * g.part_ld + nt * WN + wn] = pw;
     }
-}
-
-// Packed halves of two output fragments (f0, f1) of a wave row -> one
-// 16-byte piece per lane.  Lane l holds columns 4 c .. 4 c + 3 (c = l / 16)
-// of each fragment; v_permlane16_swap trades the odd 16-lane rows of its
-// first operand for the even rows of its second, so a lane with c even keeps
-// its own f0 columns and receives the next four from lane l + 16, and a lane
-// with c odd keeps its own f1 columns and receives the four before them from
-// lane l - 16.  The piece starts at column 4 c (c even) or 16 + 4 (c - 1) (c
-// odd) of the pair, so the four lanes of a row cover its 32 columns with
-// 64 contiguous bytes (fp16 / bf16), half the store instructions.
-__device__ __forceinline__ uint4 pair_to_piece(uint32_t x0, uint32_t y0, uint32_t x1,
-                                               uint32_t y1) {
-    const auto sx = __builtin_amdgcn_permlane16_swap(x0, x1, false, false);
-    const auto sy = __builtin_amdgcn_permlane16_swap(y0, y1, false, false);
-    return uint4{sx[0], sy[0], sx[1], sy[1]};
-}
-__device__ __forceinline__ int piece_col(int lane) {
-    return 4 * (lane >> 4) + 12 * ((lane >> 4) & 1);
-}
-
-// Largest value over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes
-// holding one fragment row).  Each swap hands every lane its partner's value
-// beside its own, in VALU instructions rather than LDS-routed permutes.
-__device__ __forceinline__ float row_max4(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const uint32_t w = __float_as_uint(x);
-    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Epilogue of the forward and save epilogues, straight from registers.  The
