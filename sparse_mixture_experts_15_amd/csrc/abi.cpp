@@ -319,14 +319,38 @@ int do_route(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, con
     });
 }
 
+// The expert GEMMs' tile tables of this plan (up and down tile heights).
+TileTables tile_tables(const Plan& p, void* ws, int* ntables) {
+    int32_t* tiles_up = at<int32_t>(ws, p.tiles_up);
+    int32_t* tiles_dn = at<int32_t>(ws, p.tiles_dn);
+    *ntables = tiles_dn == tiles_up ? 1 : 2;
+    return TileTables{{p.bm_up, p.bm_dn},
+                      {(int)p.max_tiles_up, (int)p.max_tiles_dn},
+                      {tiles_up, tiles_dn}};
+}
+
+// With w non-null (moe_forward on a batch of at most kSmallT tokens) the
+// one-workgroup dispatch also builds the tile tables and row scales that
+// do_expert_ffn would otherwise build in a launch of its own (`extra`: the
+// merged shared expert's rows); *tables_built reports it.
 int do_permute(moe_handle* h, const moe_desc* d, const Plan& p, const int32_t* idx,
                int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* sorted_slot,
-               int32_t* slot_row, void* ws, hipStream_t s) {
-    if (d->T <= kSmallT)
-        return run(h, s, L_PERM_SCATTER, [&] {
+               int32_t* slot_row, void* ws, hipStream_t s, const float* w = nullptr,
+               int64_t extra = 0, bool* tables_built = nullptr) {
+    if (tables_built) *tables_built = false;
+    if (d->T <= kSmallT) {
+        int ntables = 0;
+        TileTables tt{};
+        if (w) tt = tile_tables(p, ws, &ntables);
+        float* row_scale = w ? at<float>(ws, p.row_scale) : nullptr;
+        TRY(run(h, s, L_PERM_SCATTER, [&] {
             return launch_perm_small(s, idx, d->T, d->k, d->M, counts, offsets, sorted_token,
-                                     sorted_slot, slot_row);
-        });
+                                     sorted_slot, slot_row, w ? &tt : nullptr, ntables, w,
+                                     row_scale, extra);
+        }));
+        if (tables_built) *tables_built = w != nullptr;
+        return MOE_OK;
+    }
     int32_t* hist = at<int32_t>(ws, p.hist);
     TRY(run(h, s, L_PERM_COUNT, [&] { return launch_perm_count(s, idx, hist, d->T, d->k, d->M); }));
     TRY(run(h, s, L_PERM_SCAN, [&] {
@@ -347,21 +371,21 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
                   int32_t* sorted_token, const int32_t* sorted_slot, int32_t* offsets,
                   const float* w, const void* W1, const void* b1, const void* W2, const void* b2,
                   float* O, void* ws, hipStream_t s, const void* Wsh_gu = nullptr,
-                  const void* Wsh_dn = nullptr, bool compact = false) {
+                  const void* Wsh_dn = nullptr, bool compact = false,
+                  bool tables_built = false) {
     const bool merged = Wsh_gu != nullptr;
     const int64_t rows = merged ? p.Sx : p.S;
-    int32_t* tiles_up = at<int32_t>(ws, p.tiles_up);
-    int32_t* tiles_dn = at<int32_t>(ws, p.tiles_dn);
+    int ntables = 0;
+    const TileTables tt = tile_tables(p, ws, &ntables);
+    int32_t* tiles_up = tt.tiles[0];
+    int32_t* tiles_dn = tt.tiles[1];
     void* H = at<char>(ws, p.H);
-    TileTables tt{{p.bm_up, p.bm_dn},
-                  {(int)p.max_tiles_up, (int)p.max_tiles_dn},
-                  {tiles_up, tiles_dn}};
-    const int ntables = tiles_dn == tiles_up ? 1 : 2;
     float* row_scale = at<float>(ws, p.row_scale);
-    TRY(run(h, s, L_TILE_TABLE, [&] {
-        return launch_tile_table(s, offsets, d->M, tt, ntables, sorted_slot, w, p.S, row_scale,
-                                 merged ? d->T : 0, sorted_token);
-    }));
+    if (!tables_built)
+        TRY(run(h, s, L_TILE_TABLE, [&] {
+            return launch_tile_table(s, offsets, d->M, tt, ntables, sorted_slot, w, p.S,
+                                     row_scale, merged ? d->T : 0, sorted_token);
+        }));
     const bool swiglu = d->act == MOE_ACT_SWIGLU;
     GemmArgs up{};
     up.a = x;
@@ -855,9 +879,11 @@ int forward_impl(moe_handle* h, const moe_desc* d, const void* x, const float* W
     if (p.merged) {
         // the shared expert is group M of the routed GEMMs; Ysh is O's tail
         TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
-        TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
+        bool built = false;
+        TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s,
+                       w, d->T, &built));
         TRY(do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O,
-                          ws, s, Wsh_gu, Wsh_dn));
+                          ws, s, Wsh_gu, Wsh_dn, false, built));
         return do_combine(h, d, O, slot_row, Ysh, y, s);
     }
     const bool fork = Ysh && aux && aux != s;
@@ -875,9 +901,11 @@ int forward_impl(moe_handle* h, const moe_desc* d, const void* x, const float* W
         }
     }
     TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));
-    TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s));
+    bool built = false;
+    TRY(do_permute(h, d, p, idx, counts, offsets, sorted_token, sorted_slot, slot_row, ws, s, w,
+                   0, &built));
     TRY(do_expert_ffn(h, d, p, x, sorted_token, sorted_slot, offsets, w, W1, b1, W2, b2, O, ws, s,
-                      nullptr, nullptr, p.compact));
+                      nullptr, nullptr, p.compact, built));
     if (fork) {
         const hipError_t e = hipStreamWaitEvent(s, h->ev_join, 0);
         if (e != hipSuccess) return fail(MOE_ERR_HIP, "stream join: %s", hipGetErrorString(e));

@@ -232,11 +232,16 @@ struct TileTables {
 hipError_t launch_tile_table(hipStream_t s, int32_t* offsets, int64_t M, const TileTables& tt,
                              int count, const int32_t* sorted_slot, const float* w, int64_t S,
                              float* row_scale, int64_t extra, int32_t* sorted_token);
-// Count, scan and scatter in one workgroup for T <= kSmallT tokens.
+// Count, scan and scatter in one workgroup for T <= kSmallT tokens; with
+// ntables > 0 the same launch also does launch_tile_table's work (tables
+// tt, row scales from w, `extra` rows of group M), saving that launch.
 constexpr int64_t kSmallT = 1024;
 hipError_t launch_perm_small(hipStream_t s, const int32_t* idx, int64_t T, int k, int64_t M,
                              int32_t* counts, int32_t* offsets, int32_t* sorted_token,
-                             int32_t* sorted_slot, int32_t* slot_row);
+                             int32_t* sorted_slot, int32_t* slot_row,
+                             const TileTables* tt = nullptr, int ntables = 0,
+                             const float* w = nullptr, float* row_scale = nullptr,
+                             int64_t extra = 0);
 hipError_t launch_wgrad(hipStream_t s, const GemmArgs& g);
 hipError_t launch_gemm(hipStream_t s, int dtype, int bm, int epi, const GemmArgs& g,
                        int64_t m_tiles);

@@ -152,6 +152,49 @@ __global__ __launch_bounds__(kPermBlock) void perm_scatter(
     }
 }
 
+// One tile table, built by a whole workgroup of kScanThreads threads from
+// the expert offsets (offsets[0..M], written earlier and visible to it):
+// one thread per expert writes its own tiles after a scan of the tile
+// counts.  The extra group (index M) ends `extra` rows after the last
+// expert's; with set_end its end goes to offsets[M + 1].  Begins with a
+// barrier, so consecutive calls may share s_warp.
+__device__ void build_tiles(int32_t* offsets, int M, int64_t extra, int bm, int max_tiles,
+                            int32_t* __restrict__ tiles, bool set_end, int32_t* s_warp) {
+    __syncthreads();
+    const int Mg = extra > 0 ? M + 1 : M;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int32_t nt = 0, r0 = 0;
+    if (tid < Mg) {
+        r0 = offsets[tid];
+        const int32_t end = tid == M ? r0 + (int32_t)extra : offsets[tid + 1];
+        nt = (end - r0 + bm - 1) / bm;
+        if (tid == M && set_end) offsets[M + 1] = end;
+    }
+    int32_t incl = nt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_warp[wv] = incl;
+    __syncthreads();
+    int32_t base = 0, total = 0;
+    for (int i = 0; i < kScanThreads / 64; ++i) {
+        if (i < wv) base += s_warp[i];
+        total += s_warp[i];
+    }
+    const int32_t first = base + incl - nt;
+    for (int i = 0; i < nt; ++i) {
+        tiles[2 * (first + i)] = tid;
+        tiles[2 * (first + i) + 1] = r0 + i * bm;
+    }
+    for (int i = total + tid; i < max_tiles; i += kScanThreads) {
+        tiles[2 * i] = -1;
+        tiles[2 * i + 1] = 0;
+    }
+    if (tid == 0) tiles[2 * max_tiles] = total;
+}
+
 // The whole dispatch in one workgroup when T <= kSmallT (one token per
 // thread, decode-sized batches): the per-wave expert masks of the scatter
 // give both the counts (their popcounts) and the stable ranks, so count,
@@ -162,7 +205,11 @@ __global__ __launch_bounds__(kScanThreads) void perm_small(const int32_t* __rest
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted_token,
                                                           int32_t* __restrict__ sorted_slot,
-                                                          int32_t* __restrict__ slot_row) {
+                                                          int32_t* __restrict__ slot_row,
+                                                          TileTables tt, int ntables,
+                                                          const float* __restrict__ w,
+                                                          float* __restrict__ row_scale,
+                                                          int64_t extra) {
     constexpr int NW = kScanThreads / 64;
     extern __shared__ unsigned long long s_mask[];   // [NW][M], then s_off[M]
     int32_t* s_off = reinterpret_cast<int32_t*>(s_mask + NW * M);
@@ -217,28 +264,41 @@ __global__ __launch_bounds__(kScanThreads) void perm_small(const int32_t* __rest
     if (tid == M - 1) offsets[M] = incl;
     __syncthreads();
     const int64_t S = (int64_t)T * k;
+    const bool tables = ntables > 0;   // uniform
     for (int64_t r = total + tid; r < S; r += kScanThreads) {
         sorted_token[r] = -1;
         sorted_slot[r] = -1;
+        if (tables) row_scale[r] = 0.f;
     }
-    if (t >= T) return;
-    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (t < T) {
+        const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-        if (j >= k) break;
-        const int64_t f = (int64_t)t * k + j;
-        const int e = e_of[j];
-        if (e < 0) {
-            slot_row[f] = -1;
-            continue;
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j >= k) break;
+            const int64_t f = (int64_t)t * k + j;
+            const int e = e_of[j];
+            if (e < 0) {
+                slot_row[f] = -1;
+                continue;
+            }
+            int rank = __popcll(s_mask[wv * M + e] & below);
+            for (int w2 = 0; w2 < wv; ++w2) rank += __popcll(s_mask[w2 * M + e]);
+            const int32_t r = s_off[e] + rank;
+            sorted_slot[r] = (int32_t)f;
+            sorted_token[r] = t;
+            slot_row[f] = r;
+            if (tables) row_scale[r] = w[f];
         }
-        int rank = __popcll(s_mask[wv * M + e] & below);
-        for (int w2 = 0; w2 < wv; ++w2) rank += __popcll(s_mask[w2 * M + e]);
-        const int32_t r = s_off[e] + rank;
-        sorted_slot[r] = (int32_t)f;
-        sorted_token[r] = t;
-        slot_row[f] = r;
     }
+    if (!tables) return;
+    // the tile tables and the row scales of tile_table, without its launch:
+    // the extra group's rows (every token once, scale 1), then the tables
+    for (int64_t r = S + tid; r < S + extra; r += kScanThreads) {
+        row_scale[r] = 1.f;
+        sorted_token[r] = (int32_t)(r - S);
+    }
+    for (int y = 0; y < ntables; ++y)
+        build_tiles(offsets, M, extra, tt.bm[y], tt.max_tiles[y], tt.tiles[y], y == 0, s_warp);
 }
 
 // Per m-tile of `bm` rows: (expert, first row).  Tiles are laid out expert
@@ -270,41 +330,8 @@ __global__ __launch_bounds__(kScanThreads) void tile_table(int32_t* __restrict__
         }
         return;
     }
-    // the extra group (index M) ends `extra` rows after the last expert's
-    const int Mg = extra > 0 ? M + 1 : M;
-    const int bm = tt.bm[blockIdx.y], max_tiles = tt.max_tiles[blockIdx.y];
-    int32_t* __restrict__ tiles = tt.tiles[blockIdx.y];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    int32_t nt = 0, r0 = 0;
-    if (tid < Mg) {
-        r0 = offsets[tid];
-        const int32_t end = tid == M ? r0 + (int32_t)extra : offsets[tid + 1];
-        nt = (end - r0 + bm - 1) / bm;
-        if (tid == M && blockIdx.y == 0) offsets[M + 1] = end;
-    }
-    int32_t incl = nt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int32_t o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
-    if (lane == 63) s_warp[wv] = incl;
-    __syncthreads();
-    int32_t base = 0, total = 0;
-    for (int i = 0; i < kScanThreads / 64; ++i) {
-        if (i < wv) base += s_warp[i];
-        total += s_warp[i];
-    }
-    const int32_t first = base + incl - nt;
-    for (int i = 0; i < nt; ++i) {
-        tiles[2 * (first + i)] = tid;
-        tiles[2 * (first + i) + 1] = r0 + i * bm;
-    }
-    for (int i = total + tid; i < max_tiles; i += kScanThreads) {
-        tiles[2 * i] = -1;
-        tiles[2 * i + 1] = 0;
-    }
-    if (tid == 0) tiles[2 * max_tiles] = total;
+    build_tiles(offsets, M, extra, tt.bm[blockIdx.y], tt.max_tiles[blockIdx.y],
+                tt.tiles[blockIdx.y], blockIdx.y == 0, s_warp);
 }
 
 }  // namespace
@@ -351,9 +378,14 @@ size_t perm_small_lds(int64_t M) {
 
 hipError_t launch_perm_small(hipStream_t s, const int32_t* idx, int64_t T, int k, int64_t M,
                              int32_t* counts, int32_t* offsets, int32_t* sorted_token,
-                             int32_t* sorted_slot, int32_t* slot_row) {
+                             int32_t* sorted_slot, int32_t* slot_row, const TileTables* tt,
+                             int ntables, const float* w, float* row_scale, int64_t extra) {
+    if (ntables > 0 && (!tt || ntables > 2 || M + (extra > 0 ? 1 : 0) > kScanThreads))
+        return hipErrorInvalidValue;
+    const TileTables none{};
     hipLaunchKernelGGL(perm_small, dim3(1), dim3(kScanThreads), perm_small_lds(M), s, idx, (int)T,
-                       k, (int)M, counts, offsets, sorted_token, sorted_slot, slot_row);
+                       k, (int)M, counts, offsets, sorted_token, sorted_slot, slot_row,
+                       ntables > 0 ? *tt : none, ntables, w, row_scale, extra);
     return hipGetLastError();
 }
 
