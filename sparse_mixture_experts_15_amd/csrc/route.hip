@@ -20,6 +20,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -55,7 +57,92 @@ __device__ __forceinline__ bool better(double av, int ai, double bv, int bi) {
     return av > bv || (av == bv && ai < bi);
 }
 
-// One wave: top-k of one token from its fp32 logits `lrow[0..M)`.
+// Wave-wide reductions without LDS.  Step S pairs every lane with one
+// partner: S = 0, 1 the lanes l ^ 1 and l ^ 2 (DPP quad permutations), S = 2
+// the mirror lane inside each 8-lane half row, S = 3 inside each 16-lane row
+// (DPP mirrors), S = 4 and 5 the lanes l ^ 16 and l ^ 32 (v_permlane16_swap,
+// v_permlane32_swap).  After steps 0..5 in order every lane has met all 64
+// values.  xpair returns {own, partner} or {partner, own}; the same order in
+// every register of one step, so (value, index) pairs stay together.  Every
+// reduction below is symmetric in the two values (a strict total order, a
+// commutative sum), so both lanes of a pair hold the same bits afterwards.
+// These moves run on the VALU; the shuffles they replace were routed through
+// the LDS crossbar, where they queue behind any MFMA kernel sharing the CU.
+struct Pair32 {
+    uint32_t a, b;
+};
+template <int S>
+__device__ __forceinline__ Pair32 xpair(uint32_t x) {
+    if constexpr (S <= 3) {
+        constexpr int ctrl = S == 0 ? 0xB1 : S == 1 ? 0x4E : S == 2 ? 0x141 : 0x140;
+        return {x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, ctrl, 0xF, 0xF, false)};
+    } else if constexpr (S == 4) {
+        const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return {p[0], p[1]};
+    } else {
+        const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return {p[0], p[1]};
+    }
+}
+template <int S>
+__device__ __forceinline__ void dpair(double x, double& a, double& b) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const Pair32 lo = xpair<S>((uint32_t)u), hi = xpair<S>((uint32_t)(u >> 32));
+    a = __longlong_as_double((long long)(((uint64_t)hi.a << 32) | lo.a));
+    b = __longlong_as_double((long long)(((uint64_t)hi.b << 32) | lo.b));
+}
+template <int S>
+__device__ __forceinline__ void argmax_step(double& v, int& i) {
+    double va, vb;
+    dpair<S>(v, va, vb);
+    const Pair32 ip = xpair<S>((uint32_t)i);
+    const int ia = (int)ip.a, ib = (int)ip.b;
+    const bool tb = better(vb, ib, va, ia);
+    v = tb ? vb : va;
+    i = tb ? ib : ia;
+}
+// (v, i) of the best lane by `better` (larger v, then smaller i), in every lane
+__device__ __forceinline__ void wave_argmax(double& v, int& i) {
+    argmax_step<0>(v, i);
+    argmax_step<1>(v, i);
+    argmax_step<2>(v, i);
+    argmax_step<3>(v, i);
+    argmax_step<4>(v, i);
+    argmax_step<5>(v, i);
+}
+template <int S>
+__device__ __forceinline__ void max_step(double& v) {
+    double a, b;
+    dpair<S>(v, a, b);
+    v = fmax(a, b);
+}
+__device__ __forceinline__ double wave_max(double v) {
+    max_step<0>(v);
+    max_step<1>(v);
+    max_step<2>(v);
+    max_step<3>(v);
+    max_step<4>(v);
+    max_step<5>(v);
+    return v;
+}
+template <int S>
+__device__ __forceinline__ void sum_step(double& v) {
+    double a, b;
+    dpair<S>(v, a, b);
+    v = a + b;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+    sum_step<0>(v);
+    sum_step<1>(v);
+    sum_step<2>(v);
+    sum_step<3>(v);
+    sum_step<4>(v);
+    sum_step<5>(v);
+    return v;
+}
+
+// One wave: top-k of one token from its fp32 logits `lrow[0..M)` (LDS or
+// global; read once into registers, expert e = lane + 64 j in register j).
 // Writes k (expert, weight) pairs in ascending expert order.  With
 // n_group > 1 the experts form n_group contiguous groups and only the
 // topk_group groups with the largest best selection score compete (the
@@ -67,12 +154,16 @@ __device__ __forceinline__ void topk_epilogue_nj(const float* lrow, int M, int k
                                               int32_t* idx_t, float* w_t) {
     const int lane = threadIdx.x & 63;
     double sel[NJ];
+    float lj[NJ];
     double mx = -INFINITY;
-    // the bias loads all go out before the first score is formed
+    // the logit and bias loads all go out before the first score is formed
     float bj[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) bj[j] = 0.f;
-    if (scorer != 0 && bias) {   // uniform; lanes past M re-read a valid entry
+    for (int j = 0; j < NJ; ++j) {
+        bj[j] = 0.f;
+        lj[j] = lrow[min(lane + 64 * j, M - 1)];   // lanes past M re-read a valid entry
+    }
+    if (scorer != 0 && bias) {   // uniform
 #pragma unroll
         for (int j = 0; j < NJ; ++j) bj[j] = bias[min(lane + 64 * j, M - 1)];
     }
@@ -81,7 +172,7 @@ __device__ __forceinline__ void topk_epilogue_nj(const float* lrow, int M, int k
         const int e = lane + 64 * j;
         sel[j] = -INFINITY;
         if (e < M) {
-            const double l = (double)lrow[e];
+            const double l = (double)lj[j];
             if (scorer == 0) {
                 sel[j] = l;   // softmax is increasing in the logit
                 mx = fmax(mx, l);
@@ -95,15 +186,13 @@ __device__ __forceinline__ void topk_epilogue_nj(const float* lrow, int M, int k
     }
     double Z = 0.0;
     if (scorer == 0) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
+        mx = wave_max(mx);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int e = lane + 64 * j;
-            if (e < M) Z += exp((double)lrow[e] - mx);
+            if (e < M) Z += exp((double)lj[j] - mx);
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) Z += __shfl_xor(Z, off);
+        Z = wave_sum(Z);
     }
 
     uint32_t taken = 0;
@@ -118,8 +207,7 @@ __device__ __forceinline__ void topk_epilogue_nj(const float* lrow, int M, int k
                 const int e = lane + 64 * j;
                 if (e < M && e / gs == gi) v = fmax(v, sel[j]);
             }
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+            v = wave_max(v);
             if (lane == gi) my_gs = v;
         }
         // keep the topk_group best groups (the lower group index on a tie)
@@ -129,15 +217,8 @@ __device__ __forceinline__ void topk_epilogue_nj(const float* lrow, int M, int k
             const bool cand = lane < n_group && !mine;
             double bv = cand ? my_gs : -INFINITY;
             int bi = cand ? lane : 0x7fffffff;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const double ov = __shfl_xor(bv, off);
-                const int oi = __shfl_xor(bi, off);
-                if (better(ov, oi, bv, bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
+            wave_argmax(bv, bi);
+            bi = __builtin_amdgcn_readfirstlane(bi);
             if (lane == bi) mine = true;
             kept |= 1ull << bi;
         }
@@ -149,6 +230,7 @@ __device__ __forceinline__ void topk_epilogue_nj(const float* lrow, int M, int k
         }
     }
     int my_e = 0;
+    float my_l = 0.f;
     for (int r = 0; r < k; ++r) {
         double bv = -INFINITY;
         int bi = 0x7fffffff;
@@ -160,31 +242,32 @@ __device__ __forceinline__ void topk_epilogue_nj(const float* lrow, int M, int k
                 bi = e;
             }
         }
+        wave_argmax(bv, bi);
+        bi = __builtin_amdgcn_readfirstlane(bi);   // the same in every lane
+        // the winner's logit, from its owner lane's register
+        const int jw = bi >> 6;
+        float lw = lj[0];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const double ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (better(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
+        for (int j = 1; j < NJ; ++j)
+            if (j == jw) lw = lj[j];
+        lw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lw), bi & 63));
+        if (lane == r) {
+            my_e = bi;
+            my_l = lw;
         }
-        if (lane == r) my_e = bi;
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if ((bi & 63) == lane) taken |= 1u << jw;
     }
 
     // gate value of this lane's chosen expert
     double g = 0.0;
     if (lane < k) {
-        const double l = (double)lrow[my_e];
+        const double l = (double)my_l;
         g = (scorer == 0) ? exp(l - mx) / Z : 1.0 / (1.0 + exp(-l));
     }
-    double gsum = g;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) gsum += __shfl_xor(gsum, off);
+    const double gsum = wave_sum(g);
     int rank = 0;
     for (int i = 0; i < k; ++i) {
-        const int ei = __shfl(my_e, i);
+        const int ei = __builtin_amdgcn_readlane(my_e, i);
         rank += (ei < my_e) ? 1 : 0;
     }
     if (lane < k) {
@@ -194,22 +277,20 @@ __device__ __forceinline__ void topk_epilogue_nj(const float* lrow, int M, int k
     }
 }
 
-// The top-k epilogue with NJ expert registers per lane (M <= 64 NJ): the
-// per-lane loops unroll over exactly the registers the layer needs.
-__device__ __forceinline__ void topk_epilogue(const float* lrow, int M, int k, int scorer,
-                                              const float* bias, int renorm, double alpha,
-                                              double eps, int n_group, int topk_group,
-                                              int32_t* idx_t, float* w_t) {
-    const int nj = (M + 63) >> 6;
-#define MOE_TOPK(NJ_) topk_epilogue_nj<NJ_>(lrow, M, k, scorer, bias, renorm, alpha, eps, \
-                                            n_group, topk_group, idx_t, w_t)
-    if (nj <= 1) MOE_TOPK(1);
-    else if (nj == 2) MOE_TOPK(2);
-    else if (nj == 3) MOE_TOPK(3);
-    else if (nj == 4) MOE_TOPK(4);
-    else if (nj <= 8) MOE_TOPK(8);
-    else MOE_TOPK(kMaxLanesJ);
-#undef MOE_TOPK
+// Kernels carry NJ (expert registers per lane, M <= 64 NJ) as a template
+// parameter: the loops unroll over exactly the registers the layer needs,
+// and each instantiation allocates only its own registers (a kernel
+// covering every NJ would hold the largest one's), so the common sizes stay
+// small enough to share a CU with the expert GEMMs' waves.
+template <typename F>
+__host__ __forceinline__ hipError_t with_nj(int64_t M, F&& f) {
+    const int64_t nj = (M + 63) >> 6;
+    if (nj <= 1) return f(std::integral_constant<int, 1>{});
+    if (nj == 2) return f(std::integral_constant<int, 2>{});
+    if (nj == 3) return f(std::integral_constant<int, 3>{});
+    if (nj == 4) return f(std::integral_constant<int, 4>{});
+    if (nj <= 8) return f(std::integral_constant<int, 8>{});
+    return f(std::integral_constant<int, kMaxLanesJ>{});
 }
 
 // ---- bf16 x: exact three-way split of W_r, MFMA partial logits, top-k ----
@@ -290,6 +371,7 @@ __global__ __launch_bounds__(256) void route_logits_small(const bf16_t* __restri
 // a separate reduction pass), stores them in L[t][0..M) (the backward's
 // recomputed routing reads them there), stages them in its own LDS row and
 // runs the top-k epilogue on it.
+template <int NJ>
 __global__ __launch_bounds__(256) void route_topk_partials(
     const float* __restrict__ P, int nK, float* __restrict__ L, const float* __restrict__ bias,
     int32_t* __restrict__ idx, float* __restrict__ w, int T, int M, int k, int scorer,
@@ -343,11 +425,12 @@ __global__ __launch_bounds__(256) void route_topk_partials(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    topk_epilogue(lrow, M, k, scorer, bias, renorm, (double)alpha, (double)eps, n_group,
-                  topk_group, idx + (int64_t)t * k, w + (int64_t)t * k);
+    topk_epilogue_nj<NJ>(lrow, M, k, scorer, bias, renorm, (double)alpha, (double)eps, n_group,
+                         topk_group, idx + (int64_t)t * k, w + (int64_t)t * k);
 }
 
 // One wave per token: the top-k epilogue on its logits L[t][0..M).
+template <int NJ>
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ L,
                                                   const float* __restrict__ bias,
                                                   int32_t* __restrict__ idx, float* __restrict__ w,
@@ -357,12 +440,13 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ L,
     const int wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;   // whole wave leaves; no block barrier follows
-    topk_epilogue(L + (int64_t)t * M, M, k, scorer, bias, renorm, (double)alpha, (double)eps,
-                  n_group, topk_group, idx + (int64_t)t * k, w + (int64_t)t * k);
+    topk_epilogue_nj<NJ>(L + (int64_t)t * M, M, k, scorer, bias, renorm, (double)alpha,
+                         (double)eps, n_group, topk_group, idx + (int64_t)t * k,
+                         w + (int64_t)t * k);
 }
 
 // Generic router: one wave per token, fp64 dot products (fp32 or bf16 x).
-template <typename XT>
+template <typename XT, int NJ>
 __global__ __launch_bounds__(256) void route_simple(
     const XT* __restrict__ x, const float* __restrict__ W_r, const float* __restrict__ bias,
     int32_t* __restrict__ idx, float* __restrict__ w, int T, int D, int M, int k, int scorer,
@@ -389,8 +473,8 @@ __global__ __launch_bounds__(256) void route_simple(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    topk_epilogue(lrow, M, k, scorer, bias, renorm, (double)alpha, (double)eps, n_group,
-                  topk_group, idx + (int64_t)t * k, w + (int64_t)t * k);
+    topk_epilogue_nj<NJ>(lrow, M, k, scorer, bias, renorm, (double)alpha, (double)eps, n_group,
+                         topk_group, idx + (int64_t)t * k, w + (int64_t)t * k);
 }
 
 }  // namespace
@@ -451,10 +535,12 @@ hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, con
             hipLaunchKernelGGL(route_logits_small,
                                dim3((unsigned)((M + 3) / 4), (unsigned)((T + 3) / 4)), dim3(256),
                                0, s, static_cast<const bf16_t*>(x), W_r, (int)T, (int)D, (int)M, L);
-            hipLaunchKernelGGL(route_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, L, b,
-                               idx, w, (int)T, (int)M, k, scorer, renorm, alpha, eps, n_group,
-                               topk_group);
-            return hipGetLastError();
+            return with_nj(M, [&](auto nj) {
+                hipLaunchKernelGGL(route_topk<decltype(nj)::value>, dim3((unsigned)((T + 3) / 4)),
+                                   dim3(256), 0, s, L, b, idx, w, (int)T, (int)M, k, scorer,
+                                   renorm, alpha, eps, n_group, topk_group);
+                return hipGetLastError();
+            });
         }
         const int64_t n = M * D;
         hipLaunchKernelGGL(router_split, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s,
@@ -472,17 +558,22 @@ hipError_t launch_route(hipStream_t s, int dtype, int scorer, const void* x, con
         g.k_split = nK;
         hipError_t e = launch_gemm(s, 1, 128, EPI_DOWN_F32, g, (T + 127) / 128);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(route_topk_partials, dim3((unsigned)((T + 3) / 4)), dim3(256),
-                           4 * (size_t)M * sizeof(float), s, P, nK, L, b, idx, w, (int)T,
-                           (int)M, k, scorer, renorm, alpha, eps, n_group, topk_group);
-        return hipGetLastError();
+        return with_nj(M, [&](auto nj) {
+            hipLaunchKernelGGL(route_topk_partials<decltype(nj)::value>,
+                               dim3((unsigned)((T + 3) / 4)), dim3(256),
+                               4 * (size_t)M * sizeof(float), s, P, nK, L, b, idx, w, (int)T,
+                               (int)M, k, scorer, renorm, alpha, eps, n_group, topk_group);
+            return hipGetLastError();
+        });
     }
     dim3 grid((unsigned)((T + 3) / 4));
     const size_t lds = 4 * (size_t)M * sizeof(float);
-    hipLaunchKernelGGL(route_simple<float>, grid, dim3(256), lds, s,
-                       static_cast<const float*>(x), W_r, b, idx, w, (int)T, (int)D, (int)M, k,
-                       scorer, renorm, alpha, eps, n_group, topk_group);
-    return hipGetLastError();
+    return with_nj(M, [&](auto nj) {
+        hipLaunchKernelGGL((route_simple<float, decltype(nj)::value>), grid, dim3(256), lds, s,
+                           static_cast<const float*>(x), W_r, b, idx, w, (int)T, (int)D, (int)M,
+                           k, scorer, renorm, alpha, eps, n_group, topk_group);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace moe
