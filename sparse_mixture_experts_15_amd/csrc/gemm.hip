@@ -875,29 +875,37 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             const int krow = RPLn * ins + lane / CPRn;
             const int col = n_base + ((lane % CPRn) ^ kn_swz<BNB>(krow)) * 8;
             rowoff[q] = col < N ? (uint32_t)krow * (uint32_t)N * 2u + (uint32_t)col * 2u : kOOB;
+        } else if (g.b_tiled) {
+            // tiled weights: this lane's 16 bytes of stage 0; stage kt is
+            // TILE_STAGE bytes further (and past K reads zeros, as the A
+            // rows there do)
+            rowoff[q] = tile_base + (uint32_t)ins * 1024u + lane * 16u;
         } else {
             const int row = ROWS_PER_LOAD * ins + lrow;
             int oc, br;
             brow_map<EPI>(row, n_base, g.F_split, oc, br);
-            rowoff[q] = oc < N ? (uint32_t)br * (uint32_t)K * 2u : kOOB;
+            rowoff[q] = oc < N ? (uint32_t)br * (uint32_t)K * 2u + (uint32_t)lchunk * 16u : kOOB;
         }
+        if (q >= QB) rowoff[q] += (uint32_t)lchunk * 16u;   // stays >= kOOB when invalid
     }
-    // load q of this wave for stage kt
+    // bytes from one stage to the next: row-major operands move BK columns,
+    // tiled weights one whole stage block (wave-uniform)
+    const uint32_t bstep = g.b_tiled ? TILE_STAGE : (uint32_t)BK * 2u;
+    // load q of this wave for stage kt: offset = rowoff + kt * step, no
+    // branch per load
     auto issue_q = [&](int kt, int q) {
         bf16_t* st = sm + (kt % STAGES) * STAGE;
         const int kc = kt * BK + lchunk * 8;
         {
             const int ins = wave + 8 * q;
             // an invalid row stays >= kOOB (offsets are < 2^31); a K-tail chunk -> kOOB
-            uint32_t off = rowoff[q] + (uint32_t)kc * 2u;
+            uint32_t off = rowoff[q] + (uint32_t)kt * (q < QB ? bstep : (uint32_t)BK * 2u);
             off = kc < K ? off : kOOB;
             if (BKN && q < QB) {   // KN-layout B: whole k-rows of the stage
                 constexpr int CPRn = BNB / 8, RPLn = 64 / CPRn;
                 const int krow = kt * BK + RPLn * ins + lane / CPRn;
                 off = krow < K ? rowoff[q] + (uint32_t)(kt * BK) * (uint32_t)N * 2u : kOOB;
             }
-            if (q < QB && g.b_tiled)
-                off = tile_base + (uint32_t)kt * TILE_STAGE + (uint32_t)ins * 1024u + lane * 16u;
             if (q < QB)
                 llvm_amdgcn_raw_buffer_load_lds(rb, (lds_u32_ptr)(st + BM * BK + ins * 512), 16,
                                                 (int)off, 0, 0, 0);
