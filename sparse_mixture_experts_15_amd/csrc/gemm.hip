@@ -705,9 +705,15 @@ __device__ __forceinline__ bf16x8 kn_fragment(const bf16_t* bt, int kbase, int n
 // hold rows: eight waves, each 128 A rows (wave row wm) x 64 B rows (wave
 // column wn), accumulators acc[8][4]; the A rows sit at the stage's start,
 // the 256 B rows after them (row-major, or [K, N] when BKN).
-template <int BNB, int BKN>
+struct NoIssue {
+    __device__ void operator()() const {}
+};
+// `issue` enqueues the next stage's global loads; it runs after the first
+// fragment reads, so their LDS latency overlaps the loads' issue instead of
+// following it.
+template <int BNB, int BKN, typename Issue = NoIssue>
 __device__ __forceinline__ void mfma_stage_full256(const bf16_t* st, floatx4 (&acc)[8][4], int wm,
-                                                   int wn, int lane) {
+                                                   int wn, int lane, Issue&& issue = Issue{}) {
     constexpr int BM = 256, BK = 64, TN = 4, WROWS = 128;
     const int fr = lane & 15, fc = lane >> 4;
     // 256-row tiles, whole fragments: each K half's rows 0-3 then
@@ -746,6 +752,7 @@ __device__ __forceinline__ void mfma_stage_full256(const bf16_t* st, floatx4 (&a
     rdB(0, b0);
     rdA(0, 0, a00);
     __builtin_amdgcn_sched_group_barrier(0x100, TN * RB + 4, 0);
+    issue();
     rdA(0, 4, a01);
     mm(0, a00, b0);
 #pragma unroll
@@ -956,19 +963,23 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
             if (LPW == LPW_LO || wave < LOADS % 8) wait_stages<LPW, STAGES>(later);
             else wait_stages<LPW_LO, STAGES>(later);
             __builtin_amdgcn_s_barrier();     // every wave's loads landed; stage kt-1 fully read
-            if (kt + STAGES - 1 < nk) issue(k_first + kt + STAGES - 1);
+            const bool more = kt + STAGES - 1 < nk;
+            const int next = k_first + kt + STAGES - 1;
             const bf16_t* st = sm + ((k_first + kt) % STAGES) * STAGE;
-            body(st);
+            body(st, [&] {
+                if (more) issue(next);
+            });
         }
     };
     // the multiply of one stage for 256-row tiles whose fragments all hold rows
-    auto body_full256 = [&](const bf16_t* st) {
+    auto body_full256 = [&](const bf16_t* st, auto&& pre) {
         if constexpr (TM == 8 && BK == 64)
-            mfma_stage_full256<BNB, BKN>(st, acc, wm, wn, lane);
+            mfma_stage_full256<BNB, BKN>(st, acc, wm, wn, lane, pre);
     };
     // the multiply of one stage in general (fragments past the group's
     // last row skip their reads and MFMAs)
-    auto body_general = [&](const bf16_t* st) {
+    auto body_general = [&](const bf16_t* st, auto&& pre) {
+        pre();
         if (TM <= 4 && wlive == TM) {
             // whole fragments: one straight block (every fragment read, then
             // the MFMAs) the scheduler can overlap freely.  Measured faster
