@@ -428,7 +428,7 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
         dn.cexp = reinterpret_cast<int8_t*>(O) + compact_exp_offset(rows, d->D);
     }
     dn.tiles = tiles_dn;
-    dn.group_m = gemm_group_m(rows, d->M, p.bm_dn, d->group_m);
+    dn.group_m = gemm_group_m(rows, d->M, p.bm_dn, d->group_m, true);
     if (merged) {
         dn.b_extra = Wsh_dn;
         dn.extra_group = (int)d->M;

@@ -186,9 +186,10 @@ hipError_t launch_tile_weights(hipStream_t s, const void* src, void* dst, int64_
 
 // m-tiles per group of the tile order for a grouped GEMM: about the m-tiles
 // one expert spans, so that the workgroups one XCD runs together share that
-// expert's weight tiles and rows in its L2.
+// expert's weight tiles and rows in its L2; one for a grouped down
+// projection (`down`, groups > 1), whose groups are dealt to the XCDs.
 // `request` (1..16) overrides the choice.
-int gemm_group_m(int64_t rows, int64_t groups, int bm, int request = 0);
+int gemm_group_m(int64_t rows, int64_t groups, int bm, int request = 0, bool down = false);
 // Columns of the EPI_DH_* partial-dot buffer (part_ld) for a GEMM of N
 // output columns on the tile height bm.
 int gemm_part_cols(int bm, int64_t N);

@@ -1389,8 +1389,15 @@ int gemm_block_m(int dtype, int64_t rows, int64_t groups, bool down, int64_t b_r
     return 256;
 }
 
-int gemm_group_m(int64_t rows, int64_t groups, int bm, int request) {
+int gemm_group_m(int64_t rows, int64_t groups, int bm, int request, bool down) {
     if (request >= 1 && request <= 16) return request;
+    // Grouped down projections deal whole groups to the XCDs; one m-tile
+    // per group spreads the experts' uneven tiles over the XCDs in finer
+    // pieces, at the price of more L2 misses (more fabric traffic, the
+    // same or lower time): GLM-4.5 prefill down projection 1.150-1.160 ->
+    // 1.134 ms, GLM-5 3.63-3.64 -> 3.57 ms against two m-tiles per group
+    // (the up projections, in hardware order, lose with one: 1.93 -> 2.07).
+    if (down && groups > 1) return 1;
     const int64_t per = (rows / (groups > 0 ? groups : 1) + bm / 2) / bm;
     return per < 1 ? 1 : per > 4 ? 4 : (int)per;
 }
