@@ -110,7 +110,10 @@ Plan make_plan(const moe_desc* d, bool allow_merge = true) {
         p.O = take(std::max((size_t)p.S * d->D * 4,
                             (size_t)compact_row_bytes(p.S, d->D)));
         p.Hsh = take((size_t)d->T * d->F_shared * p.esz);
-        p.Ysh = take(d->F_shared > 0 ? (size_t)d->T * d->D * 4 : 0);
+        // fp32 shared rows (the stage entry points), or compact ones
+        p.Ysh = take(d->F_shared > 0 ? std::max((size_t)d->T * d->D * 4,
+                                                (size_t)compact_row_bytes(d->T, d->D))
+                                     : 0);
     }
     p.route = take(route_workspace(d->dtype, d->T, d->D, d->M));
     p.total = off;
@@ -443,8 +446,11 @@ int do_expert_ffn(moe_handle* h, const moe_desc* d, const Plan& p, const void* x
                [&] { return launch_gemm(s, d->dtype, p.bm_dn, EPI_DOWN_SCALED, dn, p.max_tiles_dn); });
 }
 
+// The shared expert; with `compact` its rows go to Ysh's space in the
+// compact format of the routed rows (fp16 with a power-of-two scale per 64
+// values; moe_forward's combine reads them), else as fp32 rows.
 int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, const void* Wgu,
-              const void* Wdn, float* Ysh, void* ws, hipStream_t s) {
+              const void* Wdn, float* Ysh, void* ws, hipStream_t s, bool compact = false) {
     void* Hsh = at<char>(ws, p.Hsh);
     const int64_t mt_up = (d->T + p.bm_sh_up - 1) / p.bm_sh_up;
     const int64_t mt_dn = (d->T + p.bm_sh_dn - 1) / p.bm_sh_dn;
@@ -470,16 +476,24 @@ int do_shared(moe_handle* h, const moe_desc* d, const Plan& p, const void* x, co
     dn.b_stride = tiled ? tiled_elems(d->D, d->F_shared, false) : 0;
     dn.b_tiled = tiled;
     dn.c = Ysh;
+    if (compact) {   // weight 1 (row_w NULL), no bias
+        dn.c16 = Ysh;
+        dn.cexp = reinterpret_cast<int8_t*>(Ysh) + compact_exp_offset(d->T, d->D);
+    }
     dn.dense_rows = d->T;
     dn.a_rows = d->T;
     dn.b_rows = (int)d->D;
     dn.K = (int)d->F_shared;
     dn.N = (int)d->D;
     dn.xcd_mode = gemm_xcd_mode(false, true, false, d->tile_order[MOE_GEMM_SHARED_DOWN]);
-    return run(h, s, L_SHARED_DOWN,
-               [&] { return launch_gemm(s, d->dtype, p.bm_sh_dn, EPI_DOWN_F32, dn, mt_dn); });
+    return run(h, s, L_SHARED_DOWN, [&] {
+        return launch_gemm(s, d->dtype, p.bm_sh_dn, compact ? EPI_DOWN_SCALED : EPI_DOWN_F32, dn,
+                           mt_dn);
+    });
 }
 
+// With `compact` the expert rows, and the shared rows when present, are in
+// the compact format.
 int do_combine(moe_handle* h, const moe_desc* d, const float* O, const int32_t* slot_row,
                const float* Ysh, void* y, hipStream_t s, bool compact = false) {
     return run(h, s, L_COMBINE, [&] {
@@ -487,7 +501,10 @@ int do_combine(moe_handle* h, const moe_desc* d, const float* O, const int32_t* 
             return launch_combine_compact(
                 s, d->out_dtype, O,
                 reinterpret_cast<const int8_t*>(O) + compact_exp_offset(d->T * d->k, d->D),
-                slot_row, Ysh, y, d->T, d->k, d->D);
+                slot_row, nullptr, Ysh,
+                Ysh ? reinterpret_cast<const int8_t*>(Ysh) + compact_exp_offset(d->T, d->D)
+                    : nullptr,
+                y, d->T, d->k, d->D);
         return launch_combine(s, d->out_dtype, O, slot_row, Ysh, y, d->T, d->k, d->D);
     });
 }
@@ -893,11 +910,11 @@ int forward_impl(moe_handle* h, const moe_desc* d, const void* x, const float* W
             if ((e = hipEventRecord(h->ev_fork, s)) != hipSuccess ||
                 (e = hipStreamWaitEvent(aux, h->ev_fork, 0)) != hipSuccess)
                 return fail(MOE_ERR_HIP, "stream fork: %s", hipGetErrorString(e));
-            TRY(do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, aux));
+            TRY(do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, aux, p.compact));
             if ((e = hipEventRecord(h->ev_join, aux)) != hipSuccess)
                 return fail(MOE_ERR_HIP, "stream join: %s", hipGetErrorString(e));
         } else {
-            TRY(do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, s));
+            TRY(do_shared(h, d, p, x, Wsh_gu, Wsh_dn, Ysh, ws, s, p.compact));
         }
     }
     TRY(do_route(h, d, p, x, W_r, bias, idx, w, ws, s));

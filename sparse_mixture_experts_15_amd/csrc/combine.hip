@@ -82,10 +82,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // so the fp32 sum runs over exactly the values the rows hold, in the same
 // slot order, then the shared row, then one rounding.  A lane's V columns
 // share one scale group (V divides kRowGroup and d0 is a multiple of V).
+// The shared row is fp32 (Ysh) or compact as well (Ysh16 / YshExp, one row
+// per token, the same format).
 template <typename TY>
 __global__ __launch_bounds__(256) void combine_compact_kernel(
     const uint16_t* __restrict__ O16, const int8_t* __restrict__ Oexp,
-    const int32_t* __restrict__ slot_row, const float* __restrict__ Ysh, TY* __restrict__ y,
+    const int32_t* __restrict__ slot_row, const float* __restrict__ Ysh,
+    const uint16_t* __restrict__ Ysh16, const int8_t* __restrict__ YshExp, TY* __restrict__ y,
     int Tn, int k, int D, int chunks) {
     constexpr int V = Out<TY>::V;
     static_assert(kRowGroup % V == 0, "a lane's columns lie in one scale group");
@@ -102,11 +105,10 @@ __global__ __launch_bounds__(256) void combine_compact_kernel(
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-        if (rows[j] < 0) continue;
-        const uint16_t* p = O16 + (int64_t)rows[j] * D + d0;
-        const int e = Oexp[(int64_t)rows[j] * G + d0 / kRowGroup];
+    // acc += row `row` of a compact matrix (values v16, exponents ve)
+    auto add_compact = [&](const uint16_t* v16, const int8_t* ve, int64_t row) {
+        const uint16_t* p = v16 + row * D + d0;
+        const int e = ve[row * G + d0 / kRowGroup];
         uint16_t h[V];
         if constexpr (V == 8) {
             const u32x4 u = *reinterpret_cast<const u32x4*>(p);
@@ -123,8 +125,15 @@ __global__ __launch_bounds__(256) void combine_compact_kernel(
 #pragma unroll
         for (int i = 0; i < V; ++i)
             acc[i] += ldexpf((float)__builtin_bit_cast(_Float16, h[i]), e);
+    };
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (rows[j] < 0) continue;
+        add_compact(O16, Oexp, rows[j]);
     }
-    if (Ysh) {
+    if (Ysh16) {
+        add_compact(Ysh16, YshExp, t);
+    } else if (Ysh) {
         float v[V];
         load_f32<V>(Ysh + (int64_t)t * D + d0, v);
 #pragma unroll
@@ -137,7 +146,8 @@ __global__ __launch_bounds__(256) void combine_compact_kernel(
 
 hipError_t launch_combine_compact(hipStream_t s, int out_dtype, const void* O16,
                                   const int8_t* Oexp, const int32_t* slot_row, const float* Ysh,
-                                  void* y, int64_t T, int k, int64_t D) {
+                                  const void* Ysh16, const int8_t* YshExp, void* y, int64_t T,
+                                  int k, int64_t D) {
     if (T == 0) return hipSuccess;
     const int V = out_dtype == 1 ? Out<bf16_t>::V : Out<float>::V;
     const int chunks = (int)((D + 64 * V - 1) / (64 * V));
@@ -145,10 +155,12 @@ hipError_t launch_combine_compact(hipStream_t s, int out_dtype, const void* O16,
     const uint16_t* o = static_cast<const uint16_t*>(O16);
     if (out_dtype == 1)
         hipLaunchKernelGGL(combine_compact_kernel<bf16_t>, grid, dim3(256), 0, s, o, Oexp,
-                           slot_row, Ysh, static_cast<bf16_t*>(y), (int)T, k, (int)D, chunks);
+                           slot_row, Ysh, static_cast<const uint16_t*>(Ysh16), YshExp,
+                           static_cast<bf16_t*>(y), (int)T, k, (int)D, chunks);
     else
         hipLaunchKernelGGL(combine_compact_kernel<float>, grid, dim3(256), 0, s, o, Oexp,
-                           slot_row, Ysh, static_cast<float*>(y), (int)T, k, (int)D, chunks);
+                           slot_row, Ysh, static_cast<const uint16_t*>(Ysh16), YshExp,
+                           static_cast<float*>(y), (int)T, k, (int)D, chunks);
     return hipGetLastError();
 }
 

@@ -120,7 +120,7 @@ struct GemmArgs {
     const void* b;            // [E, NB, K] dtype
     int64_t b_stride;         // elements between experts in b
     const void* bias;         // [E, N] dtype, nullable (GELU b1 or DOWN b2)
-    const float* row_w;       // DOWN_SCALED: scale of sorted row r (its slot's weight)
+    const float* row_w;       // DOWN_SCALED: scale of sorted row r (its slot's weight); NULL: 1
     void* c;                  // [rows, N]
     const int32_t* tiles;     // grouped: per m-tile (expert, row0); NULL: dense
     const int32_t* offsets;   // grouped: expert row ranges [M+1]
@@ -250,10 +250,13 @@ hipError_t launch_combine(hipStream_t s, int out_dtype, const float* O, const in
                           const float* Ysh, void* y, int64_t T, int k, int64_t D);
 // The combine over compact rows (fp16 values O16 with exponents Oexp, as the
 // compact EPI_DOWN_SCALED epilogue writes them); same order and rounding of
-// the fp32 sum as launch_combine.
+// the fp32 sum as launch_combine.  The shared rows are fp32 (Ysh) or, with
+// Ysh16 non-null, compact in the same format (values Ysh16, exponents
+// YshExp, one row per token).
 hipError_t launch_combine_compact(hipStream_t s, int out_dtype, const void* O16,
                                   const int8_t* Oexp, const int32_t* slot_row, const float* Ysh,
-                                  void* y, int64_t T, int k, int64_t D);
+                                  const void* Ysh16, const int8_t* YshExp, void* y, int64_t T,
+                                  int k, int64_t D);
 
 // Backward (backward.hip).
 hipError_t launch_transpose(hipStream_t s, const void* src, int64_t ld_src, int64_t src_rows,

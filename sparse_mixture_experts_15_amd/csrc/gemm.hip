@@ -943,7 +943,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16(GemmArgs g, int m_tiles, int 
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int64_t r = tl.r0 + wm * WROWS + 16 * i + (lane & 15);
-        wpre[i] = (EPI == EPI_DOWN_SCALED && i < wlive && r < tl.rend) ? g.row_w[r] : 1.f;
+        wpre[i] = (EPI == EPI_DOWN_SCALED && g.row_w && i < wlive && r < tl.rend) ? g.row_w[r]
+                                                                                  : 1.f;
     }
 
     // STAGES-deep ring: stages kt+1 .. kt+STAGES-1 load while stage kt is
@@ -1284,7 +1285,7 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmArgs g) {
                 if (n < N) C[r * N + n] = silu_f32(acc[i][j]) * acc[i][j + 2];
             }
         } else {
-            const float wr = (EPI == EPI_DOWN_SCALED) ? g.row_w[r] : 1.f;
+            const float wr = (EPI == EPI_DOWN_SCALED && g.row_w) ? g.row_w[r] : 1.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n = n_base + tx + 16 * j;

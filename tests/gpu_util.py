@@ -192,8 +192,9 @@ def rounding_bounds(cfg, h, idx, w, compact=False):
     the bf16 down projection, so an output element O_i = w sum_f H_f W2_if
     can be off by up to 2^-8 w sum_f |H_f| |W2_if|.  With `compact` (the
     forward's compact expert rows) each row element also carries up to
-    2^-11 |O_i|.  Returns that bound per (token, slot) row [T, k, D] and for
-    the shared expert [T, D] (or None).  Computed with numpy from the same
+    2^-11 |O_i|, and so does each shared row element (the forward's shared
+    rows take the same format).  Returns that bound per (token, slot) row
+    [T, k, D] and for the shared expert [T, D] (or None).  Computed with numpy from the same
     inputs; it is an error allowance, never an expected value."""
     X = widen(h["x"])
     W1, W2 = widen(h["W1"]), widen(h["W2"])
@@ -217,7 +218,10 @@ def rounding_bounds(cfg, h, idx, w, compact=False):
         Z = X @ gu.T
         from scipy import special
         g, u = Z[:, :cfg.F_shared], Z[:, cfg.F_shared:]
-        bsh = BF16_REL * (np.abs(g * special.expit(g) * u) @ np.abs(dn).T)
+        Hsh = g * special.expit(g) * u
+        bsh = BF16_REL * (np.abs(Hsh) @ np.abs(dn).T)
+        if compact:   # the forward's shared rows are compact too
+            bsh = bsh + COMPACT_REL * np.abs(Hsh @ dn.T)
     return bnd, bsh
 
 
@@ -232,7 +236,8 @@ def rounding_bounds_tokens(cfg, h, idx, w, tokens, compact=False):
     only, [len(tokens), D]: per routed slot 2^-8 |w| sum_f |H_f| |W2_if|, plus
     the shared expert's 2^-8 sum_f |Hsh_f| |Wsh_dn_if|.  Only the experts those
     tokens reach are widened (fp32 suffices for an allowance), so it runs at
-    full layer sizes.  `compact` adds the compact rows' 2^-11 |O| per slot."""
+    full layer sizes.  `compact` adds the compact rows' 2^-11 |O| per slot
+    and 2^-11 |Ysh| for the shared row."""
     from scipy import special
     X = _widen32(h["x"][tokens])
     out = np.zeros((len(tokens), cfg.D), np.float64)
@@ -254,7 +259,11 @@ def rounding_bounds_tokens(cfg, h, idx, w, tokens, compact=False):
     if cfg.F_shared:
         Z = (X @ _widen32(h["Wsh_gu"]).T).astype(np.float64)
         g, u = Z[:, :cfg.F_shared], Z[:, cfg.F_shared:]
-        out += BF16_REL * (np.abs(g * special.expit(g) * u) @ np.abs(_widen32(h["Wsh_dn"])).T)
+        Hsh = g * special.expit(g) * u
+        dn = _widen32(h["Wsh_dn"]).astype(np.float64)
+        out += BF16_REL * (np.abs(Hsh) @ np.abs(dn).T)
+        if compact:   # the forward's shared rows are compact too
+            out += COMPACT_REL * np.abs(Hsh @ dn.T)
     return out
 
 

@@ -118,7 +118,8 @@ def _stage_parity(cfg, seed=0, tiled=False, **tuning):
     check_float(cfg, to_np(y).reshape(T, D), y_o, "combine y", bound=ybnd, plain=wide)
 
     # whole layer, shared expert on a second stream, fp32 output (its expert
-    # rows compact for bf16 layers: up to 2^-11 |O| more per slot)
+    # and shared rows compact for bf16 layers: up to 2^-11 |O| more per slot
+    # and 2^-11 |Ysh| for the shared row)
     aux = torch.cuda.Stream()
     y_f = forward(L, t, aux=aux)
     torch.cuda.synchronize()
@@ -126,6 +127,8 @@ def _stage_parity(cfg, seed=0, tiled=False, **tuning):
     fbnd = ybnd
     if uses_compact_rows(cfg):
         fbnd = ybnd + COMPACT_REL * np.abs(slots_o).sum(axis=1)
+        if sh_o is not None:
+            fbnd = fbnd + COMPACT_REL * np.abs(sh_o)
     check_float(cfg, to_np(y_f).reshape(T, D)[keep], y_o[keep], "forward y", bound=fbnd[keep],
                 plain=wide)
     # tie-exempt tokens: the oracle on the GPU's own selection
@@ -191,12 +194,33 @@ def test_forward_deterministic_and_stream_invariant(name):
     assert torch.equal(y1, y4)
 
 
+def _row_sums(cfg, L, t, On, sr):
+    """Per token: the sum of |row| over the compact rows the combine adds
+    (its routed rows On via slot_row, and its shared row, computed by the
+    shared-expert stage in fp32) and the sum of those rows' largest
+    magnitudes."""
+    tot = np.zeros((cfg.T, cfg.D))
+    rowmax = np.zeros(cfg.T)
+    for j in range(cfg.k):
+        ok = sr[:, j] >= 0
+        tot[ok] += On[sr[ok, j]]
+        rowmax[ok] += On[sr[ok, j]].max(axis=1)
+    if cfg.F_shared:
+        Ysh = torch.zeros(cfg.T * cfg.D, dtype=torch.float32, device="cuda")
+        B.moe_shared_expert(L.handle, L.desc, t["x"], t["Wsh_gu"], t["Wsh_dn"], Ysh, L.ws)
+        torch.cuda.synchronize()
+        Ya = np.abs(to_np(Ysh).reshape(cfg.T, cfg.D).astype(np.float64))
+        tot += Ya
+        rowmax += Ya.max(axis=1)
+    return tot, rowmax
+
+
 @pytest.mark.parametrize("name", ["glm45_small", "glam_tiles", "glm45_mid", "glam_mid",
                                   "glm5_rows", "glm5_small"])
 def test_compact_rows_within_fp16_rounding(name):
     """The forward with compact expert rows against the same forward with
     fp32 rows: per output element the difference stays within the compact
-    format's rounding of every routed row it sums, 2^-11 |O_j| (relative
+    format's rounding of every routed and shared row it sums, 2^-11 |O_j| (relative
     error of one fp16 rounding after an exact power-of-two scale), plus the
     two fp32 sums' own rounding and fp16 underflow of values far below
     their group's largest."""
@@ -218,12 +242,7 @@ def test_compact_rows_within_fp16_rounding(name):
     torch.cuda.synchronize()
     On = np.abs(to_np(O).reshape(S, cfg.D).astype(np.float64))
     sr = to_np(p["slot_row"]).reshape(cfg.T, cfg.k)
-    tot = np.zeros((cfg.T, cfg.D))
-    rowmax = np.zeros(cfg.T)
-    for j in range(cfg.k):
-        ok = sr[:, j] >= 0
-        tot[ok] += On[sr[ok, j]]
-        rowmax[ok] += On[sr[ok, j]].max(axis=1)
+    tot, rowmax = _row_sums(cfg, L32, t, On, sr)
     a32 = to_np(y32).reshape(cfg.T, cfg.D).astype(np.float64)
     ac = to_np(yc).reshape(cfg.T, cfg.D).astype(np.float64)
     allow = (COMPACT_REL * tot + 2 * (cfg.k + 1) * 2.0 ** -24 * (tot + np.abs(a32))
@@ -265,12 +284,7 @@ def test_compact_rows_extreme_magnitudes():
     On = np.abs(to_np(O).reshape(S, cfg.D).astype(np.float64))
     assert On.max() > 1e9 and On[On > 0].min() < 1e-9, "the layer does not span the range"
     sr = to_np(p["slot_row"]).reshape(cfg.T, cfg.k)
-    tot = np.zeros((cfg.T, cfg.D))
-    rowmax = np.zeros(cfg.T)
-    for j in range(cfg.k):
-        ok = sr[:, j] >= 0
-        tot[ok] += On[sr[ok, j]]
-        rowmax[ok] += On[sr[ok, j]].max(axis=1)
+    tot, rowmax = _row_sums(cfg, L32, t, On, sr)
     a32 = to_np(outs["fp32"][1]).reshape(cfg.T, cfg.D).astype(np.float64)
     ac = to_np(outs["compact"][1]).reshape(cfg.T, cfg.D).astype(np.float64)
     assert np.isfinite(ac).all()
