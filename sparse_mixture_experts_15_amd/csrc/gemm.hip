@@ -1342,7 +1342,10 @@ hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64
         // (256 x 256 with K = 32 stages, 4 or 5 deep, measured slower than 2 x 64)
         if (bm == 256) return launch_bf16<EPI, 256, 256, 2>(s, g, m_tiles);
         if (bm == 160) return launch_bf16<EPI, 160, 256, 3>(s, g, m_tiles);
-        if (bm == 64) return launch_bf16<EPI, 64, 128, 5>(s, g, m_tiles);
+        if (bm == 64) {   // down projections: 256 B rows, 4 stages (160 KB)
+            if constexpr (EPI == EPI_DOWN_SCALED) return launch_bf16<EPI, 64, 256, 4>(s, g, m_tiles);
+            else return launch_bf16<EPI, 64, 128, 5>(s, g, m_tiles);
+        }
         return launch_bf16<EPI, 128, 256, 3>(s, g, m_tiles);
     }
     if constexpr (EPI > EPI_DOWN_F32) {
@@ -1366,7 +1369,10 @@ hipError_t launch_one(hipStream_t s, int dtype, int bm, const GemmArgs& g, int64
 // for groups of a few rows (decode) the up projection takes 64 x 128 tiles
 // with a 5-stage ring, twice the workgroups over the same weights, which
 // evens out the last round of workgroups (GLM-4.5 decode up projection
-// 0.29 -> 0.26 ms; the down projection, K = expert width, is slower so).
+// 0.29 -> 0.26 ms), and the down projection (K = expert width) 64 x 256
+// tiles with a 4-stage ring, three stages of weights in flight (decode
+// layer 0.4542-0.4550 -> 0.4524-0.4531 ms against 128 x 256 x 3; 64 x 128
+// tiles were slower there).
 // Groups of hundreds of rows are MFMA-bound: 256-row tiles halve the LDS
 // traffic per MFMA and take the scheduled full-tile K loop, for the down
 // projection too (GLM-4.5 prefill down projection 1.51 -> 1.30 ms against
@@ -1384,7 +1390,7 @@ int gemm_block_m(int dtype, int64_t rows, int64_t groups, bool down, int64_t b_r
         return tiles256 >= 256 ? 256 : 128;
     }
     const int64_t avg = rows / groups;
-    if (avg <= 16 && !down) return 64;
+    if (avg <= 16) return 64;
     if (avg <= 96) return 128;
     if (avg <= 136) return 160;
     return 256;
