@@ -1204,7 +1204,8 @@ int moe_profile_start(moe_handle* h, int capacity, const char* filter) {
     if (g.err != hipSuccess) return fail(MOE_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
     while ((int)h->prof_events.size() < 2 * capacity) {
         hipEvent_t ev;
-        const hipError_t e = hipEventCreate(&ev);
+        // timing only: no system-scope cache writeback at each record
+        const hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableSystemFence);
         if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
         h->prof_events.push_back(ev);
     }
